@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X, OPT-13B-shaped layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt13b]
+
+One step is one pass of the whole hot path over one batch: translate the 64
+appended tokens to slots, append their K/V to the pools, run the partition
+pass of decode attention and the log-sum-exp merge pass.  Inputs are built
+and resident in HBM before timing; each step uses one of R replicas of the
+pools (different addresses), cycled, so no step finds the previous step's KV in
+the 256 MiB MALL or the L2s.
+
+Prints ONE JSON line.  `value` is algorithmic bytes per step / time per step
+(GB/s); `roofline` prices the partition kernel alone (algorithmic decode bytes
+per launch / its mean launch time, HIP events on its stream); `cpu_baseline`
+times the float64 CPU oracle on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention achieved HBM GB/s (% of MI355X peak) + KV tokens/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json")
+KERNEL_SOURCES = ("paged_kv_cache_119_amd/csrc/decode.hip", "paged_kv_cache_119_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_119_amd/csrc/pkv_launch.h")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="opt13b")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args(argv)
+
+
+def main(argv=None) -> int:
+    args = parse(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU step (heads and sequences shard with "
+              "no exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_119_amd as pkv
+    from paged_kv_cache_119_amd import accounting as acc
+    from paged_kv_cache_119_amd._binding import pool_desc_of
+    from synth import build_tables, make_pools, make_query, normal_16bit
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_cache_119_amd.build import build
+        build()
+    lib = pkv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t = build_tables(args.config, block_size=args.block_size)
+    S, H, D, B = t.num_seqs, t.num_heads, t.head_dim, t.block_size
+    dsize = 2
+    tab = torch.from_numpy(t.block_tables).to(dev)
+    lens = torch.from_numpy(t.context_lens).to(dev)
+    seq = torch.arange(S, dtype=torch.int32, device=dev)
+    pos = torch.from_numpy((t.context_lens - 1).astype(np.int32)).to(dev)
+    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    print(f"[bench] {args.config}: S={S} H={H} D={D} B={B} N={t.num_blocks} "
+          f"kv_tokens={t.kv_tokens()} replicas={args.replicas}", file=sys.stderr, flush=True)
+
+    reps = []
+    for r in range(args.replicas):
+        t.seed += 1000 * r
+        kp, vp = make_pools(t, dev)
+        q = make_query(t, dev)
+        knew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 9)
+        vnew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 10)
+        t.seed -= 1000 * r
+        reps.append((kp, vp, q, knew, vnew, torch.empty_like(q)))
+    desc = pool_desc_of(reps[0][0])
+    P = pkv.decode_partition_size(S, H, t.max_blocks, reps[0][0], args.partition_size)
+    ws = pkv.alloc_workspace(S, H, t.max_blocks, reps[0][0], args.partition_size)
+    ws_bytes = ws.numel()
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+    dref = ctypes.byref(desc)
+
+    # argument marshalling done once; the timed loop only issues the four calls
+    calls = []
+    for kp, vp, q, knew, vnew, out in reps:
+        a_slot = (slots.data_ptr(), tab.data_ptr(), S, t.max_blocks, seq.data_ptr(), pos.data_ptr(), S, dref, sp)
+        a_app = (kp.data_ptr(), vp.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0, 0, slots.data_ptr(), S,
+                 dref, sp)
+        a_dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), tab.data_ptr(), lens.data_ptr(),
+                 ctypes.c_float(t.scale), S, H, t.max_blocks, dref, P, ws.data_ptr(), ws_bytes, sp)
+        a_mrg = (out.data_ptr(), lens.data_ptr(), S, H, t.max_blocks, dref, P, ws.data_ptr(), ws_bytes, sp)
+        calls.append((a_slot, a_app, a_dec, a_mrg))
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {pkv.status_string(st)}")
+
+    def step(i, ev=None):
+        a_slot, a_app, a_dec, a_mrg = calls[i % len(calls)]
+        check(lib.pkv_slot_mapping(*a_slot), "slot_mapping")
+        check(lib.pkv_reshape_and_cache(*a_app), "reshape_and_cache")
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.pkv_decode_partitions(*a_dec), "decode_partitions")
+        if ev is not None:
+            ev[1].record(stream)
+        check(lib.pkv_decode_merge(*a_mrg), "decode_merge")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # whole-step time without per-kernel events (same work), for ms_per_step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps ({elapsed * 1e3 / args.steps:.3f} ms/step host clock with events, "
+          f"{ms_per_step:.4f} ms/step by events)", file=sys.stderr, flush=True)
+
+    dec = acc.decode_bytes(t.context_lens, H, D, dsize, B)
+    app = acc.append_bytes(S, S, H, D, dsize)
+    step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_mean_ms = float(np.mean(kern_ms))
+    achieved = dec["total"] / (kern_mean_ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("config") == args.config and \
+                tr.get("partition_size") == P:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # one parity spot check of the timed configuration (outputs finite)
+    assert torch.isfinite(reps[0][5].float()).all().item(), "non-finite output"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(t, reps[0], args.cpu_budget_s)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": t.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {S} seqs x {H} heads x {D}, B={B}, "
+                               f"context_len {describe_lengths(t)}, one decode step + append of {S} tokens",
+                   "global_batch": S, "kv_tokens": t.kv_tokens(), "block_size": B, "partition_size": P,
+                   "pool_blocks": t.num_blocks, "replicas": args.replicas, "parallelism": "none (1 GPU)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": dec["total"],
+                     "mean_launch_us": round(kern_mean_ms * 1e3, 2),
+                     "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def describe_lengths(t) -> str:
+    L = t.context_lens
+    return f"min {int(L.min())} median {int(__import__('numpy').median(L))} max {int(L.max())}"
+
+
+def cpu_baseline(t, rep, budget_s: float):
+    """Float64 oracle on host copies of one replica, sequence by sequence until
+    the time budget is used (at least one sequence), one BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_oracle as po
+    from paged_kv_cache_119_amd import accounting as acc
+    from synth import to_bits
+
+    kp, vp, q, _, _, _ = rep
+    kb, vb, qb = to_bits(kp), to_bits(vp), to_bits(q)
+    done = []
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(t.num_seqs):
+            for h in range(t.num_heads):
+                po.decode_one(qb, kb, vb, t.block_tables, t.context_lens, t.scale, t.block_size, t.dtype, s, h)
+            done.append(s)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    lens = t.context_lens[done]
+    by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size)["total"]
+    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of {t.num_seqs} sequences (all {t.num_heads} heads), "
+                      f"{int(lens.sum())} KV tokens, {dt:.1f} s, numpy float64, 1 thread",
+            "kv_tokens_per_s": round(float(lens.sum()) / dt, 1)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

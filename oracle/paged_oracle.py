@@ -190,13 +190,10 @@ def gather(pool_bits, block_table_row, context_len: int, block_size: int, head: 
     [GA] "“逐个 block 做 gather”具体执行什么": look up the logical block's pool
     block, form the in-block address, read the row.
     """
-    D = pool_bits.shape[3]
-    out = np.empty((context_len, D), dtype=np.uint16)
-    for pos in range(context_len):
-        slot = slot_of(block_table_row, pos, block_size)
-        blk, off = divmod(slot, block_size)
-        out[pos] = pool_bits[blk, head, off, :]
-    return out
+    slots = [slot_of(block_table_row, pos, block_size) for pos in range(context_len)]
+    blk = np.array([x // block_size for x in slots], dtype=np.int64)
+    off = np.array([x % block_size for x in slots], dtype=np.int64)
+    return pool_bits[blk, head, off, :].copy()
 
 
 def attend(q64: np.ndarray, K64: np.ndarray, V64: np.ndarray, scale64: float):

@@ -1,0 +1,13 @@
+"""MI355X-native paged decode attention and paged KV-cache append.
+
+The computation runs in ``libpagedkv.so`` (hand-written HIP for gfx950, C ABI
+declared in ``include/pagedkv.h``); this package is a thin ctypes binding over
+it plus byte accounting for the roofline.  Build the library with
+``python -m paged_kv_cache_119_amd.build``.
+"""
+
+from ._binding import (EXPORTS, LIB_PATH, PagedKVError, PoolDesc, alloc_workspace,  # noqa: F401
+                       decode_merge, decode_partition_size, decode_partitions, decode_workspace_bytes,
+                       load_library, make_pool_desc, paged_attention_decode, pool_bytes, pool_desc_of,
+                       pool_index, reshape_and_cache, slot_mapping, status_string, version,
+                       workspace_views)

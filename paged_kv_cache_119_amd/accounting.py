@@ -75,3 +75,9 @@ def append_bytes(num_valid_tokens: int, num_tokens: int, num_heads: int, head_di
     write = 2 * num_valid_tokens * row
     slots = num_tokens * SLOT_BYTES
     return {"read": read, "write": write, "slots": slots, "total": read + write + slots}
+
+
+def slot_mapping_bytes(num_tokens: int) -> int:
+    """Slot translation: read (sequence, position) and one table entry, write
+    one int64 slot per token."""
+    return int(num_tokens) * (4 + 4 + TABLE_ENTRY_BYTES + SLOT_BYTES)

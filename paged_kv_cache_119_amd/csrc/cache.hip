@@ -1,0 +1,89 @@
+// Cache append and slot translation for gfx950.
+//
+// Append ("PagedAttention 完全拆解", 原理详解（三）, item 1, fused reshape and
+// block write): each new token's K and V rows, laid out [token][head][dim] as
+// projected, are written to pool[slot / B][head][slot % B][:] in one kernel.
+// Each thread moves one 16-byte piece of one (token, head) row of K and the
+// same piece of V; consecutive threads cover consecutive pieces of a row, so
+// reads and writes are both contiguous 16-byte accesses.
+//
+// Slot translation (iaim.asia block-table article, "KV Cache 如何按块分配",
+// BLOCK_SIZE=16 table): slot = block_tables[s][pos / B] * B + pos % B.
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+namespace {
+
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    uint16_t *__restrict__ kp, uint16_t *__restrict__ vp, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, int64_t k_stride, int64_t v_stride,
+    const int64_t *__restrict__ slots, int32_t T, int32_t Hkv, int32_t B, int32_t D,
+    int64_t num_blocks) {
+  const int vpr = D / 8;                       // 16-byte pieces per head row
+  const int64_t per_tok = (int64_t)Hkv * vpr;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * per_tok) return;
+  const int t = (int)(idx / per_tok);
+  const int r = (int)(idx - (int64_t)t * per_tok);
+  const int h = r / vpr;
+  const int piece = r - h * vpr;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * B) return;
+  const int64_t blk = slot / B;
+  const int64_t off = slot - blk * B;
+  const int64_t dst = ((blk * Hkv + h) * B + off) * D + piece * 8;
+  const u32x4 kv = *reinterpret_cast<const u32x4 *>(k + (int64_t)t * k_stride + h * D + piece * 8);
+  const u32x4 vv = *reinterpret_cast<const u32x4 *>(v + (int64_t)t * v_stride + h * D + piece * 8);
+  *reinterpret_cast<u32x4 *>(kp + dst) = kv;
+  *reinterpret_cast<u32x4 *>(vp + dst) = vv;
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(int64_t *__restrict__ slots,
+                                                           const int32_t *__restrict__ tables,
+                                                           int32_t S, int32_t maxb,
+                                                           const int32_t *__restrict__ seq,
+                                                           const int32_t *__restrict__ pos,
+                                                           int32_t T, int32_t B,
+                                                           int64_t num_blocks) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int s = seq[t];
+  const int x = pos[t];
+  int64_t out = -1;
+  if (s >= 0 && s < S && x >= 0 && x < maxb * B) {
+    const int32_t blk = tables[(int64_t)s * maxb + x / B];
+    if (blk >= 0 && (int64_t)blk < num_blocks) out = (int64_t)blk * B + x % B;
+  }
+  slots[t] = out;
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, const void *v,
+                                    int64_t k_stride, int64_t v_stride, const int64_t *slots,
+                                    int32_t T, int32_t Hkv, int32_t B, int32_t D,
+                                    int64_t num_blocks, hipStream_t stream) {
+  const int64_t threads = (int64_t)T * Hkv * (D / 8);
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<uint16_t *>(k_pool), reinterpret_cast<uint16_t *>(v_pool),
+                     reinterpret_cast<const uint16_t *>(k), reinterpret_cast<const uint16_t *>(v),
+                     k_stride, v_stride, slots, T, Hkv, B, D, num_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_mapping(int64_t *slots, const int32_t *tables, int32_t S, int32_t maxb,
+                               const int32_t *seq, const int32_t *pos, int32_t T, int32_t B,
+                               int64_t num_blocks, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int grid = (T + 255) / 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(256), 0, stream, slots, tables, S,
+                     maxb, seq, pos, T, B, num_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every symbol include/pagedkv.h declares,
+and its host-only entry points (sizes, indices, validation) behave as
+documented.  No kernel is launched: every call here returns before touching
+the GPU, so this runs on a CPU-only machine."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_119_amd as pkv
+from paged_kv_cache_119_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from paged_kv_cache_119_amd.build import build
+        build()
+    return bd.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(bd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert pkv.version() == 1
+    for code in range(6):
+        assert len(pkv.status_string(code)) > 0
+    assert pkv.status_string(99) == "unknown status"
+
+
+def test_pool_bytes_and_index(lib):
+    assert pkv.pool_bytes(2300, 16, 40, 128, "f16") == 2300 * 40 * 16 * 128 * 2
+    assert pkv.pool_bytes(10, 12, 4, 64) == 0          # unsupported block size
+    assert pkv.pool_bytes(10, 16, 4, 96) == 0          # unsupported head_dim
+    d = pkv.make_pool_desc(10, 16, 4, 64, "bf16")
+    assert pkv.pool_index(d, 2, 1, 3, 5) == ((2 * 4 + 1) * 16 + 3) * 64 + 5
+    assert pkv.pool_index(d, 0, 0, 0, 0) == 0
+    assert pkv.pool_index(d, 9, 3, 15, 63) == 10 * 4 * 16 * 64 - 1
+    for bad in ((10, 0, 0, 0), (-1, 0, 0, 0), (0, 4, 0, 0), (0, 0, 16, 0), (0, 0, 0, 64)):
+        assert pkv.pool_index(d, *bad) == -1
+
+
+def _desc(N=100, B=16, H=4, D=128, dt="f16"):
+    return pkv.make_pool_desc(N, B, H, D, dt)
+
+
+def test_partition_size_rules(lib):
+    f = lib.pkv_decode_partition_size
+    d = _desc()
+    assert f(8, 4, 128, ctypes.byref(d), 0) == 512                 # long tables: 512
+    assert f(8, 4, 13, ctypes.byref(d), 0) == 208                  # short: one partition
+    assert f(8, 4, 13, ctypes.byref(_desc(D=64)), 0) == 224        # D = 64 steps are 32 tokens
+    assert f(8, 4, 128, ctypes.byref(d), 256) == 256
+    assert f(8, 4, 128, ctypes.byref(d), 24) == 0                  # not a multiple of 16
+    assert f(8, 4, 128, ctypes.byref(_desc(B=64)), 32) == 0        # not a multiple of B
+    assert f(8, 4, 128, ctypes.byref(_desc(B=8)), 8192) == 0       # P / B > 512
+    assert f(8, 5, 128, ctypes.byref(d), 0) == 0                   # heads != kv heads
+
+
+def test_workspace_bytes(lib):
+    f = lib.pkv_decode_workspace_bytes
+    d = _desc(D=128)
+    assert f(8, 4, 13, ctypes.byref(d), 0) == 0                    # single partition: none
+    S, H, maxb, P = 64, 4, 128, 512
+    MP = maxb * 16 // P
+    U = S * H * MP
+    sec = -(-U * 4 // 256) * 256
+    assert f(S, H, maxb, ctypes.byref(d), P) == 2 * sec + -(-U * 128 * 4 // 256) * 256
+
+
+def test_validation_returns_status_before_any_launch(lib):
+    d = _desc()
+    nul = None
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, ctypes.byref(d), 0,
+                                        nul, 0, nul)
+    assert st == 1                                                  # PKV_ERR_NULL
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, None, 0, nul, 0, nul)
+    assert st == 1
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, -1, 4, 8, ctypes.byref(d), 0,
+                                        nul, 0, nul)
+    assert st == 2                                                  # PKV_ERR_SHAPE
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 8, 8, ctypes.byref(d), 0,
+                                        nul, 0, nul)
+    assert st == 3                                                  # GQA not supported yet
+    bad = _desc(B=12)
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, ctypes.byref(bad), 0,
+                                        nul, 0, nul)
+    assert st == 3
+    # a multi-partition call with fake (never dereferenced) pointers and no workspace
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, fake, 1.0, 4, 4, 128,
+                                        ctypes.byref(d), 256, nul, 0, nul)
+    assert st == 4                                                  # PKV_ERR_WORKSPACE
+    # misaligned q
+    st = lib.pkv_paged_attention_decode(fake, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, fake, 1.0,
+                                        4, 4, 8, ctypes.byref(d), 0, nul, 0, nul)
+    assert st == 2
+    # zero sequences is a no-op that succeeds without touching anything
+    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 0, 4, 8, ctypes.byref(d), 0,
+                                        nul, 0, nul)
+    assert st == 0
+
+
+def test_append_validation(lib):
+    d = _desc()
+    nul = None
+    assert lib.pkv_reshape_and_cache(nul, nul, nul, nul, 0, 0, nul, 0, ctypes.byref(d), nul) == 0
+    assert lib.pkv_reshape_and_cache(nul, nul, nul, nul, 0, 0, nul, 5, ctypes.byref(d), nul) == 1
+    assert lib.pkv_reshape_and_cache(nul, nul, nul, nul, 0, 0, nul, -1, ctypes.byref(d), nul) == 2
+    fake = ctypes.c_void_p(1 << 20)
+    # token stride shorter than a row
+    assert lib.pkv_reshape_and_cache(fake, fake, fake, fake, 8, 0, fake, 5, ctypes.byref(d), nul) == 2
+    assert lib.pkv_slot_mapping(nul, nul, 4, 8, nul, nul, 0, ctypes.byref(d), nul) == 0
+    assert lib.pkv_slot_mapping(nul, nul, 4, 8, nul, nul, 3, ctypes.byref(d), nul) == 1
+    assert lib.pkv_slot_mapping(fake, fake, 4, 0, fake, fake, 3, ctypes.byref(d), nul) == 2
+
+
+def test_product_path_never_imports_the_oracle():
+    """The library package must not reach the CPU oracle in any form."""
+    pkg = os.path.join(ROOT, "paged_kv_cache_119_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert not re.search(r"(import\s+oracle|from\s+oracle|oracle\.)", text), fn
+                assert "paged_oracle" not in text, fn

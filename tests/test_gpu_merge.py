@@ -1,0 +1,92 @@
+"""GPU: the split-context row on its own -- the partition pass's partial
+results against the oracle's partials, and the merge pass fed with the
+oracle's partials against the oracle's log-sum-exp merge."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_119_amd as pkv  # noqa: E402
+from oracle import paged_oracle as po  # noqa: E402
+from synth import build_tables, make_pools, make_query, to_bits  # noqa: E402
+
+from .gpu_util import DEV, assert_close, device_tables, log  # noqa: E402
+
+LENGTHS = [1, 100, 256, 257, 700, 1024, 1500, 2048, 33, 512]
+P = 256
+
+
+def _case(dtype="f16", D=128, B=16):
+    t = build_tables(params=dict(name="merge", index=50, num_heads=2, head_dim=D, dtype=dtype, block_size=B,
+                                 num_seqs=len(LENGTHS), lengths=("fixed", LENGTHS), pool=("slack", 1.2),
+                                 tables="permute", max_len=2048))
+    return t
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_partition_pass_partials_match_oracle(dtype):
+    log(f"partition pass partials {dtype}")
+    t = _case(dtype)
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    out = torch.zeros_like(q)
+    ws = pkv.alloc_workspace(t.num_seqs, t.num_heads, t.max_blocks, kp, P)
+    pkv.decode_partitions(q, kp, vp, tab, lens, t.scale, out, ws, partition_size=P)
+    torch.cuda.synchronize()
+    m, l, o = pkv.workspace_views(ws, t.num_seqs, t.num_heads, t.max_blocks, kp, P)
+    m, l, o = m.cpu().numpy(), l.cpu().numpy(), o.cpu().numpy()
+    qb, kb, vb = to_bits(q), to_bits(kp), to_bits(vp)
+    ob = to_bits(out)
+    for s, L in enumerate(LENGTHS):
+        n = -(-L // P)
+        for h in range(t.num_heads):
+            if n == 1:
+                ref = po.decode_one(qb, kb, vb, t.block_tables, t.context_lens, t.scale, t.block_size, dtype, s, h)
+                assert_close(ob[s, h][None], ref[None], dtype, f"single-partition row s={s} h={h}")
+                continue
+            rm, rl, ro = po.partials(qb, kb, vb, t.block_tables, t.context_lens, t.scale, t.block_size, dtype,
+                                     P, s, h)
+            np.testing.assert_allclose(m[s, h, :n], rm, rtol=1e-5, atol=1e-5)
+            # l and o are relative to each side's own max; rescale to the oracle's
+            f = np.exp(m[s, h, :n].astype(np.float64) - rm)
+            np.testing.assert_allclose(l[s, h, :n] * f, rl, rtol=1e-4)
+            np.testing.assert_allclose(o[s, h, :n] * f[:, None], ro, rtol=1e-3, atol=1e-3 * rl[:, None])
+            assert np.all(ob[s, h] == 0)  # untouched by the partition pass
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_merge_pass_on_oracle_partials(dtype):
+    log(f"merge pass on oracle partials {dtype}")
+    t = _case(dtype)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    qb, kb, vb = to_bits(q), to_bits(kp), to_bits(vp)
+    ws = pkv.alloc_workspace(t.num_seqs, t.num_heads, t.max_blocks, kp, P)
+    ws.zero_()
+    m, l, o = pkv.workspace_views(ws, t.num_seqs, t.num_heads, t.max_blocks, kp, P)
+    ref = np.zeros((t.num_seqs, t.num_heads, t.head_dim))
+    multi = []
+    for s, L in enumerate(LENGTHS):
+        n = -(-L // P)
+        if n < 2:
+            continue
+        multi.append(s)
+        for h in range(t.num_heads):
+            rm, rl, ro = po.partials(qb, kb, vb, t.block_tables, t.context_lens, t.scale, t.block_size, dtype,
+                                     P, s, h)
+            m[s, h, :n] = torch.from_numpy(rm.astype(np.float32))
+            l[s, h, :n] = torch.from_numpy(rl.astype(np.float32))
+            o[s, h, :n] = torch.from_numpy(ro.astype(np.float32))
+            ref[s, h] = po.lse_merge(rm, rl, ro)
+    out = torch.zeros_like(q)
+    _, lens = device_tables(t)
+    pkv.decode_merge(out, lens, t.max_blocks, kp, ws, partition_size=P)
+    torch.cuda.synchronize()
+    ob = to_bits(out)
+    assert_close(ob[multi], ref[multi], dtype, "merge")
+    single = [s for s in range(t.num_seqs) if s not in multi]
+    assert np.all(ob[single] == 0)  # rows with one partition are not the merge's
