@@ -54,7 +54,8 @@ def test_partition_pass_partials_match_oracle(dtype):
             # l and o are relative to each side's own max; rescale to the oracle's
             f = np.exp(m[s, h, :n].astype(np.float64) - rm)
             np.testing.assert_allclose(l[s, h, :n] * f, rl, rtol=1e-4)
-            np.testing.assert_allclose(o[s, h, :n] * f[:, None], ro, rtol=1e-3, atol=1e-3 * rl[:, None])
+            err = np.abs(o[s, h, :n] * f[:, None] - ro)
+            assert np.all(err <= 1e-3 * np.abs(ro) + 1e-4 * rl[:, None]), (s, h, float(err.max()))
             assert np.all(ob[s, h] == 0)  # untouched by the partition pass
 
 
