@@ -24,14 +24,12 @@
 //    lane), so the hot loop has no cross-group traffic at all.  Groups and
 //    waves are merged once at the end, by the same log-sum-exp rule.
 //  * Chunks go round-robin over the waves; each wave double-buffers its
-//    chunks (loads of chunk c + NW are issued before chunk c is consumed).
+//    chunks (the loads of chunk c + NW are issued before chunk c is consumed).
 //  * exp2 runs on v_exp_f32 with log2(e) folded into the scale.
 //  * Unused slots of the last block are selected out (score -inf, V term
 //    skipped), never multiplied by zero, so NaN in them cannot leak.
 //  * The accumulation order depends only on logical positions, so results are
 //    bitwise independent of where blocks sit in the pool.
-
-#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -40,13 +38,21 @@ namespace pkv {
 
 namespace {
 
-constexpr int kNumWaves = 4;
+// Wavefronts per workgroup of the partition pass (build-time setting).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kNumWaves = PKV_DECODE_WAVES;
+// 16-byte loads per lane per tensor in one wavefront step (build-time setting).
+#ifndef PKV_DECODE_LOADS
+#define PKV_DECODE_LOADS 4
+#endif
 
 template <int DT, int D, int B, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams a) {
   constexpr int LPT = D / 8;    // lanes per token row
   constexpr int TPI = 64 / LPT; // token rows per load instruction
-  constexpr int NL = 4;         // load instructions per tensor per chunk
+  constexpr int NL = PKV_DECODE_LOADS;  // load instructions per tensor per chunk
   constexpr int TC = NL * TPI;  // tokens per chunk
   static_assert(B % TPI == 0, "a load must not straddle two blocks");
 
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int L = a.lens[s];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)s * a.H + h) * D;
 
@@ -91,7 +97,8 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
   const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k_pool);
   const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v_pool);
   const int64_t blk_stride = (int64_t)a.Hkv * B * D;  // elements per pool block
-  const int64_t head_off = (int64_t)h * B * D + lane * 8;
+  const int64_t head_base = (int64_t)h * B * D;       // scalar part of the tile offset
+  const int lane_off = lane * 8;                       // this lane's 8 elements
   const int row = lane / LPT;
 
   const u32x4 qv = *reinterpret_cast<const u32x4 *>(
@@ -104,46 +111,55 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
+  // Issue the 2 * NL loads of chunk c.  Every address is a scalar base (block
+  // id from LDS, moved to a scalar register) plus this lane's 16-byte offset.
   auto load_chunk = [&](int c, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int lt = c * TC + i * TPI;            // first token of this load
-      const int lb = min(lt / B, nblk - 1);       // clamp: never past the last entry
+      int lb, off;
+      if constexpr (TC >= B) {  // a chunk covers TC / B whole blocks
+        lb = c * (TC / B) + (i * TPI) / B;
+        off = (i * TPI) % B;
+      } else {                  // a block holds B / TC chunks
+        lb = c / (B / TC);
+        off = (c % (B / TC)) * TC + i * TPI;
+      }
+      lb = min(lb, nblk - 1);   // tail loads stay inside the last block
       int blk = __builtin_amdgcn_readfirstlane(s_tab[lb]);
       if (blk < 0 || (int64_t)blk >= a.num_blocks) {
         bad = true;
         blk = 0;
       }
-      const int64_t e = (int64_t)blk * blk_stride + head_off + (lt % B) * D;
-      kr[i] = *reinterpret_cast<const u32x4 *>(kp + e);
-      vr[i] = *reinterpret_cast<const u32x4 *>(vp + e);
+      const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
+      kr[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
+      vr[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
     }
   };
 
-  auto consume = [&](int c, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL], auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
+  // Fold chunk c into this lane group's online softmax.  Branch-free: rows at
+  // or past n get score -inf and a zeroed V row (selected, never multiplied),
+  // so the poison in unused slots cannot leak.
+  auto consume = [&](int c, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
     float z[NL];
-    bool valid[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      z[i] = group_sum<LPT>(dot8<DT>(qv, kr[i])) * a.scale_log2;
-      valid[i] = true;
-      if constexpr (kMasked) {
-        valid[i] = (c * TC + i * TPI + row) < n;
-        z[i] = valid[i] ? z[i] : kNegInf;
-      }
+      const bool valid = (c * TC + i * TPI + row) < n;
+      const float d = group_sum<LPT>(dot8<DT>(qv, kr[i])) * a.scale_log2;
+      z[i] = valid ? d : kNegInf;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      vr[i] = valid ? vr[i] : zero;
     }
     float mx = z[0];
 #pragma unroll
     for (int i = 1; i < NL; ++i) mx = fmaxf(mx, z[i]);
     const float mnew = fmaxf(m, mx);
-    if (mnew == kNegInf) return;  // nothing valid in this lane group yet
-    const float alpha = fast_exp2(m - mnew);  // m == -inf gives 0
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
+    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
     float pz[NL];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      pz[i] = fast_exp2(z[i] - mnew);  // masked: 2^-inf = 0
+      pz[i] = fast_exp2(z[i] - mref);  // -inf gives 0
       psum += pz[i];
     }
     l = l * alpha + psum;
@@ -154,38 +170,42 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
       const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v0 = lo16<DT>(w[j]);
-        const float v1 = hi16<DT>(w[j]);
-        if constexpr (kMasked) {
-          acc[2 * j] = valid[i] ? fmaf(pz[i], v0, acc[2 * j]) : acc[2 * j];
-          acc[2 * j + 1] = valid[i] ? fmaf(pz[i], v1, acc[2 * j + 1]) : acc[2 * j + 1];
-        } else {
-          acc[2 * j] = fmaf(pz[i], v0, acc[2 * j]);
-          acc[2 * j + 1] = fmaf(pz[i], v1, acc[2 * j + 1]);
-        }
+        acc[2 * j] = fmaf(pz[i], lo16<DT>(w[j]), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(pz[i], hi16<DT>(w[j]), acc[2 * j + 1]);
       }
     }
     m = mnew;
   };
 
-  using Full = std::integral_constant<bool, false>;
-  using Masked = std::integral_constant<bool, true>;
-
+  // This wave's chunks are c_k = wave + k * NW, k < my_n; two are in flight at
+  // a time.  The loop body always runs both halves and has a single back
+  // edge, so the same loads are outstanding on every path into it and the
+  // wait before each consume leaves the other chunk's 2 * NL loads in flight.
   const int nch = (n + TC - 1) / TC;
-  u32x4 ka[NL], va[NL], kb[NL], vb[NL];
-  int c = wave;
-  if (c < nch) load_chunk(c, ka, va);
-  while (c < nch) {
-    const int c1 = c + NW;
-    if (c1 < nch) load_chunk(c1, kb, vb);
-    if ((c + 1) * TC <= n) consume(c, ka, va, Full{});
-    else consume(c, ka, va, Masked{});
-    if (c1 >= nch) break;
-    const int c2 = c1 + NW;
-    if (c2 < nch) load_chunk(c2, ka, va);
-    if ((c1 + 1) * TC <= n) consume(c1, kb, vb, Full{});
-    else consume(c1, kb, vb, Masked{});
-    c = c2;
+  if (wave < nch) {
+    const int my_n = (nch - wave + NW - 1) / NW;
+    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+    load_chunk(wave, ka, va);
+    int k = 0;
+    for (; k + 2 < my_n; k += 2) {
+      const int c = wave + k * NW;
+      load_chunk(c + NW, kb, vb);
+      // keep the prefetch ahead of the consume (the scheduler would sink it)
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c, ka, va);
+      load_chunk(c + 2 * NW, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c + NW, kb, vb);
+    }
+    const int c = wave + k * NW;
+    if (k + 1 < my_n) {
+      load_chunk(c + NW, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c, ka, va);
+      consume(c + NW, kb, vb);
+    } else {
+      consume(c, ka, va);
+    }
   }
 
   // Merge the lane groups of this wave (same dims, different tokens).

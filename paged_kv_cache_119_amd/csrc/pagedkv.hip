@@ -28,7 +28,10 @@ bool pool_ok(const pkv_pool *p) {
 }
 
 // Tokens one wavefront step of the partition kernel covers.
-int chunk_tokens(int head_dim) { return 4 * (64 / (head_dim / 8)); }
+#ifndef PKV_DECODE_LOADS
+#define PKV_DECODE_LOADS 4
+#endif
+int chunk_tokens(int head_dim) { return PKV_DECODE_LOADS * (64 / (head_dim / 8)); }
 
 int partition_unit(const pkv_pool *p) {
   const int tc = chunk_tokens(p->head_dim);
