@@ -22,13 +22,15 @@
  *  - Every data pointer is a DEVICE pointer unless stated otherwise; every
  *    struct pointer (pkv_pool) is a HOST pointer read during the call only.
  *  - The caller owns all memory, including the decode workspace.  The library
- *    allocates nothing, keeps no pointer after a call returns, holds no global
- *    mutable state and never synchronises: each call only enqueues kernels on
- *    `stream` (a hipStream_t; NULL means the default stream) and returns.
- *    Calls are thread-safe.
+ *    allocates no device memory and keeps no pointer after a call returns.
+ *    Its only state is a cache of each device's compute-unit count and of the
+ *    decode kernels' occupancy, filled on first use under a lock.  It never
+ *    synchronises: each call only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL means the default stream) of the current device and
+ *    returns.  Calls are thread-safe.
  *  - Host-side validation runs before anything is enqueued; a call that
- *    returns an error status has enqueued nothing.  PKV_ERR_HIP means a launch
- *    was rejected by the runtime.
+ *    returns an error status has enqueued nothing.  PKV_ERR_HIP means the
+ *    runtime rejected a launch or a device query.
  *  - Element types: 16-bit IEEE binary16 (PKV_F16) or bfloat16 (PKV_BF16).
  *    Arithmetic is float32 with exact products; outputs are rounded to the
  *    element type, nearest-even.
@@ -135,20 +137,36 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
                                  const pkv_pool *p, void *stream);
 
 /*
- * Partition size and workspace.
+ * How the context is split, and the workspace.
  *
- * partition_size P (tokens) splits each sequence's context into chunks of P
- * tokens processed by separate workgroups.  P must be a multiple of B and of
- * the 16 (D = 128) or 32 (D = 64) tokens one wavefront step covers, with
- * P / B <= 512.  0 selects a size from (num_seqs, num_heads, max_blocks, B, D).
- * pkv_decode_partition_size() returns the size a call would use (0 if the
- * arguments are invalid).
+ * partition_size selects how each sequence's context is cut into pieces that
+ * run in parallel before the log-sum-exp merge:
  *
- * Workspace layout (float32), with MP = ceil(max_blocks_per_seq * B / P) and
- * U = num_seqs * num_heads * MP, unit u = (s * num_heads + h) * MP + p:
+ *  - partition_size > 0: fixed partitions of P tokens, partition p holding
+ *    tokens [p*P, min((p+1)*P, L)).  P must be a multiple of B and of the 16
+ *    (D = 128) or 32 (D = 64) tokens one wavefront step covers, with P / B <= 512.
+ *  - partition_size == 0: a work-balanced split.  Every wavefront the device
+ *    holds at once takes an equal share of all (sequence, head, token) work,
+ *    each (sequence, head) also costing a fixed overhead, so batches with very
+ *    different context lengths keep every compute unit busy.  The cut points
+ *    depend on the context lengths and on the device (compute units and
+ *    occupancy), so results are identical run to run on one device and build.
+ *    Batches of more than 4096 sequences fall back to fixed partitions of 512.
+ *
+ * pkv_decode_partition_size() returns the P a call uses: P > 0 for fixed
+ * partitions, 0 for the balanced split, -1 if the arguments are invalid.
+ * pkv_decode_workspace_bytes() returns the workspace a call needs (0 when none
+ * is needed or the arguments are invalid; the balanced split always needs
+ * one, and its size depends on the current device).
+ *
+ * Workspace layout of fixed partitions (float32), with
+ * MP = ceil(max_blocks_per_seq * B / P) and U = num_seqs * num_heads * MP,
+ * unit u = (s * num_heads + h) * MP + p:
  *   [ m: U floats ][ l: U floats ][ o: U * D floats ], each section starting on
  *   a 256-byte boundary.  m is the partition's largest score z = scale * q.k
  *   (natural-log units), l = sum exp(z - m), o = sum exp(z - m) * v.
+ * The balanced split's workspace holds a cost prefix and per-piece partial
+ * results in the same (m, l, o) form; its layout is internal.
  */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                   const pkv_pool *p, int32_t partition_size);
@@ -174,13 +192,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *   context_lens  int32 [num_seqs]
  *   scale         float32, normally 1 / sqrt(D)
  *   num_heads     query heads; must equal Hkv in this version
+ *   out           must be 16-byte aligned
  *   workspace     >= pkv_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                 may be NULL only when that size is 0
  *
- * Runs the partition pass, then (only if some sequence may span several
- * partitions) the merge pass, both on `stream`.  Deterministic: the result
- * depends only on logical positions, not on where blocks sit in the pool or
- * whether they are shared.
+ * Runs the split pass, then (when some row may be split) the merge pass, both
+ * on `stream`.  Deterministic: on a given device the result depends only on
+ * logical positions, not on where blocks sit in the pool or whether they are
+ * shared.
  *
  * Device-side data rules: L == 0 gives a zero row; L < 0 or
  * L > max_blocks_per_seq * B gives a NaN row; a needed table entry outside
@@ -196,11 +215,15 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                       size_t workspace_bytes, void *stream);
 
 /*
- * pkv_decode_partitions -- the partition pass of pkv_paged_attention_decode on
- * its own.  Sequences with ceil(L / P) <= 1 get their final output row in
- * `out`; for every other sequence each partition p < ceil(L / P) writes its
- * partial (m, l, o) into the workspace (layout above) and `out` is untouched.
- * Same arguments and rules as pkv_paged_attention_decode.
+ * pkv_decode_partitions -- the split pass of pkv_paged_attention_decode on its
+ * own.  With fixed partitions (P > 0): sequences with ceil(L / P) <= 1 get
+ * their final output row in `out`, rows of empty (L == 0) or invalid contexts
+ * are written as described above, and for every other sequence each partition
+ * p < ceil(L / P) writes its partial (m, l, o) into the workspace (layout
+ * above) while its `out` row is untouched.  With the balanced split (P == 0):
+ * every (sequence, head) handled in one piece gets its output row, the others
+ * leave partials; the merge pass completes the output.  Same arguments and
+ * rules as pkv_paged_attention_decode.
  */
 pkv_status pkv_decode_partitions(void *out, const void *q, const void *k_pool, const void *v_pool,
                                  const int32_t *block_tables, const int32_t *context_lens,
@@ -210,11 +233,14 @@ pkv_status pkv_decode_partitions(void *out, const void *q, const void *k_pool, c
                                  void *stream);
 
 /*
- * pkv_decode_merge -- the merge pass on its own.  For every sequence with
- * n = ceil(L / P) >= 2 partitions and 0 <= L <= max_blocks_per_seq * B:
+ * pkv_decode_merge -- the merge pass on its own.  With fixed partitions, for
+ * every sequence with n = ceil(L / P) >= 2 partitions and
+ * 0 <= L <= max_blocks_per_seq * B:
  *   M = max_p m_p,  out[s][h] = sum_p exp(m_p - M) o_p / sum_p exp(m_p - M) l_p,
- * reading partials p < n from the workspace.  Other rows of `out` are not
- * touched.  Arguments as in pkv_paged_attention_decode.
+ * reading partials p < n from the workspace; other rows of `out` are not
+ * touched.  With the balanced split it merges the (sequence, head) rows that
+ * were cut into several pieces and writes the rows of empty or invalid
+ * contexts.  Arguments as in pkv_paged_attention_decode.
  */
 pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_seqs,
                             int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,

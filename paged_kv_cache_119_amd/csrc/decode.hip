@@ -1,33 +1,48 @@
-// Paged decode attention for gfx950: partition pass + log-sum-exp merge pass.
+// Paged decode attention for gfx950: split-context pass + log-sum-exp merge.
 //
 // What is computed ("PagedAttention 完全拆解", 背景 attention equation and
 // 原理详解（二） blockwise form): for each sequence s and head h,
 //   o = sum_j exp(z_j - m) v_j / sum_j exp(z_j - m),   z_j = scale * q . k_j,
 // over the sequence's logical tokens j < L, with k_j and v_j found through the
-// block table.  Long contexts are cut into partitions of P tokens whose
+// block table.  The context is cut into pieces processed in parallel whose
 // partial results are merged afterwards (iaim.asia block-table article,
 // "vLLM 内核里的缓解写法": segments in parallel, then a reduction).
 //
-// Mapping to CDNA4 (this is our design, not the pages' warp-per-block one):
-//  * One workgroup of NW wavefronts per (sequence, head, partition).  The
-//    partition's table entries are staged in LDS with one coalesced load;
-//    waves then read the (wave-uniform) block id from LDS, so the pool address
-//    base lives in scalar registers.
-//  * A wavefront step ("chunk") covers TC tokens: NL = 4 loads of 16 bytes per
-//    lane from K and 4 from V.  With the [N][Hkv][B][D] layout a load
-//    instruction reads 1 KiB of consecutive bytes (TPI whole token rows of one
-//    block), so every load is fully coalesced however blocks are scattered.
-//  * LPT = D / 8 lanes hold one token's row (8 elements each); the q.k partial
+// Two ways of cutting, one inner engine:
+//  * Fixed partitions (partition_size P > 0): one workgroup of NW wavefronts
+//    per (sequence, head, partition of P tokens); the partition's table
+//    entries are staged in LDS once and the waves take chunks round-robin.
+//  * Work-balanced (partition_size 0): every wavefront of a grid sized to
+//    what the GPU holds at once is a worker that owns an equal slice of the
+//    flattened (sequence, head, chunk) space, where each (sequence, head)
+//    also costs a fixed overhead of kPieceChunks chunks.  A worker
+//    turns its slice into pieces (one per (sequence, head) it touches),
+//    stages each piece's table entries in its own LDS window and streams it.
+//    Batches with very different context lengths therefore load every CU
+//    evenly, with no empty workgroups and no long tail.  No atomics and no
+//    inter-workgroup synchronisation: a piece that is not a whole (sequence,
+//    head) writes a partial result that a second launch merges.
+//
+// Inner engine (WaveAttn), per wavefront:
+//  * A "chunk" covers TC tokens: NL loads of 16 bytes per lane from K and NL
+//    from V.  With the [N][Hkv][B][D] pool layout one load instruction reads
+//    1 KiB of consecutive bytes (TPI whole token rows of one block), so every
+//    load is fully coalesced however the blocks are scattered.  Each address
+//    is a scalar tile base (block id read from LDS, moved to a scalar
+//    register) plus the lane's 16-byte offset.
+//  * LPT = D / 8 lanes hold one token row (8 elements each); the q.k partial
 //    sums of those lanes are reduced with DPP inside the 16-lane row.  The TPI
-//    token rows of a load stay in separate lane groups, and each group keeps
-//    its own online-softmax state (running max m, sum l, 8 accumulators per
-//    lane), so the hot loop has no cross-group traffic at all.  Groups and
-//    waves are merged once at the end, by the same log-sum-exp rule.
-//  * Chunks go round-robin over the waves; each wave double-buffers its
-//    chunks (the loads of chunk c + NW are issued before chunk c is consumed).
+//    token rows of a load stay in separate lane groups, each with its own
+//    online softmax (running max m, sum l, 8 accumulators per lane), so the
+//    hot loop has no other cross-lane traffic.  Groups are merged once at the
+//    end by the log-sum-exp rule.
+//  * Chunks are double-buffered: the loads of the next chunk are issued before
+//    the current one is consumed (a counted loop with one back edge keeps the
+//    compiler's wait at exactly one chunk outstanding).
 //  * exp2 runs on v_exp_f32 with log2(e) folded into the scale.
-//  * Unused slots of the last block are selected out (score -inf, V term
-//    skipped), never multiplied by zero, so NaN in them cannot leak.
+//  * Tokens outside the piece (the unused tail of a last block included) are
+//    selected out -- score -inf, V row zeroed -- never multiplied by zero, so
+//    NaN in unused slots cannot leak.
 //  * The accumulation order depends only on logical positions, so results are
 //    bitwise independent of where blocks sit in the pool.
 
@@ -38,23 +53,183 @@ namespace pkv {
 
 namespace {
 
-// Wavefronts per workgroup of the partition pass (build-time setting).
-#ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
-#endif
 constexpr int kNumWaves = PKV_DECODE_WAVES;
-// 16-byte loads per lane per tensor in one wavefront step (build-time setting).
-#ifndef PKV_DECODE_LOADS
-#define PKV_DECODE_LOADS 4
-#endif
+
+template <int D>
+struct Geo {
+  static constexpr int LPT = D / 8;          // lanes per token row
+  static constexpr int TPI = 64 / LPT;       // token rows per load instruction
+  static constexpr int NL = kDecodeLoads;    // loads per tensor per chunk
+  static constexpr int TC = NL * TPI;        // tokens per chunk
+};
+
+// One wavefront's online softmax over part of one (sequence, head).
+template <int DT, int D, int B>
+struct WaveAttn {
+  using G = Geo<D>;
+  static constexpr int LPT = G::LPT, TPI = G::TPI, NL = G::NL, TC = G::TC;
+  static_assert(B % TPI == 0, "a load must not straddle two blocks");
+
+  const uint16_t *kp;
+  const uint16_t *vp;
+  int64_t blk_stride;   // elements per pool block (all heads)
+  int64_t head_base;    // offset of this head's tile inside a block
+  int64_t num_blocks;
+  float scale_log2;
+  int lane_off;         // this lane's 8 elements inside a 1 KiB load
+  int row;              // lane group (token row of a load)
+  u32x4 qv;
+  bool bad;
+  float m, l;
+  float acc[8];
+
+  __device__ __forceinline__ void init(const DecodeParams &a, int s, int h, int lane) {
+    kp = reinterpret_cast<const uint16_t *>(a.k_pool);
+    vp = reinterpret_cast<const uint16_t *>(a.v_pool);
+    blk_stride = (int64_t)a.Hkv * B * D;
+    head_base = (int64_t)h * B * D;
+    num_blocks = a.num_blocks;
+    scale_log2 = a.scale_log2;
+    lane_off = lane * 8;
+    row = lane / LPT;
+    qv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) +
+                                          ((int64_t)s * a.H + h) * D + (lane % LPT) * 8);
+    bad = false;
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  }
+
+  // Issue the 2 * NL loads of chunk c (tokens c*TC .. c*TC+TC-1 of the
+  // sequence).  `tab` holds the table entries of logical blocks tab_base ..;
+  // logical blocks past lb_max are clamped to it (their tokens are masked).
+  __device__ __forceinline__ void load(int c, const int32_t *tab, int tab_base, int lb_max,
+                                       u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      int lb, off;
+      if constexpr (TC >= B) {  // a chunk covers TC / B whole blocks
+        lb = c * (TC / B) + (i * TPI) / B;
+        off = (i * TPI) % B;
+      } else {                  // a block holds B / TC chunks
+        lb = c / (B / TC);
+        off = (c % (B / TC)) * TC + i * TPI;
+      }
+      lb = min(lb, lb_max);
+      int blk = __builtin_amdgcn_readfirstlane(tab[lb - tab_base]);
+      if (blk < 0 || (int64_t)blk >= num_blocks) {
+        bad = true;
+        blk = 0;
+      }
+      const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
+      kr[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
+      vr[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+    }
+  }
+
+  // Fold chunk c into this lane group's online softmax; tokens outside
+  // [t_lo, t_hi) are selected out.  Branch-free.
+  __device__ __forceinline__ void consume(int c, int t_lo, int t_hi, u32x4 (&kr)[NL],
+                                          u32x4 (&vr)[NL]) {
+    float z[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int tok = c * TC + i * TPI + row;
+      const bool valid = tok >= t_lo && tok < t_hi;
+      const float d = group_sum<LPT>(dot8<DT>(qv, kr[i])) * scale_log2;
+      z[i] = valid ? d : kNegInf;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      vr[i] = valid ? vr[i] : zero;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mx = fmaxf(mx, z[i]);
+    const float mnew = fmaxf(m, mx);
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
+    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
+    float pz[NL];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      pz[i] = fast_exp2(z[i] - mref);  // -inf gives 0
+      psum += pz[i];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(pz[i], lo16<DT>(w[j]), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(pz[i], hi16<DT>(w[j]), acc[2 * j + 1]);
+      }
+    }
+    m = mnew;
+  }
+
+  // Chunks c0, c0 + stride, ... (count of them), two in flight.  The loop
+  // body always runs both halves and has a single back edge, so the same loads
+  // are outstanding on every path into it and the wait before each consume
+  // leaves the other chunk's 2 * NL loads in flight.
+  __device__ __forceinline__ void run(int c0, int stride, int count, const int32_t *tab,
+                                      int tab_base, int lb_max, int t_lo, int t_hi) {
+    if (count <= 0) return;
+    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+    load(c0, tab, tab_base, lb_max, ka, va);
+    int k = 0;
+    for (; k + 2 < count; k += 2) {
+      const int c = c0 + k * stride;
+      load(c + stride, tab, tab_base, lb_max, kb, vb);
+      // keep the prefetch ahead of the consume (the scheduler would sink it)
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c, t_lo, t_hi, ka, va);
+      load(c + 2 * stride, tab, tab_base, lb_max, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c + stride, t_lo, t_hi, kb, vb);
+    }
+    const int c = c0 + k * stride;
+    if (k + 1 < count) {
+      load(c + stride, tab, tab_base, lb_max, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(c, t_lo, t_hi, ka, va);
+      consume(c + stride, t_lo, t_hi, kb, vb);
+    } else {
+      consume(c, t_lo, t_hi, ka, va);
+    }
+  }
+
+  // Merge the lane groups (same dims, different tokens); afterwards every lane
+  // group holds the wave's (m, l, acc).
+  __device__ __forceinline__ void merge_groups() {
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const float l2 = __shfl_xor(l, off);
+      const float mm = fmaxf(m, m2);
+      const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
+      const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
+      l = l * f1 + l2 * f2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o2 = __shfl_xor(acc[j], off);
+        acc[j] = acc[j] * f1 + o2 * f2;
+      }
+      m = mm;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fixed partitions
+// ---------------------------------------------------------------------------
 
 template <int DT, int D, int B, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams a) {
-  constexpr int LPT = D / 8;    // lanes per token row
-  constexpr int TPI = 64 / LPT; // token rows per load instruction
-  constexpr int NL = PKV_DECODE_LOADS;  // load instructions per tensor per chunk
-  constexpr int TC = NL * TPI;  // tokens per chunk
-  static_assert(B % TPI == 0, "a load must not straddle two blocks");
+  using WA = WaveAttn<DT, D, B>;
+  constexpr int TC = WA::TC;
 
   __shared__ int32_t s_tab[kTabMax];
   __shared__ float s_m[NW];
@@ -86,153 +261,34 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
   const int nparts = (L + a.P - 1) / a.P;
   if (p >= nparts) return;
   const int tok0 = p * a.P;
-  const int n = min(a.P, L - tok0);  // tokens of this partition
-  const int nblk = (n + B - 1) / B;
+  const int t_hi = min(tok0 + a.P, L);
+  const int lb0 = tok0 / B;
+  const int lb_max = (t_hi - 1) / B;
 
   // Stage this partition's table entries in LDS (one coalesced read).
-  const int32_t *trow = a.tables + (int64_t)s * a.maxb + tok0 / B;
-  for (int i = tid; i < nblk; i += NW * 64) s_tab[i] = trow[i];
+  const int32_t *trow = a.tables + (int64_t)s * a.maxb + lb0;
+  for (int i = tid; i <= lb_max - lb0; i += NW * 64) s_tab[i] = trow[i];
   __syncthreads();
 
-  const uint16_t *kp = reinterpret_cast<const uint16_t *>(a.k_pool);
-  const uint16_t *vp = reinterpret_cast<const uint16_t *>(a.v_pool);
-  const int64_t blk_stride = (int64_t)a.Hkv * B * D;  // elements per pool block
-  const int64_t head_base = (int64_t)h * B * D;       // scalar part of the tile offset
-  const int lane_off = lane * 8;                       // this lane's 8 elements
-  const int row = lane / LPT;
-
-  const u32x4 qv = *reinterpret_cast<const u32x4 *>(
-      reinterpret_cast<const uint16_t *>(a.q) + ((int64_t)s * a.H + h) * D + (lane % LPT) * 8);
-
-  bool bad = false;
-  float m = kNegInf;
-  float l = 0.f;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-
-  // Issue the 2 * NL loads of chunk c.  Every address is a scalar base (block
-  // id from LDS, moved to a scalar register) plus this lane's 16-byte offset.
-  auto load_chunk = [&](int c, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      int lb, off;
-      if constexpr (TC >= B) {  // a chunk covers TC / B whole blocks
-        lb = c * (TC / B) + (i * TPI) / B;
-        off = (i * TPI) % B;
-      } else {                  // a block holds B / TC chunks
-        lb = c / (B / TC);
-        off = (c % (B / TC)) * TC + i * TPI;
-      }
-      lb = min(lb, nblk - 1);   // tail loads stay inside the last block
-      int blk = __builtin_amdgcn_readfirstlane(s_tab[lb]);
-      if (blk < 0 || (int64_t)blk >= a.num_blocks) {
-        bad = true;
-        blk = 0;
-      }
-      const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
-      kr[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
-      vr[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
-    }
-  };
-
-  // Fold chunk c into this lane group's online softmax.  Branch-free: rows at
-  // or past n get score -inf and a zeroed V row (selected, never multiplied),
-  // so the poison in unused slots cannot leak.
-  auto consume = [&](int c, u32x4 (&kr)[NL], u32x4 (&vr)[NL]) {
-    float z[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const bool valid = (c * TC + i * TPI + row) < n;
-      const float d = group_sum<LPT>(dot8<DT>(qv, kr[i])) * a.scale_log2;
-      z[i] = valid ? d : kNegInf;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      vr[i] = valid ? vr[i] : zero;
-    }
-    float mx = z[0];
-#pragma unroll
-    for (int i = 1; i < NL; ++i) mx = fmaxf(mx, z[i]);
-    const float mnew = fmaxf(m, mx);
-    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
-    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
-    float pz[NL];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      pz[i] = fast_exp2(z[i] - mref);  // -inf gives 0
-      psum += pz[i];
-    }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = fmaf(pz[i], lo16<DT>(w[j]), acc[2 * j]);
-        acc[2 * j + 1] = fmaf(pz[i], hi16<DT>(w[j]), acc[2 * j + 1]);
-      }
-    }
-    m = mnew;
-  };
-
-  // This wave's chunks are c_k = wave + k * NW, k < my_n; two are in flight at
-  // a time.  The loop body always runs both halves and has a single back
-  // edge, so the same loads are outstanding on every path into it and the
-  // wait before each consume leaves the other chunk's 2 * NL loads in flight.
-  const int nch = (n + TC - 1) / TC;
+  WA wa;
+  wa.init(a, s, h, lane);
+  const int c_first = tok0 / TC;
+  const int nch = (t_hi - tok0 + TC - 1) / TC;
   if (wave < nch) {
     const int my_n = (nch - wave + NW - 1) / NW;
-    u32x4 ka[NL], va[NL], kb[NL], vb[NL];
-    load_chunk(wave, ka, va);
-    int k = 0;
-    for (; k + 2 < my_n; k += 2) {
-      const int c = wave + k * NW;
-      load_chunk(c + NW, kb, vb);
-      // keep the prefetch ahead of the consume (the scheduler would sink it)
-      __builtin_amdgcn_sched_barrier(0);
-      consume(c, ka, va);
-      load_chunk(c + 2 * NW, ka, va);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(c + NW, kb, vb);
-    }
-    const int c = wave + k * NW;
-    if (k + 1 < my_n) {
-      load_chunk(c + NW, kb, vb);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(c, ka, va);
-      consume(c + NW, kb, vb);
-    } else {
-      consume(c, ka, va);
-    }
+    wa.run(c_first + wave, NW, my_n, s_tab, lb0, lb_max, tok0, t_hi);
   }
+  wa.merge_groups();
 
-  // Merge the lane groups of this wave (same dims, different tokens).
+  if (lane < WA::LPT) {
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float l2 = __shfl_xor(l, off);
-    const float mm = fmaxf(m, m2);
-    const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
-    const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
-    l = l * f1 + l2 * f2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float o2 = __shfl_xor(acc[j], off);
-      acc[j] = acc[j] * f1 + o2 * f2;
-    }
-    m = mm;
-  }
-  if (lane < LPT) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s_o[wave][lane * 8 + j] = acc[j];
+    for (int j = 0; j < 8; ++j) s_o[wave][lane * 8 + j] = wa.acc[j];
     if (lane == 0) {
-      s_m[wave] = m;
-      s_l[wave] = l;
+      s_m[wave] = wa.m;
+      s_l[wave] = wa.l;
     }
   }
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  const int any_bad = __syncthreads_or(wa.bad ? 1 : 0);
 
   // Merge the waves; thread d owns output dimension d.
   for (int d = tid; d < D; d += NW * 64) {
@@ -288,43 +344,355 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
   }
 }
 
-template <int DT, int D, int B>
-hipError_t launch_partitions_t(const DecodeParams &a, hipStream_t stream) {
-  const int group = 8 * kXcdGroup;
-  const int grid = ((a.items + group - 1) / group) * group;
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves>), dim3(grid),
-                     dim3(kNumWaves * 64), 0, stream, a);
-  return hipGetLastError();
+// ---------------------------------------------------------------------------
+// Work-balanced split
+// ---------------------------------------------------------------------------
+//
+// Work is counted in chunks: a (sequence, head) with L valid tokens costs
+// ceil(L / TC) chunks plus kPieceChunks, so every cut falls on a chunk
+// boundary and only a sequence's last chunk is ever partly masked.
+
+// Cost of one sequence (all its heads); invalid and empty contexts cost 0.
+template <int TC>
+__device__ __forceinline__ int64_t seq_cost(int L, int maxb, int B, int H) {
+  return (L > 0 && L <= maxb * B) ? (int64_t)H * ((L + TC - 1) / TC + kPieceChunks) : 0;
 }
 
-template <int DT, int D>
-hipError_t launch_partitions_b(const DecodeParams &a, hipStream_t stream) {
-  switch (a.B) {
-    case 8: return launch_partitions_t<DT, D, 8>(a, stream);
-    case 16: return launch_partitions_t<DT, D, 16>(a, stream);
-    case 32: return launch_partitions_t<DT, D, 32>(a, stream);
-    case 64: return launch_partitions_t<DT, D, 64>(a, stream);
-    default: return hipErrorInvalidValue;
+// First position of worker w: floor(w * total / workers).
+__device__ __forceinline__ uint64_t worker_lo(int w, uint64_t total, int workers) {
+  return ((uint64_t)w * total) / (uint64_t)workers;
+}
+
+// Workers that get a slice: each slice is at least kMinWorkerChunks long.
+__device__ __forceinline__ int active_workers(uint64_t total, int G) {
+  const uint64_t want = total / (uint64_t)kMinWorkerChunks;
+  return (int)max((uint64_t)1, min((uint64_t)G, want));
+}
+
+// Largest worker w with worker_lo(w) <= x, for x < total.
+__device__ __forceinline__ int worker_of(uint64_t x, uint64_t total, int workers) {
+  int w = (int)((x * (uint64_t)workers) / total);
+  if (w > workers - 1) w = workers - 1;
+  while (w > 0 && worker_lo(w, total, workers) > x) --w;
+  while (w + 1 < workers && worker_lo(w + 1, total, workers) <= x) ++w;
+  return w;
+}
+
+// Prefix of seq_cost over sequences into LDS (cum[0] = 0, cum[S] = total),
+// computed by one wavefront: each lane sums a contiguous run, then a scan.
+template <int TC>
+__device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int64_t *cum, int lane) {
+  const int S = a.S;
+  const int per = (S + 63) / 64;
+  const int s0 = min(S, lane * per);
+  const int s1 = min(S, s0 + per);
+  int64_t run = 0;
+  for (int s = s0; s < s1; ++s) run += seq_cost<TC>(a.lens[s], a.maxb, a.B, a.H);
+  int64_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
+  int64_t x = incl - run;  // exclusive prefix of this lane's run
+  if (lane == 0) cum[0] = 0;
+  for (int s = s0; s < s1; ++s) {
+    x += seq_cost<TC>(a.lens[s], a.maxb, a.B, a.H);
+    cum[s + 1] = x;
+  }
+}
+
+template <int DT, int D, int B, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a) {
+  using WA = WaveAttn<DT, D, B>;
+  constexpr int TC = WA::TC;
+  constexpr int LPT = WA::LPT;
+  static_assert(TC < B || kTabWindow % (TC / B) == 0, "windows must start on chunk starts");
+
+  extern __shared__ int64_t lds[];
+  int64_t *cum = lds;                                           // [S + 1]
+  int32_t *tabs = reinterpret_cast<int32_t *>(lds + a.S + 1);   // [NW][kTabWindow]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) build_cost_prefix<TC>(a, cum, lane);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
+  }
+
+  const uint64_t total = (uint64_t)cum[a.S];
+  if (total == 0) return;
+  const int workers = active_workers(total, a.G);
+  const int w = blockIdx.x * NW + wave;
+  if (w >= workers) return;
+  const uint64_t lo = worker_lo(w, total, workers);
+  const uint64_t hi = worker_lo(w + 1, total, workers);
+  if (lo >= hi) return;
+
+  // sequence holding position lo: largest s with cum[s] <= lo
+  int sa = 0, sb = a.S;  // invariant: cum[sa] <= lo < cum[sb]
+  while (sb - sa > 1) {
+    const int mid = (sa + sb) >> 1;
+    if ((uint64_t)cum[mid] <= lo) sa = mid;
+    else sb = mid;
+  }
+
+  int32_t *tab = tabs + wave * kTabWindow;
+  uint64_t pos = lo;
+  int s = sa;
+  while (pos < hi && s < a.S) {
+    const uint64_t cs = (uint64_t)cum[s];
+    if ((uint64_t)cum[s + 1] <= pos) {  // finished or empty sequence
+      ++s;
+      continue;
+    }
+    const int sq = s;  // this piece's sequence
+    const int L = a.lens[sq];
+    const int nch = (L + TC - 1) / TC;
+    const uint64_t per = (uint64_t)(nch + kPieceChunks);
+    const int h = (int)((pos - cs) / per);
+    const uint64_t seg = cs + (uint64_t)h * per + kPieceChunks;  // first chunk's position
+    const int64_t c0 = max((int64_t)0, (int64_t)pos - (int64_t)seg);
+    const int64_t c1 = min((int64_t)nch, (int64_t)hi - (int64_t)seg);
+    pos = seg + nch;  // next (sequence, head)
+    if (h + 1 == a.H) ++s;
+    if (c1 <= c0) continue;
+
+    // ---- one piece: chunks [c0, c1) of (sq, h), tokens [t0, t1)
+    const int t0 = (int)c0 * TC;
+    const int t1 = min(L, (int)c1 * TC);
+    const int c_first = (int)c0;
+    const int c_last = (int)c1 - 1;
+    WA wa;
+    wa.init(a, sq, h, lane);
+    const int lb_max = (t1 - 1) / B;
+    const int32_t *trow = a.tables + (int64_t)sq * a.maxb;
+    // Windows of kTabWindow logical blocks; a window holds the chunks whose
+    // first token falls in it (chunks never straddle a window).
+    const int lb_first = (c_first * TC) / B;
+    for (int lb_w = lb_first; lb_w <= lb_max; lb_w += kTabWindow) {
+      int cs_, ce_;
+      if constexpr (TC >= B) {  // a chunk covers TC / B blocks; windows start on chunk starts
+        cs_ = max(c_first, lb_w / (TC / B));
+        ce_ = min(c_last, (lb_w + kTabWindow) / (TC / B) - 1);
+      } else {                  // B / TC chunks per block
+        cs_ = max(c_first, lb_w * (B / TC));
+        ce_ = min(c_last, (lb_w + kTabWindow) * (B / TC) - 1);
+      }
+      // stage this window's table entries (one coalesced read by the wave)
+      const int cnt = min(kTabWindow, lb_max - lb_w + 1);
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < cnt; i += 64) tab[i] = trow[lb_w + i];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wa.run(cs_, 1, ce_ - cs_ + 1, tab, lb_w, lb_max, t0, t1);
+    }
+    wa.merge_groups();
+
+    const int64_t g = (int64_t)sq * a.H + h;
+    if (lane < LPT) {
+      const float nanv = wa.bad ? __builtin_nanf("") : 0.f;
+      if (t0 == 0 && t1 == L) {
+        // the whole (sequence, head): final output row
+        uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D + lane * 8;
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t v0 = to16<DT>(wa.acc[2 * j] / wa.l + nanv);
+          const uint32_t v1 = to16<DT>(wa.acc[2 * j + 1] / wa.l + nanv);
+          packed[j] = v0 | (v1 << 16);
+        }
+        const u32x4 ov = {packed[0], packed[1], packed[2], packed[3]};
+        *reinterpret_cast<u32x4 *>(out_row) = ov;
+      } else {
+        const int64_t u = (int64_t)w + g;
+        float *o = a.ws_o + u * D + lane * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = wa.acc[j] + nanv;
+        if (lane == 0) {
+          a.ws_m[u] = wa.m * kLn2 + nanv;  // natural-log units
+          a.ws_l[u] = wa.l + nanv;
+        }
+      }
+    }
+  }
+}
+
+// One wavefront per (sequence, head): rows of empty or invalid contexts, and
+// the LSE merge of (sequence, head) rows split over several workers.  Lane j
+// reads piece j's (m, l); the merged row then needs one pass over the pieces.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
+  constexpr int TC = Geo<D>::TC;
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= (int64_t)a.S * a.H) return;
+  const int s = (int)(g / a.H);
+  const int h = (int)(g - (int64_t)s * a.H);
+  const int L = a.lens[s];
+  const uint64_t total = (uint64_t)a.ws_cum[a.S];
+  const uint64_t cs = (uint64_t)a.ws_cum[s];
+  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;
+  if (L <= 0 || L > a.maxb * a.B) {
+    const uint16_t v = (L == 0) ? uint16_t(0) : to16<DT>(__builtin_nanf(""));
+    for (int d = lane; d < D; d += 64) out_row[d] = v;
+    return;
+  }
+  const int workers = active_workers(total, a.G);
+  const int nch = (L + TC - 1) / TC;
+  const uint64_t seg = cs + (uint64_t)h * (nch + kPieceChunks) + kPieceChunks;
+  const int w_a = worker_of(seg, total, workers);
+  const int w_b = worker_of(seg + nch - 1, total, workers);
+  if (w_a == w_b) return;  // one piece: its worker wrote the row
+
+  // Lane j holds piece w_a + j's (m, l); rows split over more than 64 pieces
+  // (contexts of tens of thousands of tokens on few workers) loop.
+  float M = kNegInf;
+  for (int w0 = w_a; w0 <= w_b; w0 += 64) {
+    const int w = w0 + lane;
+    if (w <= w_b && worker_lo(w, total, workers) < worker_lo(w + 1, total, workers))
+      M = fmaxf(M, a.ws_m[(int64_t)w + g]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float lsum = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
+  for (int w0 = w_a; w0 <= w_b; w0 += 64) {
+    const int w = w0 + lane;
+    float f = 0.f, lw = 0.f;
+    if (w <= w_b && worker_lo(w, total, workers) < worker_lo(w + 1, total, workers)) {
+      const int64_t u = (int64_t)w + g;
+      f = fast_exp2((a.ws_m[u] - M) * kLog2e);
+      lw = a.ws_l[u];
+    }
+    const int n = min(64, w_b - w0 + 1);
+    // pieces in increasing order; their o rows are fetched 4 at a time
+    for (int j0 = 0; j0 < n; j0 += 4) {
+      float fj[4], vj[4][D / 64];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = min(j0 + q, n - 1);
+        fj[q] = (j0 + q < n) ? __shfl(f, j) : 0.f;
+        const int64_t u = (int64_t)(w0 + j) + g;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) vj[q][k] = a.ws_o[u * D + lane + 64 * k];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j0 + q >= n) break;
+        lsum += fj[q] * __shfl(lw, j0 + q);
+        // an empty slice has f = 0 and an unwritten row: skip it, do not multiply
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) o[k] = (fj[q] != 0.f) ? o[k] + fj[q] * vj[q][k] : o[k];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) out_row[lane + 64 * j] = to16<DT>(o[j] / lsum);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int B>
+struct PartitionsF {
+  static hipError_t call(const DecodeParams &a, hipStream_t st) {
+    const int group = 8 * kXcdGroup;
+    const int grid = ((a.items + group - 1) / group) * group;
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves>), dim3(grid),
+                       dim3(kNumWaves * 64), 0, st, a);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int D, int B>
+struct BalancedF {
+  static hipError_t call(const DecodeParams &a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves>), dim3(a.G / kNumWaves),
+                       dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int D, int B>
+struct BalancedPtrF {
+  static const void *call() {
+    return reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves>);
+  }
+};
+
+// Call F<DT, D, B>::call(args...) for the runtime (dtype, D, B).
+template <template <int, int, int> class F, typename R, typename... Args>
+R dispatch(int dtype, int D, int B, R fail, Args... args) {
+#define PKV_B(DT, DD)                             \
+  switch (B) {                                    \
+    case 8: return F<DT, DD, 8>::call(args...);   \
+    case 16: return F<DT, DD, 16>::call(args...); \
+    case 32: return F<DT, DD, 32>::call(args...); \
+    case 64: return F<DT, DD, 64>::call(args...); \
+    default: return fail;                         \
+  }
+  if (dtype == DT_F16) {
+    if (D == 64) { PKV_B(DT_F16, 64) }
+    if (D == 128) { PKV_B(DT_F16, 128) }
+  } else {
+    if (D == 64) { PKV_B(DT_BF16, 64) }
+    if (D == 128) { PKV_B(DT_BF16, 128) }
+  }
+#undef PKV_B
+  return fail;
 }
 
 }  // namespace
 
 int decode_waves() { return kNumWaves; }
 
+int decode_chunk_tokens(int head_dim) {
+  return head_dim == 64 ? Geo<64>::TC : Geo<128>::TC;
+}
+
+size_t balanced_lds_bytes(int num_seqs) {
+  return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)kNumWaves * kTabWindow * sizeof(int32_t);
+}
+
+const void *balanced_kernel(int dtype, int head_dim, int block_size) {
+  return dispatch<BalancedPtrF, const void *>(dtype, head_dim, block_size, nullptr);
+}
+
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream) {
-  if (a.items == 0) return hipSuccess;
-  if (a.dtype == DT_F16) {
-    if (a.D == 64) return launch_partitions_b<DT_F16, 64>(a, stream);
-    if (a.D == 128) return launch_partitions_b<DT_F16, 128>(a, stream);
-  } else {
-    if (a.D == 64) return launch_partitions_b<DT_BF16, 64>(a, stream);
-    if (a.D == 128) return launch_partitions_b<DT_BF16, 128>(a, stream);
+  if (a.S == 0) return hipSuccess;
+  if (a.balanced) {
+    if (a.G == 0) return hipSuccess;
+    return dispatch<BalancedF, hipError_t>(a.dtype, a.D, a.B, hipErrorInvalidValue, a, stream);
   }
-  return hipErrorInvalidValue;
+  if (a.items == 0) return hipSuccess;
+  return dispatch<PartitionsF, hipError_t>(a.dtype, a.D, a.B, hipErrorInvalidValue, a, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
+  if (a.S == 0) return hipSuccess;
+  if (a.balanced) {
+    const int64_t segs = (int64_t)a.S * a.H;
+    const int grid = (int)((segs + 3) / 4);
+#define PKV_BMERGE(DT, DD) \
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD>), dim3(grid), dim3(256), 0, stream, a)
+    if (a.dtype == DT_F16) {
+      if (a.D == 64) PKV_BMERGE(DT_F16, 64);
+      else PKV_BMERGE(DT_F16, 128);
+    } else {
+      if (a.D == 64) PKV_BMERGE(DT_BF16, 64);
+      else PKV_BMERGE(DT_BF16, 128);
+    }
+#undef PKV_BMERGE
+    return hipGetLastError();
+  }
   const int grid = a.S * a.H;
   if (grid == 0 || a.MP < 2) return hipSuccess;
 #define PKV_MERGE(DT, DD) \

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "pkv_launch.h"
 
 namespace {
@@ -27,55 +29,117 @@ bool pool_ok(const pkv_pool *p) {
   return elems < 9.0e18;
 }
 
-// Tokens one wavefront step of the partition kernel covers.
-#ifndef PKV_DECODE_LOADS
-#define PKV_DECODE_LOADS 4
-#endif
-int chunk_tokens(int head_dim) { return PKV_DECODE_LOADS * (64 / (head_dim / 8)); }
-
 int partition_unit(const pkv_pool *p) {
-  const int tc = chunk_tokens(p->head_dim);
+  const int tc = pkv::decode_chunk_tokens(p->head_dim);
   return p->block_size > tc ? p->block_size : tc;
-}
-
-// Resolve the partition size; returns 0 if invalid.
-int32_t resolve_partition(int32_t max_blocks, const pkv_pool *p, int32_t requested) {
-  const int unit = partition_unit(p);
-  const int64_t ctx = (int64_t)max_blocks * p->block_size;
-  int64_t P = requested;
-  if (P == 0) {
-    P = ctx <= 512 ? (ctx + unit - 1) / unit * unit : 512;
-  }
-  if (P <= 0 || P % unit != 0 || P / p->block_size > pkv::kTabMax) return 0;
-  return (int32_t)P;
 }
 
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
+// ---- device properties, cached per device (CU count, balanced-kernel occupancy)
+
+struct OccEntry {
+  int device;
+  const void *kernel;
+  size_t lds;
+  int blocks;
+};
+
+std::mutex g_cache_mu;
+int g_cus[64];            // 0 = not queried yet
+OccEntry g_occ[256];
+int g_occ_n = 0;
+
+int device_cus(int dev) {
+  if (dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
+
+int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (int i = 0; i < g_occ_n; ++i)
+      if (g_occ[i].device == dev && g_occ[i].kernel == kernel && g_occ[i].lds == lds) return g_occ[i].blocks;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, pkv::decode_waves() * 64, lds) != hipSuccess)
+    return 0;
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  if (g_occ_n < 256) g_occ[g_occ_n++] = OccEntry{dev, kernel, lds, nb};
+  return nb;
+}
+
+// Workers (wavefronts) of the balanced split on the current device: every
+// wavefront the GPU holds at once.  0 if the device cannot be queried.
+int balanced_workers(const pkv_pool *p, int32_t num_seqs) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const int cus = device_cus(dev);
+  if (cus <= 0) return 0;
+  const void *k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size);
+  if (!k) return 0;
+  // occupancy for the LDS of this many sequences, rounded up to 4 KiB
+  const size_t lds = align_up(pkv::balanced_lds_bytes(num_seqs), 4096);
+  const int nb = kernel_blocks_per_cu(dev, k, lds);
+  if (nb <= 0) return 0;
+  long long g = (long long)cus * nb * pkv::decode_waves() * pkv::kWorkerFill8 / 8;
+  g = g / pkv::decode_waves() * pkv::decode_waves();
+  if (g < pkv::decode_waves()) g = pkv::decode_waves();
+  if (g > pkv::kMaxWorkers) g = pkv::kMaxWorkers / pkv::decode_waves() * pkv::decode_waves();
+  return (int)g;
+}
+
 struct Layout {
-  int32_t P, MP;
+  bool balanced;
+  int32_t P, MP, G;
   int64_t units;
-  size_t off_l, off_o, bytes;
+  size_t off_l, off_o, off_cum, bytes;
 };
 
 pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks,
                          const pkv_pool *p, int32_t partition_size, Layout *lay) {
-  if (!pool_ok(p)) return p ? PKV_ERR_UNSUPPORTED : PKV_ERR_NULL;
+  if (!p) return PKV_ERR_NULL;
+  if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks * p->block_size > (1 << 30)) return PKV_ERR_SHAPE;
   if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
-  const int32_t P = resolve_partition(max_blocks, p, partition_size);
-  if (P == 0) return PKV_ERR_UNSUPPORTED;
+  if (partition_size < 0) return PKV_ERR_UNSUPPORTED;
   const int64_t ctx = (int64_t)max_blocks * p->block_size;
+  const int unit = partition_unit(p);
+  *lay = Layout{};
+  if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
+    // work-balanced split; the flattened cost space must stay below 2^47
+    const double cost = (double)num_seqs * num_heads * (double)(ctx + pkv::kPieceChunks);
+    if (cost >= 1.4e14) return PKV_ERR_SHAPE;
+    lay->balanced = true;
+    lay->G = balanced_workers(p, num_seqs);
+    if (num_seqs > 0 && lay->G == 0) return PKV_ERR_HIP;
+    const int64_t units = (int64_t)lay->G + (int64_t)num_seqs * num_heads;
+    lay->units = units;
+    const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
+    const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
+    lay->off_cum = 0;
+    lay->off_l = cum + sec;
+    lay->off_o = cum + 2 * sec;
+    lay->bytes = cum + 2 * sec + align_up((size_t)units * p->head_dim * sizeof(float), kAlign);
+    return PKV_OK;
+  }
+  int64_t P = partition_size;
+  if (P == 0) P = ctx <= 512 ? (ctx + unit - 1) / unit * unit : 512;
+  if (P % unit != 0 || P / p->block_size > pkv::kTabMax) return PKV_ERR_UNSUPPORTED;
   const int32_t MP = (int32_t)((ctx + P - 1) / P);
   const int64_t units = (int64_t)num_seqs * num_heads * MP;
   if (units > (int64_t)0x7FFFFF00) return PKV_ERR_SHAPE;  // 1-D grid limit
-  lay->P = P;
+  lay->P = (int32_t)P;
   lay->MP = MP;
   lay->units = units;
-  if (MP < 2 || units == 0) {
-    lay->off_l = lay->off_o = lay->bytes = 0;
-  } else {
+  if (MP >= 2 && units > 0) {
     const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
     lay->off_l = sec;
     lay->off_o = 2 * sec;
@@ -89,30 +153,46 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
                        int32_t partition_size, const void *workspace, size_t workspace_bytes,
                        bool need_inputs, pkv::DecodeParams *a) {
+  if (num_seqs == 0) {  // nothing to do; still validate the static arguments
+    if (!p) return PKV_ERR_NULL;
+    if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
+    if (num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
+    if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
+    *a = pkv::DecodeParams{};
+    return PKV_OK;
+  }
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (!p) return PKV_ERR_NULL;
+  if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
+  if (num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
+  if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
+  if (!out || !context_lens) return PKV_ERR_NULL;
+  if (need_inputs && (!q || !k_pool || !v_pool || !block_tables)) return PKV_ERR_NULL;
+  if (need_inputs && (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)))
+    return PKV_ERR_SHAPE;
+  if (!aligned(out, 16)) return PKV_ERR_SHAPE;
   Layout lay;
   const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, &lay);
   if (st != PKV_OK) return st;
-  if (num_seqs > 0) {
-    if (!out || !context_lens) return PKV_ERR_NULL;
-    if (need_inputs && (!q || !k_pool || !v_pool || !block_tables)) return PKV_ERR_NULL;
-    if (need_inputs && (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)))
-      return PKV_ERR_SHAPE;
-    if (!aligned(out, 2)) return PKV_ERR_SHAPE;
-  }
   if (lay.bytes > 0) {
     if (!workspace || workspace_bytes < lay.bytes || !aligned(workspace, kAlign))
       return PKV_ERR_WORKSPACE;
   }
   char *ws = (char *)workspace;
+  *a = pkv::DecodeParams{};
   a->out = out;
   a->q = q;
   a->k_pool = k_pool;
   a->v_pool = v_pool;
   a->tables = block_tables;
   a->lens = context_lens;
-  a->ws_m = lay.bytes ? (float *)ws : nullptr;
-  a->ws_l = lay.bytes ? (float *)(ws + lay.off_l) : nullptr;
-  a->ws_o = lay.bytes ? (float *)(ws + lay.off_o) : nullptr;
+  if (lay.bytes) {
+    const size_t m_off = lay.balanced ? align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign) : 0;
+    a->ws_m = (float *)(ws + m_off);
+    a->ws_l = (float *)(ws + lay.off_l);
+    a->ws_o = (float *)(ws + lay.off_o);
+    a->ws_cum = lay.balanced ? (int64_t *)ws : nullptr;
+  }
   a->scale_log2 = scale * 1.4426950408889634f;
   a->num_blocks = p->num_blocks;
   a->S = num_seqs;
@@ -123,7 +203,9 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   a->D = p->head_dim;
   a->P = lay.P;
   a->MP = lay.MP;
-  a->items = (int32_t)lay.units;
+  a->items = lay.balanced ? 0 : (int32_t)lay.units;
+  a->G = lay.G;
+  a->balanced = lay.balanced ? 1 : 0;
   a->dtype = p->dtype;
   return PKV_OK;
 }
@@ -206,8 +288,8 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t m
                                   const pkv_pool *p, int32_t partition_size) {
   Layout lay;
   if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, &lay) != PKV_OK)
-    return 0;
-  return lay.P;
+    return -1;
+  return lay.balanced ? 0 : lay.P;
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,

@@ -2,13 +2,44 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+// Wavefronts per workgroup of the decode kernels (build-time setting).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+// 16-byte loads per lane per tensor in one wavefront step (build-time setting).
+#ifndef PKV_DECODE_LOADS
+#define PKV_DECODE_LOADS 4
+#endif
 
 namespace pkv {
 
-// Largest number of table entries one partition stages in LDS.
+constexpr int kDecodeLoads = PKV_DECODE_LOADS;
+// Largest number of table entries one fixed partition stages in LDS.
 constexpr int kTabMax = 512;
-// Consecutive logical work items kept on one XCD.
+// Table entries one wavefront stages per LDS window in the balanced split.
+constexpr int kTabWindow = 64;
+// Balanced split: the work of a (sequence, head) is counted in chunks (one
+// wavefront step), plus a fixed overhead of kPieceChunks chunks per piece.
+#ifndef PKV_PIECE_CHUNKS
+#define PKV_PIECE_CHUNKS 1
+#endif
+constexpr int kPieceChunks = PKV_PIECE_CHUNKS;
+// Balanced split: smallest slice a worker gets, in chunks.
+constexpr int kMinWorkerChunks = 8;
+// Balanced split: workers per compute unit, as a fraction of the wavefronts a
+// compute unit holds (numerator over 8; build-time setting).
+#ifndef PKV_WORKER_FILL8
+#define PKV_WORKER_FILL8 8
+#endif
+constexpr int kWorkerFill8 = PKV_WORKER_FILL8;
+// Balanced split: most sequences (the per-workgroup cost prefix lives in LDS).
+constexpr int kBalancedMaxSeqs = 4096;
+// Balanced split: most workers (wavefronts).
+constexpr int kMaxWorkers = 16384;
+// Consecutive logical work items kept on one XCD (fixed partitions).
 constexpr int kXcdGroup = 16;
 
 struct DecodeParams {
@@ -18,18 +49,26 @@ struct DecodeParams {
   const void *v_pool;
   const int32_t *tables;   // [S][maxb]
   const int32_t *lens;     // [S]
-  float *ws_m;             // [S*H*MP]
-  float *ws_l;             // [S*H*MP]
-  float *ws_o;             // [S*H*MP*D]
+  float *ws_m;             // partial maxima
+  float *ws_l;             // partial sums
+  float *ws_o;             // partial weighted V sums, D per partial
+  int64_t *ws_cum;         // balanced split: cost prefix over sequences [S + 1]
   float scale_log2;        // scale * log2(e)
   int64_t num_blocks;      // N
   int32_t S, H, Hkv, maxb, B, D, P, MP;
-  int32_t items;           // S * H * MP
+  int32_t items;           // fixed partitions: S * H * MP
+  int32_t G;               // balanced split: workers (a multiple of the waves per workgroup)
+  int32_t balanced;        // 1: work-balanced split, 0: fixed partitions of P tokens
   int32_t dtype;
 };
 
-// Number of waves per workgroup of the partition pass.
 int decode_waves();
+// Tokens one wavefront step covers (partition sizes are multiples of it).
+int decode_chunk_tokens(int head_dim);
+// Dynamic LDS of the balanced kernel for num_seqs sequences.
+size_t balanced_lds_bytes(int num_seqs);
+// The balanced kernel instance for (dtype, D, B), for occupancy queries.
+const void *balanced_kernel(int dtype, int head_dim, int block_size);
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);

@@ -65,20 +65,23 @@ def _desc(N=100, B=16, H=4, D=128, dt="f16"):
 def test_partition_size_rules(lib):
     f = lib.pkv_decode_partition_size
     d = _desc()
-    assert f(8, 4, 128, ctypes.byref(d), 0) == 512                 # long tables: 512
-    assert f(8, 4, 13, ctypes.byref(d), 0) == 208                  # short: one partition
-    assert f(8, 4, 13, ctypes.byref(_desc(D=64)), 0) == 224        # D = 64 steps are 32 tokens
     assert f(8, 4, 128, ctypes.byref(d), 256) == 256
-    assert f(8, 4, 128, ctypes.byref(d), 24) == 0                  # not a multiple of 16
-    assert f(8, 4, 128, ctypes.byref(_desc(B=64)), 32) == 0        # not a multiple of B
-    assert f(8, 4, 128, ctypes.byref(_desc(B=8)), 8192) == 0       # P / B > 512
-    assert f(8, 5, 128, ctypes.byref(d), 0) == 0                   # heads != kv heads
+    assert f(8, 4, 128, ctypes.byref(d), 512) == 512
+    assert f(8, 4, 128, ctypes.byref(d), 24) == -1                 # not a multiple of 16
+    assert f(8, 4, 128, ctypes.byref(_desc(B=64)), 32) == -1       # not a multiple of B
+    assert f(8, 4, 128, ctypes.byref(_desc(D=64)), 48) == -1       # D = 64 steps are 32 tokens
+    assert f(8, 4, 128, ctypes.byref(_desc(B=8)), 8192) == -1      # P / B > 512
+    assert f(8, 5, 128, ctypes.byref(d), 256) == -1                # heads != kv heads
+    assert f(8, 4, 128, ctypes.byref(d), -16) == -1
+    # more than 4096 sequences: the balanced split falls back to fixed 512
+    assert f(5000, 4, 128, ctypes.byref(d), 0) == 512
+    assert f(5000, 4, 13, ctypes.byref(d), 0) == 208               # short tables: one partition
 
 
 def test_workspace_bytes(lib):
     f = lib.pkv_decode_workspace_bytes
     d = _desc(D=128)
-    assert f(8, 4, 13, ctypes.byref(d), 0) == 0                    # single partition: none
+    assert f(8, 4, 13, ctypes.byref(d), 208) == 0                  # one partition: none
     S, H, maxb, P = 64, 4, 128, 512
     MP = maxb * 16 // P
     U = S * H * MP
@@ -109,9 +112,13 @@ def test_validation_returns_status_before_any_launch(lib):
     st = lib.pkv_paged_attention_decode(fake, fake, fake, fake, fake, fake, 1.0, 4, 4, 128,
                                         ctypes.byref(d), 256, nul, 0, nul)
     assert st == 4                                                  # PKV_ERR_WORKSPACE
+    # misaligned output
+    st = lib.pkv_paged_attention_decode(ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, fake, fake, 1.0,
+                                        4, 4, 8, ctypes.byref(d), 128, nul, 0, nul)
+    assert st == 2
     # misaligned q
     st = lib.pkv_paged_attention_decode(fake, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, fake, 1.0,
-                                        4, 4, 8, ctypes.byref(d), 0, nul, 0, nul)
+                                        4, 4, 8, ctypes.byref(d), 128, nul, 0, nul)
     assert st == 2
     # zero sequences is a no-op that succeeds without touching anything
     st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 0, 4, 8, ctypes.byref(d), 0,

@@ -286,3 +286,75 @@ def test_bad_arguments_raise_before_launch():
         pkv.paged_attention_decode(q, kp, vp, tab, lens, t.scale, partition_size=16, workspace=ws)
     with pytest.raises(ValueError):
         pkv.paged_attention_decode(q[:, :2], kp, vp, tab, lens, t.scale)
+
+
+# ---------------------------------------------------------------------------
+# the work-balanced split (partition_size 0) on awkward length mixes
+# ---------------------------------------------------------------------------
+
+def _mix(kind):
+    rng = np.random.default_rng(77)
+    if kind == "many_tiny":
+        return dict(H=8, D=128, B=16, dtype="f16", lengths=list(rng.integers(1, 5, size=1000)))
+    if kind == "one_long_many_tiny":
+        L = [2048] + list(rng.integers(1, 41, size=299))
+        return dict(H=40, D=128, B=16, dtype="bf16", lengths=L)
+    if kind == "mixed_d64_b64":
+        L = list(rng.integers(1, 1025, size=37)) + [1, 1024, 64, 65]
+        return dict(H=4, D=64, B=64, dtype="f16", lengths=L)
+    if kind == "mixed_b8":
+        L = list(rng.integers(1, 700, size=50))
+        return dict(H=6, D=128, B=8, dtype="bf16", lengths=L)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["many_tiny", "one_long_many_tiny", "mixed_d64_b64", "mixed_b8"])
+def test_balanced_split_length_mixes_every_output(kind):
+    mx = _mix(kind)
+    log(f"balanced split: {kind} S={len(mx['lengths'])}")
+    t = build_tables(params=dict(name=kind, index=80, num_heads=mx["H"], head_dim=mx["D"], dtype=mx["dtype"],
+                                 block_size=mx["B"], num_seqs=len(mx["lengths"]),
+                                 lengths=("fixed", [int(x) for x in mx["lengths"]]), pool=("slack", 1.1),
+                                 tables="permute", max_len=int(max(mx["lengths"]))))
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    assert pkv.decode_partition_size(t.num_seqs, t.num_heads, t.max_blocks, kp, 0) == 0
+    out = _decode(t, q, kp, vp, tab, lens, 0)
+    ref = po.decode(to_bits(q), to_bits(kp), to_bits(vp), t.block_tables, t.context_lens, t.scale,
+                    t.block_size, t.dtype)
+    assert_close(to_bits(out), ref, t.dtype, f"balanced {kind}")
+
+
+def test_balanced_split_with_empty_and_invalid_rows():
+    lengths = [0, 5, 300, 0, 1, 77, 300, 2]
+    t = _small_case(S=len(lengths), lengths=[max(x, 1) for x in lengths])
+    lens_np = np.array(lengths, np.int32)
+    lens_np[6] = t.max_blocks * 16 + 3     # invalid: longer than the table
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    tab_np = t.block_tables.copy()
+    tab_np[2, 3] = -9                      # a needed entry outside the pool
+    out = _decode(t, q, kp, vp, torch.from_numpy(tab_np).to(DEV), torch.from_numpy(lens_np).to(DEV), 0)
+    o = po.bits_to_f64(to_bits(out), t.dtype)
+    assert np.all(o[0] == 0) and np.all(o[3] == 0)
+    assert np.all(np.isnan(o[2])) and np.all(np.isnan(o[6]))
+    good = [1, 4, 5, 7]
+    lens_ok = lens_np.copy()
+    lens_ok[6] = 0                         # the oracle gets only rows it can read
+    ref = po.decode(to_bits(q), to_bits(kp), to_bits(vp), t.block_tables, lens_ok, t.scale, 16, t.dtype)
+    assert_close(to_bits(out)[good], ref[good], t.dtype, "balanced good rows")
+
+
+def test_balanced_passes_called_separately_equal_the_fused_call():
+    t = _small_case(S=40)
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    fused = _decode(t, q, kp, vp, tab, lens, 0)
+    ws = pkv.alloc_workspace(t.num_seqs, t.num_heads, t.max_blocks, kp, 0)
+    out = torch.full_like(q, float("nan"))
+    pkv.decode_partitions(q, kp, vp, tab, lens, t.scale, out, ws, partition_size=0)
+    pkv.decode_merge(out, lens, t.max_blocks, kp, ws, partition_size=0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fused.view(torch.int16))
