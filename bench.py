@@ -3,12 +3,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config opt13b]
 
-One step is one pass of the whole hot path over one batch: translate the 64
-appended tokens to slots, append their K/V to the pools, run the partition
-pass of decode attention and the log-sum-exp merge pass.  Inputs are built
-and resident in HBM before timing; each step uses one of R replicas of the
-pools (different addresses), cycled, so no step finds the previous step's KV in
-the 256 MiB MALL or the L2s.
+One step is one pass of the whole hot path over one batch, as a serving
+engine runs it for one layer: each of the 64 sequences appends its new
+token's K/V (token context_len - 1, written into its pool slot through the
+block table) and attends over its paged context -- the split pass with the
+append fused in (pkv_decode_partitions_append) followed by the log-sum-exp
+merge (pkv_decode_merge).  `--separate-append` runs the append as its own
+two launches (pkv_slot_mapping + pkv_reshape_and_cache) before the decode
+passes instead.  Inputs are built and resident in HBM before timing; each step
+uses one of R replicas of the pools (different addresses), cycled, so no step
+finds the previous step's KV in the 256 MiB MALL or the L2s.
 
 Prints ONE JSON line.  `value` is algorithmic bytes per step / time per step
 (GB/s); `roofline` prices the partition kernel alone (algorithmic decode bytes
@@ -55,6 +59,8 @@ def parse(argv=None):
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with pkv_slot_mapping + pkv_reshape_and_cache, then decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args(argv)
@@ -114,7 +120,7 @@ def main(argv=None) -> int:
     sp = int(stream.cuda_stream)
     dref = ctypes.byref(desc)
 
-    # argument marshalling done once; the timed loop only issues the four calls
+    # argument marshalling done once; the timed loop only issues the C calls
     calls = []
     for kp, vp, q, knew, vnew, out in reps:
         a_slot = (slots.data_ptr(), tab.data_ptr(), S, t.max_blocks, seq.data_ptr(), pos.data_ptr(), S, dref, sp)
@@ -122,20 +128,27 @@ def main(argv=None) -> int:
                  dref, sp)
         a_dec = (out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), tab.data_ptr(), lens.data_ptr(),
                  ctypes.c_float(t.scale), S, H, t.max_blocks, dref, P, ws.data_ptr(), ws_bytes, sp)
+        a_fused = (out.data_ptr(), q.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0, kp.data_ptr(), vp.data_ptr(),
+                   tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale), S, H, t.max_blocks, dref, P,
+                   ws.data_ptr(), ws_bytes, sp)
         a_mrg = (out.data_ptr(), lens.data_ptr(), S, H, t.max_blocks, dref, P, ws.data_ptr(), ws_bytes, sp)
-        calls.append((a_slot, a_app, a_dec, a_mrg))
+        calls.append((a_slot, a_app, a_dec, a_fused, a_mrg))
 
     def check(st, what):
         if st != 0:
             raise RuntimeError(f"{what}: {pkv.status_string(st)}")
 
     def step(i, ev=None):
-        a_slot, a_app, a_dec, a_mrg = calls[i % len(calls)]
-        check(lib.pkv_slot_mapping(*a_slot), "slot_mapping")
-        check(lib.pkv_reshape_and_cache(*a_app), "reshape_and_cache")
+        a_slot, a_app, a_dec, a_fused, a_mrg = calls[i % len(calls)]
+        if args.separate_append:
+            check(lib.pkv_slot_mapping(*a_slot), "slot_mapping")
+            check(lib.pkv_reshape_and_cache(*a_app), "reshape_and_cache")
         if ev is not None:
             ev[0].record(stream)
-        check(lib.pkv_decode_partitions(*a_dec), "decode_partitions")
+        if args.separate_append:
+            check(lib.pkv_decode_partitions(*a_dec), "decode_partitions")
+        else:
+            check(lib.pkv_decode_partitions_append(*a_fused), "decode_partitions_append")
         if ev is not None:
             ev[1].record(stream)
         check(lib.pkv_decode_merge(*a_mrg), "decode_merge")
@@ -166,18 +179,27 @@ def main(argv=None) -> int:
           f"{ms_per_step:.4f} ms/step by events)", file=sys.stderr, flush=True)
 
     dec = acc.decode_bytes(t.context_lens, H, D, dsize, B)
-    app = acc.append_bytes(S, S, H, D, dsize)
-    step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+    if args.separate_append:
+        app = acc.append_bytes(S, S, H, D, dsize)
+        step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+        kern_bytes = dec["total"]
+        kern_name = "decode_balanced_kernel" if P == 0 else "decode_partition_kernel"
+    else:
+        # the new rows are read once (counted in the KV bytes) and written once
+        app_write = 2 * S * H * D * dsize
+        step_bytes = dec["total"] + app_write
+        kern_bytes = step_bytes
+        kern_name = ("decode_balanced_kernel" if P == 0 else "decode_partition_kernel") + " (append fused)"
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     kern_mean_ms = float(np.mean(kern_ms))
-    achieved = dec["total"] / (kern_mean_ms * 1e-3) / 1e9
+    achieved = kern_bytes / (kern_mean_ms * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash() and tr.get("config") == args.config and \
-                tr.get("partition_size") == P:
+                tr.get("partition_size") == P and tr.get("separate_append", False) == args.separate_append:
             traffic = tr.get("hbm_bytes_per_launch")
 
     if args.copy_calibration:
@@ -208,15 +230,16 @@ def main(argv=None) -> int:
         "dtype": t.dtype,
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {S} seqs x {H} heads x {D}, B={B}, "
-                               f"context_len {describe_lengths(t)}, one decode step + append of {S} tokens",
+                               f"context_len {describe_lengths(t)}, one decode step: append of {S} tokens + "
+                               f"attention ({'separate append' if args.separate_append else 'append fused'})",
                    "global_batch": S, "kv_tokens": t.kv_tokens(), "block_size": B, "partition_size": P,
                    "pool_blocks": t.num_blocks, "replicas": args.replicas, "parallelism": "none (1 GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
-        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+        "roofline": {"kernel": kern_name, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": dec["total"],
+                     "traffic": traffic, "bytes_per_launch": kern_bytes,
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2),
                      "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},

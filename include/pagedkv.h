@@ -145,19 +145,20 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
  *  - partition_size > 0: fixed partitions of P tokens, partition p holding
  *    tokens [p*P, min((p+1)*P, L)).  P must be a multiple of B and of the 16
  *    (D = 128) or 32 (D = 64) tokens one wavefront step covers, with P / B <= 512.
- *  - partition_size == 0: a work-balanced split.  Every wavefront the device
- *    holds at once takes an equal share of all (sequence, head, token) work,
- *    each (sequence, head) also costing a fixed overhead, so batches with very
- *    different context lengths keep every compute unit busy.  The cut points
- *    depend on the context lengths and on the device (compute units and
- *    occupancy), so results are identical run to run on one device and build.
- *    Batches of more than 4096 sequences fall back to fixed partitions of 512.
+ *  - partition_size == 0: a work-balanced split.  All (sequence, head, token)
+ *    work, each (sequence, head) also costing a fixed overhead, is cut into
+ *    equal slices, one per wavefront, with as many wavefronts as the device
+ *    holds at once, so batches with very different context lengths keep
+ *    every compute unit busy.  The cut points depend on the context lengths
+ *    and on the device (compute units and occupancy), so results are
+ *    identical run to run on one device and build.  Batches of more than
+ *    4096 sequences fall back to fixed partitions of 512.
  *
  * pkv_decode_partition_size() returns the P a call uses: P > 0 for fixed
  * partitions, 0 for the balanced split, -1 if the arguments are invalid.
  * pkv_decode_workspace_bytes() returns the workspace a call needs (0 when none
  * is needed or the arguments are invalid; the balanced split always needs
- * one, and its size depends on the current device).
+ * one).
  *
  * Workspace layout of fixed partitions (float32), with
  * MP = ceil(max_blocks_per_seq * B / P) and U = num_seqs * num_heads * MP,
@@ -166,7 +167,8 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
  *   a 256-byte boundary.  m is the partition's largest score z = scale * q.k
  *   (natural-log units), l = sum exp(z - m), o = sum exp(z - m) * v.
  * The balanced split's workspace holds a cost prefix and per-piece partial
- * results in the same (m, l, o) form; its layout is internal.
+ * results in the same (m, l, o) form; its layout is internal.  One call at a
+ * time may use a workspace.
  */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                   const pkv_pool *p, int32_t partition_size);
@@ -213,6 +215,48 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                       int32_t num_heads, int32_t max_blocks_per_seq,
                                       const pkv_pool *p, int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_paged_attention_decode_append -- one decode step with the append fused
+ * in: equivalent to appending row s of k_new / v_new as token L_s - 1 of
+ * every sequence with 1 <= L_s <= max_blocks_per_seq * B (pkv_slot_mapping
+ * with pos = L_s - 1, then pkv_reshape_and_cache), followed by
+ * pkv_paged_attention_decode -- in two launches instead of four.  The pool
+ * slot of token L_s - 1 receives the new row bit for bit, and attention uses
+ * the new row for that token ("PagedAttention 完全拆解", 原理详解（一）, Figure 6
+ * walk-through: the new token's K/V goes into its block, then attention runs
+ * over the blocks).
+ *
+ *   k_new, v_new  [num_seqs][Hkv][D], consecutive sequences new_token_stride
+ *                 ELEMENTS apart (0 means Hkv * D); rows 16-byte aligned
+ *   k_pool, v_pool  written (one row per sequence and head), otherwise read
+ * Other arguments and rules as in pkv_paged_attention_decode.  Rows whose
+ * table entry for token L_s - 1 lies outside [0, N) are not written and their
+ * output row is NaN.
+ */
+pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const void *k_new,
+                                             const void *v_new, int64_t new_token_stride,
+                                             void *k_pool, void *v_pool,
+                                             const int32_t *block_tables,
+                                             const int32_t *context_lens, float scale,
+                                             int32_t num_seqs, int32_t num_heads,
+                                             int32_t max_blocks_per_seq, const pkv_pool *p,
+                                             int32_t partition_size, void *workspace,
+                                             size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_decode_partitions_append -- the split pass of
+ * pkv_paged_attention_decode_append on its own (the pool writes of the append
+ * happen here); pkv_decode_merge completes it.  Arguments as in
+ * pkv_paged_attention_decode_append.
+ */
+pkv_status pkv_decode_partitions_append(void *out, const void *q, const void *k_new,
+                                        const void *v_new, int64_t new_token_stride, void *k_pool,
+                                        void *v_pool, const int32_t *block_tables,
+                                        const int32_t *context_lens, float scale, int32_t num_seqs,
+                                        int32_t num_heads, int32_t max_blocks_per_seq,
+                                        const pkv_pool *p, int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /*
  * pkv_decode_partitions -- the split pass of pkv_paged_attention_decode on its

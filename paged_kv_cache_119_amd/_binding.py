@@ -29,6 +29,8 @@ EXPORTS = (
     "pkv_decode_partition_size",
     "pkv_decode_workspace_bytes",
     "pkv_paged_attention_decode",
+    "pkv_paged_attention_decode_append",
+    "pkv_decode_partitions_append",
     "pkv_decode_partitions",
     "pkv_decode_merge",
 )
@@ -75,6 +77,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, pool, i32]),
         "pkv_paged_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
                                                       i32, pool, i32, vp, sz, vp]),
+        "pkv_paged_attention_decode_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
+                                                             i32, i32, i32, pool, i32, vp, sz, vp]),
+        "pkv_decode_partitions_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
+                                                        i32, i32, i32, pool, i32, vp, sz, vp]),
         "pkv_decode_partitions": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32,
                                                  pool, i32, vp, sz, vp]),
         "pkv_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pool, i32, vp, sz, vp]),
@@ -236,10 +242,12 @@ def decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, part
 
 
 def alloc_workspace(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size=0):
-    """A caller-owned workspace tensor of the size the decode call needs."""
+    """A caller-owned workspace tensor of the size the decode call needs,
+    zero-filled (the balanced split's counters must start at zero; every call
+    leaves them zero again)."""
     torch = _torch()
     n = decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=k_pool.device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=k_pool.device)
 
 
 def _decode_args(q, k_pool, v_pool, block_tables, context_lens, out):
@@ -282,6 +290,32 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
                                         maxb, ctypes.byref(desc), int(partition_size), ws_ptr, ws_bytes,
                                         _stream_ptr(k_pool.device))
     _check(st, "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, out=None,
+                                  partition_size=0, workspace=None):
+    """One decode step with the append fused in: row s of k_new / v_new
+    ([S, Hkv, D]) becomes token context_lens[s] - 1 of sequence s (written to
+    its pool slot), then attention runs over the paged K/V."""
+    lib = load_library()
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != k_pool.dtype or t.device != k_pool.device:
+            raise TypeError(f"{name} must be a {k_pool.dtype} tensor on {k_pool.device}")
+        if t.dim() != 3 or tuple(t.shape) != (S, desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [{S}, {desc.num_kv_heads}, {desc.head_dim}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{name} must have heads and dims contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must have the same token stride")
+    ws_ptr, ws_bytes = _workspace(workspace, S, H, maxb, k_pool, partition_size)
+    st = lib.pkv_paged_attention_decode_append(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                               int(k_new.stride(0)) if S > 0 else 0, k_pool.data_ptr(),
+                                               v_pool.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+                                               float(scale), S, H, maxb, ctypes.byref(desc), int(partition_size),
+                                               ws_ptr, ws_bytes, _stream_ptr(k_pool.device))
+    _check(st, "pkv_paged_attention_decode_append")
     return out
 
 

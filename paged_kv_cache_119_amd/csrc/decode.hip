@@ -12,14 +12,15 @@
 //  * Fixed partitions (partition_size P > 0): one workgroup of NW wavefronts
 //    per (sequence, head, partition of P tokens); the partition's table
 //    entries are staged in LDS once and the waves take chunks round-robin.
-//  * Work-balanced (partition_size 0): every wavefront of a grid sized to
-//    what the GPU holds at once is a worker that owns an equal slice of the
-//    flattened (sequence, head, chunk) space, where each (sequence, head)
-//    also costs a fixed overhead of kPieceChunks chunks.  A worker
-//    turns its slice into pieces (one per (sequence, head) it touches),
-//    stages each piece's table entries in its own LDS window and streams it.
+//  * Work-balanced (partition_size 0): the flattened (sequence, head, chunk)
+//    space, where each (sequence, head) also costs a fixed overhead of
+//    kPieceChunks chunks, is cut into equal slices, one per worker wavefront
+//    (kWorkerRounds times as many workers as the GPU holds at once, so the
+//    hardware dispatcher evens out wavefronts that get less bandwidth).  A
+//    slice becomes pieces (one per (sequence, head) it touches); each piece
+//    stages its table entries in the wavefront's own LDS window and streams.
 //    Batches with very different context lengths therefore load every CU
-//    evenly, with no empty workgroups and no long tail.  No atomics and no
+//    evenly, with no empty workgroups and no long tail.  No atomics, no
 //    inter-workgroup synchronisation: a piece that is not a whole (sequence,
 //    head) writes a partial result that a second launch merges.
 //
@@ -82,6 +83,10 @@ struct WaveAttn {
   bool bad;
   float m, l;
   float acc[8];
+  // fused append: chunk and token holding the new row (-1: none), its data
+  int app_c;
+  int app_tok;
+  u32x4 kn, vn;
 
   __device__ __forceinline__ void init(const DecodeParams &a, int s, int h, int lane) {
     kp = reinterpret_cast<const uint16_t *>(a.k_pool);
@@ -99,6 +104,32 @@ struct WaveAttn {
     l = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    app_c = -1;
+    app_tok = -1;
+  }
+
+  // Take token L - 1's K/V row from the new-token inputs (fused append).
+  __device__ __forceinline__ void set_append(const DecodeParams &a, int s, int h, int L, int lane) {
+    app_tok = L - 1;
+    app_c = app_tok / TC;
+    const int64_t e = (int64_t)s * a.new_stride + (int64_t)h * D + (lane % LPT) * 8;
+    kn = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + e);
+    vn = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + e);
+  }
+
+  // Write the new row to its pool slot (the lanes of its token row); `blk` is
+  // the table entry of logical block app_tok / B.
+  __device__ __forceinline__ void write_append(const DecodeParams &a, int blk) {
+    if (blk < 0 || (int64_t)blk >= num_blocks) {
+      bad = true;
+      return;
+    }
+    if (row != (app_tok % TPI)) return;
+    const int64_t base = (int64_t)blk * blk_stride + head_base + (app_tok % B) * D;
+    uint16_t *kw = const_cast<uint16_t *>(kp) + base + (lane_off % (LPT * 8));
+    uint16_t *vw = const_cast<uint16_t *>(vp) + base + (lane_off % (LPT * 8));
+    *reinterpret_cast<u32x4 *>(kw) = kn;
+    *reinterpret_cast<u32x4 *>(vw) = vn;
   }
 
   // Issue the 2 * NL loads of chunk c (tokens c*TC .. c*TC+TC-1 of the
@@ -132,6 +163,14 @@ struct WaveAttn {
   // [t_lo, t_hi) are selected out.  Branch-free.
   __device__ __forceinline__ void consume(int c, int t_lo, int t_hi, u32x4 (&kr)[NL],
                                           u32x4 (&vr)[NL]) {
+    if (c == app_c) {  // the chunk holding the appended token: use the new row
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool sub = (c * TC + i * TPI + row) == app_tok;
+        kr[i] = sub ? kn : kr[i];
+        vr[i] = sub ? vn : vr[i];
+      }
+    }
     float z[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -274,10 +313,13 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams 
   wa.init(a, s, h, lane);
   const int c_first = tok0 / TC;
   const int nch = (t_hi - tok0 + TC - 1) / TC;
+  const bool app = a.append && t_hi == L;  // this partition holds token L - 1
+  if (app) wa.set_append(a, s, h, L, lane);
   if (wave < nch) {
     const int my_n = (nch - wave + NW - 1) / NW;
     wa.run(c_first + wave, NW, my_n, s_tab, lb0, lb_max, tok0, t_hi);
   }
+  if (app && wave == 0) wa.write_append(a, __builtin_amdgcn_readfirstlane(s_tab[(L - 1) / B - lb0]));
   wa.merge_groups();
 
   if (lane < WA::LPT) {
@@ -358,24 +400,22 @@ __device__ __forceinline__ int64_t seq_cost(int L, int maxb, int B, int H) {
   return (L > 0 && L <= maxb * B) ? (int64_t)H * ((L + TC - 1) / TC + kPieceChunks) : 0;
 }
 
-// First position of worker w: floor(w * total / workers).
-__device__ __forceinline__ uint64_t worker_lo(int w, uint64_t total, int workers) {
-  return ((uint64_t)w * total) / (uint64_t)workers;
+// floor(x / d) for d >= 1 without the slow 64-bit integer division: a double
+// estimate corrected to the exact quotient with 64-bit multiplies.
+__device__ __forceinline__ uint64_t udiv64(uint64_t x, uint64_t d) {
+  uint64_t q = (uint64_t)((double)x / (double)d);
+  while (q > 0 && q * d > x) --q;
+  while ((q + 1) * d <= x) ++q;
+  return q;
 }
 
-// Workers that get a slice: each slice is at least kMinWorkerChunks long.
-__device__ __forceinline__ int active_workers(uint64_t total, int G) {
-  const uint64_t want = total / (uint64_t)kMinWorkerChunks;
-  return (int)max((uint64_t)1, min((uint64_t)G, want));
-}
-
-// Largest worker w with worker_lo(w) <= x, for x < total.
-__device__ __forceinline__ int worker_of(uint64_t x, uint64_t total, int workers) {
-  int w = (int)((x * (uint64_t)workers) / total);
-  if (w > workers - 1) w = workers - 1;
-  while (w > 0 && worker_lo(w, total, workers) > x) --w;
-  while (w + 1 < workers && worker_lo(w + 1, total, workers) <= x) ++w;
-  return w;
+// Workers share the cost space in equal slices: worker w owns positions
+// [min(total, w * slice), min(total, (w + 1) * slice)).  At most G workers,
+// each slice at least kMinWorkerChunks long.
+__device__ __forceinline__ uint64_t slice_of(uint64_t total, int G) {
+  const uint64_t want = total / (uint64_t)kMinWorkerChunks;  // constant divisor
+  const uint64_t workers = max((uint64_t)1, min((uint64_t)G, want));
+  return max((uint64_t)1, udiv64(total + workers - 1, workers));
 }
 
 // Prefix of seq_cost over sequences into LDS (cum[0] = 0, cum[S] = total),
@@ -424,97 +464,103 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
 
   const uint64_t total = (uint64_t)cum[a.S];
   if (total == 0) return;
-  const int workers = active_workers(total, a.G);
+  const uint64_t slice = slice_of(total, a.G);
   const int w = blockIdx.x * NW + wave;
-  if (w >= workers) return;
-  const uint64_t lo = worker_lo(w, total, workers);
-  const uint64_t hi = worker_lo(w + 1, total, workers);
+  const uint64_t lo = min(total, (uint64_t)w * slice);
+  const uint64_t hi = min(total, lo + slice);
   if (lo >= hi) return;
-
-  // sequence holding position lo: largest s with cum[s] <= lo
-  int sa = 0, sb = a.S;  // invariant: cum[sa] <= lo < cum[sb]
-  while (sb - sa > 1) {
-    const int mid = (sa + sb) >> 1;
-    if ((uint64_t)cum[mid] <= lo) sa = mid;
-    else sb = mid;
-  }
-
   int32_t *tab = tabs + wave * kTabWindow;
-  uint64_t pos = lo;
-  int s = sa;
-  while (pos < hi && s < a.S) {
-    const uint64_t cs = (uint64_t)cum[s];
-    if ((uint64_t)cum[s + 1] <= pos) {  // finished or empty sequence
-      ++s;
-      continue;
+  {
+    // sequence holding position lo: largest s with cum[s] <= lo
+    int sa = 0, sb = a.S;  // invariant: cum[sa] <= lo < cum[sb]
+    while (sb - sa > 1) {
+      const int mid = (sa + sb) >> 1;
+      if ((uint64_t)cum[mid] <= lo) sa = mid;
+      else sb = mid;
     }
-    const int sq = s;  // this piece's sequence
-    const int L = a.lens[sq];
-    const int nch = (L + TC - 1) / TC;
-    const uint64_t per = (uint64_t)(nch + kPieceChunks);
-    const int h = (int)((pos - cs) / per);
-    const uint64_t seg = cs + (uint64_t)h * per + kPieceChunks;  // first chunk's position
-    const int64_t c0 = max((int64_t)0, (int64_t)pos - (int64_t)seg);
-    const int64_t c1 = min((int64_t)nch, (int64_t)hi - (int64_t)seg);
-    pos = seg + nch;  // next (sequence, head)
-    if (h + 1 == a.H) ++s;
-    if (c1 <= c0) continue;
 
-    // ---- one piece: chunks [c0, c1) of (sq, h), tokens [t0, t1)
-    const int t0 = (int)c0 * TC;
-    const int t1 = min(L, (int)c1 * TC);
-    const int c_first = (int)c0;
-    const int c_last = (int)c1 - 1;
-    WA wa;
-    wa.init(a, sq, h, lane);
-    const int lb_max = (t1 - 1) / B;
-    const int32_t *trow = a.tables + (int64_t)sq * a.maxb;
-    // Windows of kTabWindow logical blocks; a window holds the chunks whose
-    // first token falls in it (chunks never straddle a window).
-    const int lb_first = (c_first * TC) / B;
-    for (int lb_w = lb_first; lb_w <= lb_max; lb_w += kTabWindow) {
-      int cs_, ce_;
-      if constexpr (TC >= B) {  // a chunk covers TC / B blocks; windows start on chunk starts
-        cs_ = max(c_first, lb_w / (TC / B));
-        ce_ = min(c_last, (lb_w + kTabWindow) / (TC / B) - 1);
-      } else {                  // B / TC chunks per block
-        cs_ = max(c_first, lb_w * (B / TC));
-        ce_ = min(c_last, (lb_w + kTabWindow) * (B / TC) - 1);
+    uint64_t pos = lo;
+    int s = sa;
+    while (pos < hi && s < a.S) {
+      const uint64_t cs = (uint64_t)cum[s];
+      if ((uint64_t)cum[s + 1] <= pos) {  // finished or empty sequence
+        ++s;
+        continue;
       }
-      // stage this window's table entries (one coalesced read by the wave)
-      const int cnt = min(kTabWindow, lb_max - lb_w + 1);
-      __builtin_amdgcn_wave_barrier();
-      for (int i = lane; i < cnt; i += 64) tab[i] = trow[lb_w + i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      wa.run(cs_, 1, ce_ - cs_ + 1, tab, lb_w, lb_max, t0, t1);
-    }
-    wa.merge_groups();
+      const int sq = s;  // this piece's sequence
+      const int L = a.lens[sq];
+      const int nch = (L + TC - 1) / TC;
+      const uint64_t per = (uint64_t)(nch + kPieceChunks);
+      const int h = (int)((pos - cs) / per);
+      const uint64_t seg = cs + (uint64_t)h * per + kPieceChunks;  // first chunk's position
+      const int64_t c0 = max((int64_t)0, (int64_t)pos - (int64_t)seg);
+      const int64_t c1 = min((int64_t)nch, (int64_t)hi - (int64_t)seg);
+      pos = seg + nch;  // next (sequence, head)
+      if (h + 1 == a.H) ++s;
+      if (c1 <= c0) continue;
 
-    const int64_t g = (int64_t)sq * a.H + h;
-    if (lane < LPT) {
-      const float nanv = wa.bad ? __builtin_nanf("") : 0.f;
-      if (t0 == 0 && t1 == L) {
-        // the whole (sequence, head): final output row
-        uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D + lane * 8;
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t v0 = to16<DT>(wa.acc[2 * j] / wa.l + nanv);
-          const uint32_t v1 = to16<DT>(wa.acc[2 * j + 1] / wa.l + nanv);
-          packed[j] = v0 | (v1 << 16);
+      // ---- one piece: chunks [c0, c1) of (sq, h), tokens [t0, t1)
+      const int t0 = (int)c0 * TC;
+      const int t1 = min(L, (int)c1 * TC);
+      const int c_first = (int)c0;
+      const int c_last = (int)c1 - 1;
+      WA wa;
+      wa.init(a, sq, h, lane);
+      const bool app = a.append && t1 == L;  // this piece holds token L - 1
+      if (app) wa.set_append(a, sq, h, L, lane);
+      const int lb_max = (t1 - 1) / B;
+      const int32_t *trow = a.tables + (int64_t)sq * a.maxb;
+      // Windows of kTabWindow logical blocks; a window holds the chunks whose
+      // first token falls in it (chunks never straddle a window).
+      const int lb_first = (c_first * TC) / B;
+      int lb_last_w = lb_first;
+      for (int lb_w = lb_first; lb_w <= lb_max; lb_w += kTabWindow) {
+        lb_last_w = lb_w;
+        int cs_, ce_;
+        if constexpr (TC >= B) {  // a chunk covers TC / B blocks; windows start on chunk starts
+          cs_ = max(c_first, lb_w / (TC / B));
+          ce_ = min(c_last, (lb_w + kTabWindow) / (TC / B) - 1);
+        } else {                  // B / TC chunks per block
+          cs_ = max(c_first, lb_w * (B / TC));
+          ce_ = min(c_last, (lb_w + kTabWindow) * (B / TC) - 1);
         }
-        const u32x4 ov = {packed[0], packed[1], packed[2], packed[3]};
-        *reinterpret_cast<u32x4 *>(out_row) = ov;
-      } else {
-        const int64_t u = (int64_t)w + g;
-        float *o = a.ws_o + u * D + lane * 8;
+        // stage this window's table entries (one coalesced read by the wave)
+        const int cnt = min(kTabWindow, lb_max - lb_w + 1);
+        __builtin_amdgcn_wave_barrier();
+        for (int i = lane; i < cnt; i += 64) tab[i] = trow[lb_w + i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wa.run(cs_, 1, ce_ - cs_ + 1, tab, lb_w, lb_max, t0, t1);
+      }
+      // the last window holds the appended token's block (lb_max)
+      if (app) wa.write_append(a, __builtin_amdgcn_readfirstlane(tab[lb_max - lb_last_w]));
+      wa.merge_groups();
+
+      const int64_t g = (int64_t)sq * a.H + h;
+      if (lane < LPT) {
+        const float nanv = wa.bad ? __builtin_nanf("") : 0.f;
+        if (t0 == 0 && t1 == L) {
+          // the whole (sequence, head): final output row
+          uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D + lane * 8;
+          uint32_t packed[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = wa.acc[j] + nanv;
-        if (lane == 0) {
-          a.ws_m[u] = wa.m * kLn2 + nanv;  // natural-log units
-          a.ws_l[u] = wa.l + nanv;
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t v0 = to16<DT>(wa.acc[2 * j] / wa.l + nanv);
+            const uint32_t v1 = to16<DT>(wa.acc[2 * j + 1] / wa.l + nanv);
+            packed[j] = v0 | (v1 << 16);
+          }
+          const u32x4 ov = {packed[0], packed[1], packed[2], packed[3]};
+          *reinterpret_cast<u32x4 *>(out_row) = ov;
+        } else {
+          const int64_t u = (int64_t)w + g;  // unique: workers and rows both advance along the cost space
+          float *o = a.ws_o + u * D + lane * 8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[j] = wa.acc[j] + nanv;
+          if (lane == 0) {
+            a.ws_m[u] = wa.m * kLn2 + nanv;  // natural-log units
+            a.ws_l[u] = wa.l + nanv;
+          }
         }
       }
     }
@@ -522,8 +568,8 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
 }
 
 // One wavefront per (sequence, head): rows of empty or invalid contexts, and
-// the LSE merge of (sequence, head) rows split over several workers.  Lane j
-// reads piece j's (m, l); the merged row then needs one pass over the pieces.
+// the LSE merge of (sequence, head) rows cut over several workers.  Lane j
+// reads worker t_a + j's (m, l); the merged row then needs one pass.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
   constexpr int TC = Geo<D>::TC;
@@ -533,7 +579,6 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   const int s = (int)(g / a.H);
   const int h = (int)(g - (int64_t)s * a.H);
   const int L = a.lens[s];
-  const uint64_t total = (uint64_t)a.ws_cum[a.S];
   const uint64_t cs = (uint64_t)a.ws_cum[s];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;
   if (L <= 0 || L > a.maxb * a.B) {
@@ -541,20 +586,19 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
     for (int d = lane; d < D; d += 64) out_row[d] = v;
     return;
   }
-  const int workers = active_workers(total, a.G);
   const int nch = (L + TC - 1) / TC;
   const uint64_t seg = cs + (uint64_t)h * (nch + kPieceChunks) + kPieceChunks;
-  const int w_a = worker_of(seg, total, workers);
-  const int w_b = worker_of(seg + nch - 1, total, workers);
-  if (w_a == w_b) return;  // one piece: its worker wrote the row
+  const uint64_t total = (uint64_t)a.ws_cum[a.S];
+  const uint64_t slice = slice_of(total, a.G);
+  const int64_t t_a = (int64_t)udiv64(seg, slice);
+  const int64_t t_b = (int64_t)udiv64(seg + nch - 1, slice);
+  if (t_a == t_b) return;  // one worker: it wrote the row
 
-  // Lane j holds piece w_a + j's (m, l); rows split over more than 64 pieces
-  // (contexts of tens of thousands of tokens on few workers) loop.
+  // Rows cut over more than 64 workers (contexts of thousands of tokens) loop.
   float M = kNegInf;
-  for (int w0 = w_a; w0 <= w_b; w0 += 64) {
-    const int w = w0 + lane;
-    if (w <= w_b && worker_lo(w, total, workers) < worker_lo(w + 1, total, workers))
-      M = fmaxf(M, a.ws_m[(int64_t)w + g]);
+  for (int64_t t0 = t_a; t0 <= t_b; t0 += 64) {
+    const int64_t t = t0 + lane;
+    if (t <= t_b) M = fmaxf(M, a.ws_m[t + g]);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -563,23 +607,22 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   float o[D / 64];
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
-  for (int w0 = w_a; w0 <= w_b; w0 += 64) {
-    const int w = w0 + lane;
+  for (int64_t t0 = t_a; t0 <= t_b; t0 += 64) {
+    const int64_t t = t0 + lane;
     float f = 0.f, lw = 0.f;
-    if (w <= w_b && worker_lo(w, total, workers) < worker_lo(w + 1, total, workers)) {
-      const int64_t u = (int64_t)w + g;
-      f = fast_exp2((a.ws_m[u] - M) * kLog2e);
-      lw = a.ws_l[u];
+    if (t <= t_b) {
+      f = fast_exp2((a.ws_m[t + g] - M) * kLog2e);
+      lw = a.ws_l[t + g];
     }
-    const int n = min(64, w_b - w0 + 1);
-    // pieces in increasing order; their o rows are fetched 4 at a time
+    const int n = (int)min((int64_t)64, t_b - t0 + 1);
+    // workers in increasing order; their o rows are fetched 4 at a time
     for (int j0 = 0; j0 < n; j0 += 4) {
       float fj[4], vj[4][D / 64];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int j = min(j0 + q, n - 1);
         fj[q] = (j0 + q < n) ? __shfl(f, j) : 0.f;
-        const int64_t u = (int64_t)(w0 + j) + g;
+        const int64_t u = t0 + j + g;
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) vj[q][k] = a.ws_o[u * D + lane + 64 * k];
       }
@@ -587,9 +630,8 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
       for (int q = 0; q < 4; ++q) {
         if (j0 + q >= n) break;
         lsum += fj[q] * __shfl(lw, j0 + q);
-        // an empty slice has f = 0 and an unwritten row: skip it, do not multiply
 #pragma unroll
-        for (int k = 0; k < D / 64; ++k) o[k] = (fj[q] != 0.f) ? o[k] + fj[q] * vj[q][k] : o[k];
+        for (int k = 0; k < D / 64; ++k) o[k] += fj[q] * vj[q][k];
       }
     }
   }

@@ -75,9 +75,10 @@ int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
   return nb;
 }
 
-// Workers (wavefronts) of the balanced split on the current device: every
-// wavefront the GPU holds at once.  0 if the device cannot be queried.
-int balanced_workers(const pkv_pool *p, int32_t num_seqs) {
+// Workers (wavefronts) the balanced split launches on the current device:
+// kWorkerRounds times as many as the device holds at once.  0 if the device
+// cannot be queried.
+int balanced_waves(const pkv_pool *p, int32_t num_seqs) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
@@ -88,18 +89,16 @@ int balanced_workers(const pkv_pool *p, int32_t num_seqs) {
   const size_t lds = align_up(pkv::balanced_lds_bytes(num_seqs), 4096);
   const int nb = kernel_blocks_per_cu(dev, k, lds);
   if (nb <= 0) return 0;
-  long long g = (long long)cus * nb * pkv::decode_waves() * pkv::kWorkerFill8 / 8;
-  g = g / pkv::decode_waves() * pkv::decode_waves();
-  if (g < pkv::decode_waves()) g = pkv::decode_waves();
+  long long g = (long long)cus * nb * pkv::decode_waves() * pkv::kWorkerRounds;
   if (g > pkv::kMaxWorkers) g = pkv::kMaxWorkers / pkv::decode_waves() * pkv::decode_waves();
   return (int)g;
 }
 
 struct Layout {
   bool balanced;
-  int32_t P, MP, G;
+  int32_t P, MP;
   int64_t units;
-  size_t off_l, off_o, off_cum, bytes;
+  size_t off_m, off_l, off_o, off_cum, bytes;
 };
 
 pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks,
@@ -114,17 +113,22 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   const int unit = partition_unit(p);
   *lay = Layout{};
   if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
-    // work-balanced split; the flattened cost space must stay below 2^47
-    const double cost = (double)num_seqs * num_heads * (double)(ctx + pkv::kPieceChunks);
-    if (cost >= 1.4e14) return PKV_ERR_SHAPE;
+    // work-balanced split; the cost space (chunks) must stay far below 2^47
+    const int tc = pkv::decode_chunk_tokens(p->head_dim);
+    const int64_t row_cost = (ctx + tc - 1) / tc + pkv::kPieceChunks;
+    const double cost = (double)num_seqs * num_heads * (double)row_cost;
+    if (cost >= 1.0e12) return PKV_ERR_SHAPE;
     lay->balanced = true;
-    lay->G = balanced_workers(p, num_seqs);
-    if (num_seqs > 0 && lay->G == 0) return PKV_ERR_HIP;
-    const int64_t units = (int64_t)lay->G + (int64_t)num_seqs * num_heads;
+    // a worker's slice is at least kMinWorkerChunks long, which bounds the
+    // workers; each (worker, row) pair it touches can hold a partial
+    const int64_t workers =
+        ((int64_t)num_seqs * num_heads * row_cost + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
+    const int64_t units = workers + (int64_t)num_seqs * num_heads;
     lay->units = units;
     const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
     const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
     lay->off_cum = 0;
+    lay->off_m = cum;
     lay->off_l = cum + sec;
     lay->off_o = cum + 2 * sec;
     lay->bytes = cum + 2 * sec + align_up((size_t)units * p->head_dim * sizeof(float), kAlign);
@@ -141,6 +145,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   lay->units = units;
   if (MP >= 2 && units > 0) {
     const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
+    lay->off_m = 0;
     lay->off_l = sec;
     lay->off_o = 2 * sec;
     lay->bytes = 2 * sec + align_up((size_t)units * p->head_dim * sizeof(float), kAlign);
@@ -187,11 +192,14 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   a->tables = block_tables;
   a->lens = context_lens;
   if (lay.bytes) {
-    const size_t m_off = lay.balanced ? align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign) : 0;
-    a->ws_m = (float *)(ws + m_off);
+    a->ws_m = (float *)(ws + lay.off_m);
     a->ws_l = (float *)(ws + lay.off_l);
     a->ws_o = (float *)(ws + lay.off_o);
-    a->ws_cum = lay.balanced ? (int64_t *)ws : nullptr;
+    a->ws_cum = lay.balanced ? (int64_t *)(ws + lay.off_cum) : nullptr;
+  }
+  if (lay.balanced) {
+    a->G = balanced_waves(p, num_seqs);
+    if (a->G == 0) return PKV_ERR_HIP;
   }
   a->scale_log2 = scale * 1.4426950408889634f;
   a->num_blocks = p->num_blocks;
@@ -204,13 +212,36 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   a->P = lay.P;
   a->MP = lay.MP;
   a->items = lay.balanced ? 0 : (int32_t)lay.units;
-  a->G = lay.G;
   a->balanced = lay.balanced ? 1 : 0;
   a->dtype = p->dtype;
   return PKV_OK;
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// Validation and parameters shared by the two fused-append entry points.
+pkv_status fill_append(void *out, const void *q, const void *k_new, const void *v_new,
+                       int64_t new_token_stride, void *k_pool, void *v_pool,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                       const pkv_pool *p, int32_t partition_size, void *workspace,
+                       size_t workspace_bytes, pkv::DecodeParams *a) {
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                                    num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
+                                    workspace, workspace_bytes, true, a);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (!k_new || !v_new) return PKV_ERR_NULL;
+  const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
+  if (new_token_stride == 0) new_token_stride = row;
+  if (new_token_stride < row || new_token_stride % 8 != 0) return PKV_ERR_SHAPE;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return PKV_ERR_SHAPE;
+  a->append = 1;
+  a->k_new = k_new;
+  a->v_new = v_new;
+  a->new_stride = new_token_stride;
+  return PKV_OK;
+}
+
 
 }  // namespace
 
@@ -324,6 +355,42 @@ pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_
                                     workspace, workspace_bytes, false, &a);
   if (st != PKV_OK) return st;
   return hip_status(pkv::launch_decode_merge(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const void *k_new,
+                                             const void *v_new, int64_t new_token_stride,
+                                             void *k_pool, void *v_pool,
+                                             const int32_t *block_tables,
+                                             const int32_t *context_lens, float scale,
+                                             int32_t num_seqs, int32_t num_heads,
+                                             int32_t max_blocks_per_seq, const pkv_pool *p,
+                                             int32_t partition_size, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+  pkv::DecodeParams a;
+  const pkv_status st = fill_append(out, q, k_new, v_new, new_token_stride, k_pool, v_pool,
+                                    block_tables, context_lens, scale, num_seqs, num_heads,
+                                    max_blocks_per_seq, p, partition_size, workspace,
+                                    workspace_bytes, &a);
+  if (st != PKV_OK) return st;
+  const pkv_status s1 = hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(pkv::launch_decode_merge(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_decode_partitions_append(void *out, const void *q, const void *k_new,
+                                        const void *v_new, int64_t new_token_stride, void *k_pool,
+                                        void *v_pool, const int32_t *block_tables,
+                                        const int32_t *context_lens, float scale, int32_t num_seqs,
+                                        int32_t num_heads, int32_t max_blocks_per_seq,
+                                        const pkv_pool *p, int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  pkv::DecodeParams a;
+  const pkv_status st = fill_append(out, q, k_new, v_new, new_token_stride, k_pool, v_pool,
+                                    block_tables, context_lens, scale, num_seqs, num_heads,
+                                    max_blocks_per_seq, p, partition_size, workspace,
+                                    workspace_bytes, &a);
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_pool,

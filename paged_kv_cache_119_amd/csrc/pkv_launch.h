@@ -27,17 +27,19 @@ constexpr int kTabWindow = 64;
 #define PKV_PIECE_CHUNKS 1
 #endif
 constexpr int kPieceChunks = PKV_PIECE_CHUNKS;
-// Balanced split: smallest slice a worker gets, in chunks.
+// Balanced split: smallest slice a worker gets, in chunks (this also bounds
+// the number of workers, hence of partial results, independently of the GPU).
 constexpr int kMinWorkerChunks = 8;
-// Balanced split: workers per compute unit, as a fraction of the wavefronts a
-// compute unit holds (numerator over 8; build-time setting).
-#ifndef PKV_WORKER_FILL8
-#define PKV_WORKER_FILL8 8
+// Balanced split: workers launched per wavefront the GPU holds at once; with
+// more than one round the hardware dispatcher balances rounds as slots free
+// up (build-time setting).
+#ifndef PKV_WORKER_ROUNDS
+#define PKV_WORKER_ROUNDS 1
 #endif
-constexpr int kWorkerFill8 = PKV_WORKER_FILL8;
+constexpr int kWorkerRounds = PKV_WORKER_ROUNDS;
 // Balanced split: most sequences (the per-workgroup cost prefix lives in LDS).
 constexpr int kBalancedMaxSeqs = 4096;
-// Balanced split: most workers (wavefronts).
+// Balanced split: most wavefronts launched.
 constexpr int kMaxWorkers = 16384;
 // Consecutive logical work items kept on one XCD (fixed partitions).
 constexpr int kXcdGroup = 16;
@@ -57,9 +59,16 @@ struct DecodeParams {
   int64_t num_blocks;      // N
   int32_t S, H, Hkv, maxb, B, D, P, MP;
   int32_t items;           // fixed partitions: S * H * MP
-  int32_t G;               // balanced split: workers (a multiple of the waves per workgroup)
+  int32_t G;               // balanced split: workers (wavefronts) launched, a multiple of the waves per workgroup
   int32_t balanced;        // 1: work-balanced split, 0: fixed partitions of P tokens
   int32_t dtype;
+  // Fused append (append != 0): the row of token L - 1 of every (sequence,
+  // head) is taken from k_new / v_new ([S][Hkv][D], token stride new_stride
+  // elements) and also written to its pool slot.
+  int32_t append;
+  const void *k_new;
+  const void *v_new;
+  int64_t new_stride;
 };
 
 int decode_waves();

@@ -358,3 +358,48 @@ def test_balanced_passes_called_separately_equal_the_fused_call():
     pkv.decode_merge(out, lens, t.max_blocks, kp, ws, partition_size=0)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), fused.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# the fused decode step: append token L - 1, then attend
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fused_append_decode_matches_append_then_decode(P, dtype):
+    """Pools after the fused call equal the oracle's append of token L - 1
+    bit for bit; outputs match the oracle over the updated pools."""
+    log(f"fused append+decode {dtype} P={P}")
+    t = _small_case(S=30, dtype=dtype)
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    from synth import normal_16bit
+    knew = normal_16bit((t.num_seqs, t.num_heads, t.head_dim), dtype, DEV, 501)
+    vnew = normal_16bit((t.num_seqs, t.num_heads, t.head_dim), dtype, DEV, 502)
+    kpo, vpo = to_bits(kp), to_bits(vp)
+    out = pkv.paged_attention_decode_append(q, knew, vnew, kp, vp, tab, lens, t.scale, partition_size=P)
+    torch.cuda.synchronize()
+    slots = po.slot_mapping(t.block_tables, np.arange(t.num_seqs), t.context_lens - 1, t.block_size)
+    po.reshape_and_cache(to_bits(knew), to_bits(vnew), kpo, vpo, slots, t.block_size)
+    assert np.array_equal(to_bits(kp), kpo) and np.array_equal(to_bits(vp), vpo)
+    ref = po.decode(to_bits(q), kpo, vpo, t.block_tables, t.context_lens, t.scale, t.block_size, dtype)
+    assert_close(to_bits(out), ref, dtype, f"fused P={P}")
+
+
+def test_fused_append_equals_separate_calls_bitwise():
+    t = _small_case(S=20)
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    kp2, vp2 = kp.clone(), vp.clone()
+    q = make_query(t, DEV)
+    from synth import normal_16bit
+    knew = normal_16bit((t.num_seqs, t.num_heads, t.head_dim), t.dtype, DEV, 503)
+    vnew = normal_16bit((t.num_seqs, t.num_heads, t.head_dim), t.dtype, DEV, 504)
+    fused = pkv.paged_attention_decode_append(q, knew, vnew, kp, vp, tab, lens, t.scale)
+    seq = torch.arange(t.num_seqs, dtype=torch.int32, device=DEV)
+    pkv.reshape_and_cache(knew, vnew, kp2, vp2, pkv.slot_mapping(tab, seq, lens - 1, kp2))
+    sep = pkv.paged_attention_decode(q, kp2, vp2, tab, lens, t.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kp.view(torch.int16), kp2.view(torch.int16))
+    assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
