@@ -24,7 +24,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -36,16 +35,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention achieved HBM GB/s (% of MI355X peak) + KV tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json")
-KERNEL_SOURCES = ("paged_kv_cache_119_amd/csrc/decode.hip", "paged_kv_cache_119_amd/csrc/pkv_device.h",
-                  "paged_kv_cache_119_amd/csrc/pkv_launch.h")
-
-
-def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def parse(argv=None):
@@ -79,6 +68,7 @@ def main(argv=None) -> int:
 
     import paged_kv_cache_119_amd as pkv
     from paged_kv_cache_119_amd import accounting as acc
+    from paged_kv_cache_119_amd.rocprof_summary import kernel_hash
     from paged_kv_cache_119_amd._binding import pool_desc_of
     from synth import build_tables, make_pools, make_query, normal_16bit
 

@@ -1,0 +1,140 @@
+"""Summarise rocprofv3 CSV output of bench.py into profiles/.
+
+    python -m paged_kv_cache_119_amd.rocprof_summary \\
+        --trace DIR_WITH_kernel_stats.csv --fetch DIR_WITH_FETCH_counter_collection.csv \\
+        --write DIR_WITH_WRITE_counter_collection.csv --config opt13b --partition-size 0 \\
+        --algorithmic-bytes N --command "..." [--command "..."] --out profiles/decode_balanced_opt13b.md
+
+Writes a short Markdown summary (mean kernel durations from the kernel trace;
+HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
+same counter reads for the 1 GiB device copy bench.py runs with
+--copy-calibration) and the traffic record bench.py reports while the decode
+kernel sources are unchanged.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("paged_kv_cache_119_amd/csrc/decode.hip", "paged_kv_cache_119_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_119_amd/csrc/pkv_launch.h")
+COPY_BYTES_KIB = (1 << 30) / 1024.0
+
+
+def kernel_hash(root: str = ROOT) -> str:
+    """Hash of the decode kernel sources: a traffic record is valid only for them."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def kernel_stats(trace_dir: str) -> list:
+    rows = list(csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+    out = []
+    for r in rows:
+        out.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                    "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3})
+    return out
+
+
+def counter_means(counter_dir: str) -> dict:
+    rows = list(csv.DictReader(open(_one(os.path.join(counter_dir, "**", "*counter_collection.csv")))))
+    agg = {}
+    for r in rows:
+        agg.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    return agg
+
+
+def copy_scale(agg: dict, counter: str) -> float:
+    """KiB the counter reports for the 1 GiB calibration copy -> scale to true bytes."""
+    vals = [max(v) for (k, c), v in agg.items() if c == counter and "copyBuffer" in k]
+    if not vals:
+        raise RuntimeError(f"no calibration copy found for {counter}")
+    return COPY_BYTES_KIB / max(vals)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--config", default="opt13b")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--separate-append", action="store_true")
+    ap.add_argument("--kernel", default="decode_balanced_kernel")
+    ap.add_argument("--algorithmic-bytes", type=int, required=True)
+    ap.add_argument("--command", action="append", required=True,
+                    help="a command the profiles were taken with (repeat for each run)")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json"))
+    args = ap.parse_args(argv)
+
+    stats = kernel_stats(args.trace)
+    fetch = counter_means(args.fetch)
+    write = counter_means(args.write)
+    fs = copy_scale(fetch, "FETCH_SIZE")
+    ws = copy_scale(write, "WRITE_SIZE")
+
+    def per_dispatch(agg, counter, scale):
+        out = {}
+        for (k, c), v in agg.items():
+            if c == counter and "pkv" in k:
+                out[k] = sum(v) / len(v) * scale * 1024.0
+        return out
+
+    fb = per_dispatch(fetch, "FETCH_SIZE", fs)
+    wb = per_dispatch(write, "WRITE_SIZE", ws)
+    main_k = [k for k in fb if args.kernel in k]
+    if not main_k:
+        raise RuntimeError(f"kernel {args.kernel} not in the counter output")
+    traffic = fb[main_k[0]] + wb.get(main_k[0], 0.0)
+
+    lines = [f"# rocprofv3 summary: {args.kernel}, {args.config} workload", "",
+             "Commands (from the repository root, on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.command]
+    lines += ["",
+             "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "pkv" in r["name"]:
+            lines.append(f"| `{r['name'][:100]}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
+                         f"{r['max_us']:.2f} |")
+    lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Scale factors from the 1 GiB device copy in the same runs: FETCH_SIZE x {fs:.4f}, "
+              f"WRITE_SIZE x {ws:.4f}.", "",
+              "| kernel | fetched MB | written MB |", "|---|---|---|"]
+    for k in sorted(fb):
+        lines.append(f"| `{k[:100]}` | {fb[k] / 1e6:.2f} | {wb.get(k, 0.0) / 1e6:.2f} |")
+    lines += ["", f"Algorithmic bytes of one `{args.kernel}` launch: {args.algorithmic_bytes / 1e6:.2f} MB; "
+              f"measured traffic {traffic / 1e6:.2f} MB ({traffic / args.algorithmic_bytes:.3f}x).", ""]
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    rec = {"kernel": args.kernel, "config": args.config, "partition_size": args.partition_size,
+           "separate_append": args.separate_append, "kernel_hash": kernel_hash(),
+           "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fb[main_k[0]]),
+           "write_bytes": round(wb.get(main_k[0], 0.0)), "fetch_scale": fs, "write_scale": ws,
+           "commands": args.command}
+    with open(args.traffic_json, "w") as f:
+        json.dump(rec, f, indent=2)
+    print(args.out, args.traffic_json, f"traffic {traffic / 1e6:.2f} MB")
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
