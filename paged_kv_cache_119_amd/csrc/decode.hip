@@ -8,23 +8,16 @@
 // partial results are merged afterwards (iaim.asia block-table article,
 // "vLLM 内核里的缓解写法": segments in parallel, then a reduction).
 //
-// Two ways of cutting, one inner engine:
+// Two ways of cutting:
 //  * Fixed partitions (partition_size P > 0): one workgroup of NW wavefronts
 //    per (sequence, head, partition of P tokens); the partition's table
-//    entries are staged in LDS once and the waves take chunks round-robin.
-//  * Work-balanced (partition_size 0): the flattened (sequence, head, chunk)
-//    space, where each (sequence, head) also costs a fixed overhead of
-//    kPieceChunks chunks, is cut into equal slices, one per worker wavefront
-//    (kWorkerRounds times as many workers as the GPU holds at once, so the
-//    hardware dispatcher evens out wavefronts that get less bandwidth).  A
-//    slice becomes pieces (one per (sequence, head) it touches); each piece
-//    stages its table entries in the wavefront's own LDS window and streams.
-//    Batches with very different context lengths therefore load every CU
-//    evenly, with no empty workgroups and no long tail.  No atomics, no
-//    inter-workgroup synchronisation: a piece that is not a whole (sequence,
-//    head) writes a partial result that a second launch merges.
+//    entries are staged in LDS once and the waves take chunks round-robin
+//    (WaveAttn below).
+//  * Work-balanced (partition_size 0): all chunks of the batch are cut into
+//    equal slices, one per wavefront; each wavefront runs its slice as one
+//    pipelined stream of chunks (Stream below).
 //
-// Inner engine (WaveAttn), per wavefront:
+// Inner engine of the fixed partitions (WaveAttn), per wavefront:
 //  * A "chunk" covers TC tokens: NL loads of 16 bytes per lane from K and NL
 //    from V.  With the [N][Hkv][B][D] pool layout one load instruction reads
 //    1 KiB of consecutive bytes (TPI whole token rows of one block), so every
@@ -390,14 +383,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // Work-balanced split
 // ---------------------------------------------------------------------------
 //
-// Work is counted in chunks: a (sequence, head) with L valid tokens costs
-// ceil(L / TC) chunks plus kPieceChunks, so every cut falls on a chunk
-// boundary and only a sequence's last chunk is ever partly masked.
+// Work is counted in chunks: the cost space [0, total) lists the chunks of
+// every (sequence, head) row, rows in order (sequence major), where a row
+// with L valid tokens has ceil(L / TC) chunks.  It is cut into equal slices,
+// one per worker wavefront w.  The part of a row a slice covers is a
+// "piece".  A piece that is the whole row writes the output row; any other
+// writes a partial result to slot w + g (workers and rows both advance along
+// the cost space, so the slot is unique) and the merge launch combines a
+// row's partials in worker order.
+//
+// A wavefront runs its slice as one stream of chunks through three stages --
+// table entries of chunk n + 2, K/V rows of chunk n + 1, arithmetic on chunk
+// n -- so piece and row boundaries cost no exposed memory latency.  Every
+// step issues the same loads (after the last chunk they repeat it and hit
+// the cache), so the compiler's waits stay exact.  A wavefront lowers its
+// priority as it progresses through its slice, so wavefronts that share a
+// SIMD finish together instead of in order of age.
 
-// Cost of one sequence (all its heads); invalid and empty contexts cost 0.
+// Chunks of a row of L tokens; invalid and empty contexts have none.
 template <int TC>
-__device__ __forceinline__ int64_t seq_cost(int L, int maxb, int B, int H) {
-  return (L > 0 && L <= maxb * B) ? (int64_t)H * ((L + TC - 1) / TC + kPieceChunks) : 0;
+__device__ __forceinline__ int row_chunks(int L, int maxb, int B) {
+  return (L > 0 && L <= maxb * B) ? (L + TC - 1) / TC : 0;
 }
 
 // floor(x / d) for d >= 1 without the slow 64-bit integer division: a double
@@ -409,6 +415,12 @@ __device__ __forceinline__ uint64_t udiv64(uint64_t x, uint64_t d) {
   return q;
 }
 
+__device__ __forceinline__ uint64_t uni64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Workers share the cost space in equal slices: worker w owns positions
 // [min(total, w * slice), min(total, (w + 1) * slice)).  At most G workers,
 // each slice at least kMinWorkerChunks long.
@@ -418,16 +430,21 @@ __device__ __forceinline__ uint64_t slice_of(uint64_t total, int G) {
   return max((uint64_t)1, udiv64(total + workers - 1, workers));
 }
 
-// Prefix of seq_cost over sequences into LDS (cum[0] = 0, cum[S] = total),
-// computed by one wavefront: each lane sums a contiguous run, then a scan.
+// Prefix of the chunk count over sequences into LDS (cum[0] = 0, cum[S] =
+// total) and a copy of the context lengths, computed by one wavefront: each
+// lane sums a contiguous run, then a scan.
 template <int TC>
-__device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int64_t *cum, int lane) {
+__device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int64_t *cum, int32_t *lens, int lane) {
   const int S = a.S;
   const int per = (S + 63) / 64;
   const int s0 = min(S, lane * per);
   const int s1 = min(S, s0 + per);
   int64_t run = 0;
-  for (int s = s0; s < s1; ++s) run += seq_cost<TC>(a.lens[s], a.maxb, a.B, a.H);
+  for (int s = s0; s < s1; ++s) {
+    const int L = a.lens[s];
+    lens[s] = L;
+    run += (int64_t)a.H * row_chunks<TC>(L, a.maxb, a.B);
+  }
   int64_t incl = run;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -437,139 +454,417 @@ __device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int64_t
   int64_t x = incl - run;  // exclusive prefix of this lane's run
   if (lane == 0) cum[0] = 0;
   for (int s = s0; s < s1; ++s) {
-    x += seq_cost<TC>(a.lens[s], a.maxb, a.B, a.H);
+    x += (int64_t)a.H * row_chunks<TC>(lens[s], a.maxb, a.B);
     cum[s + 1] = x;
   }
 }
 
-template <int DT, int D, int B, int NW>
+// One chunk of the stream: chunk c of row (s, h), in the piece [cb, ce) of
+// that row the slice covers.  `valid` is false once the stream has ended;
+// the other fields then repeat the last chunk.
+struct Chunk {
+  int s, h, L, c, cb, ce;
+  bool valid;
+};
+
+template <int DT, int D, int B, bool APP>
+struct Stream {
+  using G = Geo<D>;
+  static constexpr int LPT = G::LPT, TPI = G::TPI, NL = G::NL, TC = G::TC;
+  static constexpr int NE = TC >= B ? TC / B : 1;  // table entries per chunk
+  static_assert(B % TPI == 0, "a load must not straddle two blocks");
+
+  struct Buf {
+    u32x4 k[NL], v[NL];
+    u32x4 q, kn, vn;
+    int app_blk;
+    bool bad;
+  };
+
+  // constants of the call
+  const uint16_t *kp;
+  const uint16_t *vp;
+  const uint16_t *qp;
+  const uint16_t *knp;
+  const uint16_t *vnp;
+  const int32_t *tables;
+  uint16_t *outp;
+  float *ws_m;
+  float *ws_l;
+  float *ws_o;
+  const int64_t *cum;
+  const int32_t *lens;
+  int64_t blk_stride, num_blocks, new_stride;
+  int S, H, maxb;
+  float scale_log2;
+  int lane, lane_off, row, qoff;
+  int64_t worker;
+  // producer (cursor over the slice)
+  uint64_t it_hi;
+  int cs_, ch_, cL, cn, cc, ccb, cce;  // s, h, L, chunks of row, chunk, piece [cb, ce)
+  uint64_t cseg;                      // cost position of chunk 0 of row (s, h)
+  bool cvalid;
+  Chunk last;
+  // running state of the current piece
+  u32x4 qv;
+  float m, l, acc[8];
+  bool bad;
+
+  __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_,
+                                       int lane_) {
+    kp = reinterpret_cast<const uint16_t *>(a.k_pool);
+    vp = reinterpret_cast<const uint16_t *>(a.v_pool);
+    qp = reinterpret_cast<const uint16_t *>(a.q);
+    knp = reinterpret_cast<const uint16_t *>(a.k_new);
+    vnp = reinterpret_cast<const uint16_t *>(a.v_new);
+    tables = a.tables;
+    outp = reinterpret_cast<uint16_t *>(a.out);
+    ws_m = a.ws_m;
+    ws_l = a.ws_l;
+    ws_o = a.ws_o;
+    cum = cum_;
+    lens = lens_;
+    blk_stride = (int64_t)a.Hkv * B * D;
+    num_blocks = a.num_blocks;
+    new_stride = a.new_stride;
+    S = a.S;
+    H = a.H;
+    maxb = a.maxb;
+    scale_log2 = a.scale_log2;
+    lane = lane_;
+    lane_off = lane * 8;
+    row = lane / LPT;
+    qoff = (lane % LPT) * 8;
+    cvalid = false;
+  }
+
+  __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
+  __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
+
+  // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
+  __device__ __forceinline__ int find_seq(uint64_t p) const {
+    int base = 0, span = S;
+    while (span > 1) {
+      const int step = (span + 63) >> 6;
+      const int idx = base + lane * step;
+      const bool ok = idx < base + span && (uint64_t)cum[idx] <= p;
+      const uint64_t mask = __ballot(ok);
+      const int j = __builtin_amdgcn_readfirstlane(__popcll(mask)) - 1;
+      base += j * step;
+      span = min(step, span - j * step);
+    }
+    return base;
+  }
+
+  // Start the slice [lo, hi) (lo < hi <= total).
+  __device__ __forceinline__ void enter(uint64_t lo, uint64_t hi) {
+    it_hi = hi;
+    const int s = find_seq(lo);
+    const uint64_t base = cum_at(s);
+    cs_ = s;
+    cL = len_at(s);
+    cn = (cL + TC - 1) / TC;  // sequence s has chunks: cum[s + 1] > lo >= cum[s]
+    const uint64_t off = lo - base;  // < H * cn
+    const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
+    ch_ = (int)h;
+    cseg = base + (uint64_t)h * cn;
+    ccb = (int)(lo - cseg);
+    cc = ccb;
+    cce = (int)min((uint64_t)cn, hi - cseg);
+    cvalid = true;
+  }
+
+  // Move to the row after (s, h) inside the slice, or end the slice.
+  __device__ __forceinline__ void next_row() {
+    const uint64_t pos = cseg + cn;
+    if (pos >= it_hi) {
+      cvalid = false;
+      return;
+    }
+    if (ch_ + 1 < H) {
+      ++ch_;
+    } else {
+      int s = cs_ + 1;
+      while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
+      cs_ = s;
+      ch_ = 0;
+      cL = len_at(s);
+      cn = (cL + TC - 1) / TC;
+    }
+    cseg = pos;
+    ccb = 0;
+    cc = 0;
+    cce = (int)min((uint64_t)cn, it_hi - cseg);
+  }
+
+  // The next chunk of the stream.
+  __device__ __forceinline__ Chunk produce() {
+    if (!cvalid) {
+      Chunk none = last;
+      none.valid = false;
+      return none;
+    }
+    Chunk ch;
+    ch.s = cs_;
+    ch.h = ch_;
+    ch.L = cL;
+    ch.c = cc;
+    ch.cb = ccb;
+    ch.ce = cce;
+    ch.valid = true;
+    last = ch;
+    if (cc + 1 < cce) ++cc;
+    else next_row();
+    return ch;
+  }
+
+  __device__ __forceinline__ static int first_block(int c) { return TC >= B ? c * (TC / B) : c / (B / TC); }
+  __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * TC) - 1) / B; }
+  __device__ __forceinline__ static bool is_app_chunk(const Chunk &d) {
+    return d.c == d.ce - 1 && d.ce * TC >= d.L;  // the chunk of token L - 1
+  }
+
+  // Stage 1: this lane's table entry of chunk d (entries past the piece's
+  // last block are clamped to it; their tokens are masked).
+  __device__ __forceinline__ uint32_t load_entries(const Chunk &d) const {
+    const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
+    return (uint32_t)tables[(int64_t)d.s * maxb + lb];
+  }
+
+  // Stage 2: the K/V rows of chunk d, its query row and (fused append) the
+  // new-token rows of its row.
+  __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
+    const int64_t head_base = (int64_t)d.h * B * D;
+    bool bd = false;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      int ei, off;
+      if constexpr (TC >= B) {
+        ei = (i * TPI) / B;
+        off = (i * TPI) % B;
+      } else {
+        ei = 0;
+        off = (d.c % (B / TC)) * TC + i * TPI;
+      }
+      int blk = __builtin_amdgcn_readlane((int)e, ei);
+      if (blk < 0 || (int64_t)blk >= num_blocks) {
+        bd = true;
+        blk = 0;
+      }
+      const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
+      b.k[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
+      b.v[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+    }
+    b.bad = bd;
+    // Issued for every chunk (an L2 hit after the first), so every chunk
+    // issues the same loads.
+    b.q = *reinterpret_cast<const u32x4 *>(qp + ((int64_t)d.s * H + d.h) * D + qoff);
+    if constexpr (APP) {
+      const int64_t ne = (int64_t)d.s * new_stride + (int64_t)d.h * D + qoff;
+      b.kn = *reinterpret_cast<const u32x4 *>(knp + ne);
+      b.vn = *reinterpret_cast<const u32x4 *>(vnp + ne);
+      const int ei = TC >= B ? min(NE - 1, max(0, (d.L - 1) / B - first_block(d.c))) : 0;
+      b.app_blk = __builtin_amdgcn_readlane((int)e, ei);
+    }
+  }
+
+  // Stage 3: fold chunk d into the piece's online softmax; tokens outside the
+  // piece are selected out (score -inf, V row zeroed).
+  __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
+    if (d.c == d.cb) {
+      qv = b.q;
+      m = kNegInf;
+      l = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+      bad = false;
+    }
+    bad = bad || b.bad;
+    const bool app = APP && is_app_chunk(d);
+    if (app) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool sub = (d.c * TC + i * TPI + row) == d.L - 1;
+        b.k[i] = sub ? b.kn : b.k[i];
+        b.v[i] = sub ? b.vn : b.v[i];
+      }
+    }
+    const int t_lo = d.cb * TC;
+    const int t_hi = min(d.L, d.ce * TC);
+    float z[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int tok = d.c * TC + i * TPI + row;
+      const bool valid = tok >= t_lo && tok < t_hi;
+      const float dd = group_sum<LPT>(dot8<DT>(qv, b.k[i])) * scale_log2;
+      z[i] = valid ? dd : kNegInf;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      b.v[i] = valid ? b.v[i] : zero;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) mx = fmaxf(mx, z[i]);
+    const float mnew = fmaxf(m, mx);
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
+    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
+    float pz[NL];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      pz[i] = fast_exp2(z[i] - mref);  // -inf gives 0
+      psum += pz[i];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(pz[i], lo16<DT>(w[j]), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(pz[i], hi16<DT>(w[j]), acc[2 * j + 1]);
+      }
+    }
+    m = mnew;
+    if (d.c == d.ce - 1) finish_piece(d, b, app);
+  }
+
+  __device__ __forceinline__ void finish_piece(const Chunk &d, const Buf &b, bool app) {
+    if (APP && app) {
+      const int blk = b.app_blk;
+      if (blk < 0 || (int64_t)blk >= num_blocks) {
+        bad = true;
+      } else if (row == (d.L - 1) % TPI) {
+        const int64_t base = (int64_t)blk * blk_stride + (int64_t)d.h * B * D + ((d.L - 1) % B) * D + qoff;
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(kp) + base) = b.kn;
+        *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(vp) + base) = b.vn;
+      }
+    }
+    // merge the lane groups (same dims, different tokens)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const float l2 = __shfl_xor(l, off);
+      const float mm = fmaxf(m, m2);
+      const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
+      const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
+      l = l * f1 + l2 * f2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o2 = __shfl_xor(acc[j], off);
+        acc[j] = acc[j] * f1 + o2 * f2;
+      }
+      m = mm;
+    }
+    const int64_t g = (int64_t)d.s * H + d.h;
+    if (lane < LPT) {
+      const float nanv = bad ? __builtin_nanf("") : 0.f;
+      if (d.cb == 0 && d.ce * TC >= d.L) {
+        // the whole row: final output
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t v0 = to16<DT>(acc[2 * j] / l + nanv);
+          const uint32_t v1 = to16<DT>(acc[2 * j + 1] / l + nanv);
+          packed[j] = v0 | (v1 << 16);
+        }
+        const u32x4 ov = {packed[0], packed[1], packed[2], packed[3]};
+        *reinterpret_cast<u32x4 *>(outp + g * D + lane * 8) = ov;
+      } else {
+        const int64_t u = worker + g;
+        float *o = ws_o + u * D + lane * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = acc[j] + nanv;
+        if (lane == 0) {
+          ws_m[u] = m * kLn2 + nanv;  // natural-log units
+          ws_l[u] = l + nanv;
+        }
+      }
+    }
+  }
+
+  // The stream: stage 1 of chunk n + 2, stage 2 of chunk n + 1, stage 3 of
+  // chunk n.  The loop body handles two chunks (one per buffer) and has one
+  // back edge, so the wait before each consume leaves the younger chunk's
+  // loads in flight.  The priority falls from 3 to 0 as the wavefront passes
+  // quarters of its slice (th1..th3 chunks).
+  __device__ __forceinline__ void run(int th1, int th2, int th3) {
+    Chunk d0 = produce();
+    if (!d0.valid) return;
+    int done = 0;
+    Buf ba, bb;
+    uint32_t ea = load_entries(d0);
+    Chunk d1 = produce();
+    uint32_t eb = load_entries(d1);
+    load_kv(d0, ea, ba);
+    for (;;) {
+      const Chunk d2 = produce();
+      ea = load_entries(d2);
+      load_kv(d1, eb, bb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d0, ba);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d1.valid) break;
+      const Chunk d3 = produce();
+      eb = load_entries(d3);
+      load_kv(d2, ea, ba);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d1, bb);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d2.valid) break;
+      d0 = d2;
+      d1 = d3;
+    }
+  }
+};
+
+template <int DT, int D, int B, int NW, bool APP>
 __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a) {
-  using WA = WaveAttn<DT, D, B>;
-  constexpr int TC = WA::TC;
-  constexpr int LPT = WA::LPT;
-  static_assert(TC < B || kTabWindow % (TC / B) == 0, "windows must start on chunk starts");
+  using ST = Stream<DT, D, B, APP>;
+  constexpr int TC = ST::TC;
 
   extern __shared__ int64_t lds[];
-  int64_t *cum = lds;                                           // [S + 1]
-  int32_t *tabs = reinterpret_cast<int32_t *>(lds + a.S + 1);   // [NW][kTabWindow]
+  int64_t *cum = lds;                                         // [S + 1]
+  int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) build_cost_prefix<TC>(a, cum, lane);
+  if (wave == 0) build_cost_prefix<TC>(a, cum, lens, lane);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
   }
-
-  const uint64_t total = (uint64_t)cum[a.S];
+  const uint64_t total = uni64((uint64_t)cum[a.S]);
   if (total == 0) return;
+
   const uint64_t slice = slice_of(total, a.G);
   const int w = blockIdx.x * NW + wave;
   const uint64_t lo = min(total, (uint64_t)w * slice);
   const uint64_t hi = min(total, lo + slice);
   if (lo >= hi) return;
-  int32_t *tab = tabs + wave * kTabWindow;
-  {
-    // sequence holding position lo: largest s with cum[s] <= lo
-    int sa = 0, sb = a.S;  // invariant: cum[sa] <= lo < cum[sb]
-    while (sb - sa > 1) {
-      const int mid = (sa + sb) >> 1;
-      if ((uint64_t)cum[mid] <= lo) sa = mid;
-      else sb = mid;
-    }
 
-    uint64_t pos = lo;
-    int s = sa;
-    while (pos < hi && s < a.S) {
-      const uint64_t cs = (uint64_t)cum[s];
-      if ((uint64_t)cum[s + 1] <= pos) {  // finished or empty sequence
-        ++s;
-        continue;
-      }
-      const int sq = s;  // this piece's sequence
-      const int L = a.lens[sq];
-      const int nch = (L + TC - 1) / TC;
-      const uint64_t per = (uint64_t)(nch + kPieceChunks);
-      const int h = (int)((pos - cs) / per);
-      const uint64_t seg = cs + (uint64_t)h * per + kPieceChunks;  // first chunk's position
-      const int64_t c0 = max((int64_t)0, (int64_t)pos - (int64_t)seg);
-      const int64_t c1 = min((int64_t)nch, (int64_t)hi - (int64_t)seg);
-      pos = seg + nch;  // next (sequence, head)
-      if (h + 1 == a.H) ++s;
-      if (c1 <= c0) continue;
-
-      // ---- one piece: chunks [c0, c1) of (sq, h), tokens [t0, t1)
-      const int t0 = (int)c0 * TC;
-      const int t1 = min(L, (int)c1 * TC);
-      const int c_first = (int)c0;
-      const int c_last = (int)c1 - 1;
-      WA wa;
-      wa.init(a, sq, h, lane);
-      const bool app = a.append && t1 == L;  // this piece holds token L - 1
-      if (app) wa.set_append(a, sq, h, L, lane);
-      const int lb_max = (t1 - 1) / B;
-      const int32_t *trow = a.tables + (int64_t)sq * a.maxb;
-      // Windows of kTabWindow logical blocks; a window holds the chunks whose
-      // first token falls in it (chunks never straddle a window).
-      const int lb_first = (c_first * TC) / B;
-      int lb_last_w = lb_first;
-      for (int lb_w = lb_first; lb_w <= lb_max; lb_w += kTabWindow) {
-        lb_last_w = lb_w;
-        int cs_, ce_;
-        if constexpr (TC >= B) {  // a chunk covers TC / B blocks; windows start on chunk starts
-          cs_ = max(c_first, lb_w / (TC / B));
-          ce_ = min(c_last, (lb_w + kTabWindow) / (TC / B) - 1);
-        } else {                  // B / TC chunks per block
-          cs_ = max(c_first, lb_w * (B / TC));
-          ce_ = min(c_last, (lb_w + kTabWindow) * (B / TC) - 1);
-        }
-        // stage this window's table entries (one coalesced read by the wave)
-        const int cnt = min(kTabWindow, lb_max - lb_w + 1);
-        __builtin_amdgcn_wave_barrier();
-        for (int i = lane; i < cnt; i += 64) tab[i] = trow[lb_w + i];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        wa.run(cs_, 1, ce_ - cs_ + 1, tab, lb_w, lb_max, t0, t1);
-      }
-      // the last window holds the appended token's block (lb_max)
-      if (app) wa.write_append(a, __builtin_amdgcn_readfirstlane(tab[lb_max - lb_last_w]));
-      wa.merge_groups();
-
-      const int64_t g = (int64_t)sq * a.H + h;
-      if (lane < LPT) {
-        const float nanv = wa.bad ? __builtin_nanf("") : 0.f;
-        if (t0 == 0 && t1 == L) {
-          // the whole (sequence, head): final output row
-          uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D + lane * 8;
-          uint32_t packed[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t v0 = to16<DT>(wa.acc[2 * j] / wa.l + nanv);
-            const uint32_t v1 = to16<DT>(wa.acc[2 * j + 1] / wa.l + nanv);
-            packed[j] = v0 | (v1 << 16);
-          }
-          const u32x4 ov = {packed[0], packed[1], packed[2], packed[3]};
-          *reinterpret_cast<u32x4 *>(out_row) = ov;
-        } else {
-          const int64_t u = (int64_t)w + g;  // unique: workers and rows both advance along the cost space
-          float *o = a.ws_o + u * D + lane * 8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] = wa.acc[j] + nanv;
-          if (lane == 0) {
-            a.ws_m[u] = wa.m * kLn2 + nanv;  // natural-log units
-            a.ws_l[u] = wa.l + nanv;
-          }
-        }
-      }
-    }
-  }
+  ST st;
+  st.init(a, cum, lens, lane);
+  st.worker = w;
+  st.enter(lo, hi);
+  const int n = (int)(hi - lo);
+  const int th1 = n / 4, th2 = n / 2, th3 = (3 * n) / 4;
+  __builtin_amdgcn_s_setprio(3);
+  st.run(th1, th2, th3);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // One wavefront per (sequence, head): rows of empty or invalid contexts, and
-// the LSE merge of (sequence, head) rows cut over several workers.  Lane j
-// reads worker t_a + j's (m, l); the merged row then needs one pass.
+// the LSE merge of rows cut over several workers.  Lane j reads the j-th
+// worker's (m, l); the merged row then needs one pass.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
   constexpr int TC = Geo<D>::TC;
@@ -579,7 +874,6 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   const int s = (int)(g / a.H);
   const int h = (int)(g - (int64_t)s * a.H);
   const int L = a.lens[s];
-  const uint64_t cs = (uint64_t)a.ws_cum[s];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;
   if (L <= 0 || L > a.maxb * a.B) {
     const uint16_t v = (L == 0) ? uint16_t(0) : to16<DT>(__builtin_nanf(""));
@@ -587,18 +881,18 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
     return;
   }
   const int nch = (L + TC - 1) / TC;
-  const uint64_t seg = cs + (uint64_t)h * (nch + kPieceChunks) + kPieceChunks;
-  const uint64_t total = (uint64_t)a.ws_cum[a.S];
-  const uint64_t slice = slice_of(total, a.G);
+  const uint64_t seg = (uint64_t)a.ws_cum[s] + (uint64_t)h * nch;
+  const uint64_t end = seg + nch;  // the row's chunks are [seg, end)
+  const uint64_t slice = slice_of((uint64_t)a.ws_cum[a.S], a.G);
   const int64_t t_a = (int64_t)udiv64(seg, slice);
-  const int64_t t_b = (int64_t)udiv64(seg + nch - 1, slice);
-  if (t_a == t_b) return;  // one worker: it wrote the row
+  const int64_t n = (int64_t)udiv64(end - 1, slice) - t_a + 1;
+  if (n <= 1) return;  // one piece: it wrote the row
 
-  // Rows cut over more than 64 workers (contexts of thousands of tokens) loop.
+  auto item_at = [&](int64_t j) { return t_a + j; };
   float M = kNegInf;
-  for (int64_t t0 = t_a; t0 <= t_b; t0 += 64) {
-    const int64_t t = t0 + lane;
-    if (t <= t_b) M = fmaxf(M, a.ws_m[t + g]);
+  for (int64_t j0 = 0; j0 < n; j0 += 64) {
+    const int64_t j = j0 + lane;
+    if (j < n) M = fmaxf(M, a.ws_m[item_at(j) + g]);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -607,29 +901,30 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   float o[D / 64];
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
-  for (int64_t t0 = t_a; t0 <= t_b; t0 += 64) {
-    const int64_t t = t0 + lane;
+  for (int64_t j0 = 0; j0 < n; j0 += 64) {
+    const int64_t j = j0 + lane;
     float f = 0.f, lw = 0.f;
-    if (t <= t_b) {
-      f = fast_exp2((a.ws_m[t + g] - M) * kLog2e);
-      lw = a.ws_l[t + g];
+    if (j < n) {
+      const int64_t u = item_at(j) + g;
+      f = fast_exp2((a.ws_m[u] - M) * kLog2e);
+      lw = a.ws_l[u];
     }
-    const int n = (int)min((int64_t)64, t_b - t0 + 1);
+    const int cnt = (int)min((int64_t)64, n - j0);
     // workers in increasing order; their o rows are fetched 4 at a time
-    for (int j0 = 0; j0 < n; j0 += 4) {
+    for (int q0 = 0; q0 < cnt; q0 += 4) {
       float fj[4], vj[4][D / 64];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int j = min(j0 + q, n - 1);
-        fj[q] = (j0 + q < n) ? __shfl(f, j) : 0.f;
-        const int64_t u = t0 + j + g;
+        const int jj = min(q0 + q, cnt - 1);
+        fj[q] = (q0 + q < cnt) ? __shfl(f, jj) : 0.f;
+        const int64_t u = item_at(j0 + jj) + g;
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) vj[q][k] = a.ws_o[u * D + lane + 64 * k];
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (j0 + q >= n) break;
-        lsum += fj[q] * __shfl(lw, j0 + q);
+        if (q0 + q >= cnt) break;
+        lsum += fj[q] * __shfl(lw, q0 + q);
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) o[k] += fj[q] * vj[q][k];
       }
@@ -657,16 +952,21 @@ struct PartitionsF {
 template <int DT, int D, int B>
 struct BalancedF {
   static hipError_t call(const DecodeParams &a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves>), dim3(a.G / kNumWaves),
-                       dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
+    if (a.append)
+      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, true>), dim3(a.G / kNumWaves),
+                         dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
+    else
+      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, false>), dim3(a.G / kNumWaves),
+                         dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
     return hipGetLastError();
   }
 };
 
 template <int DT, int D, int B>
 struct BalancedPtrF {
-  static const void *call() {
-    return reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves>);
+  static const void *call(int append) {
+    return append ? reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, true>)
+                  : reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false>);
   }
 };
 
@@ -701,11 +1001,11 @@ int decode_chunk_tokens(int head_dim) {
 }
 
 size_t balanced_lds_bytes(int num_seqs) {
-  return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)kNumWaves * kTabWindow * sizeof(int32_t);
+  return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *balanced_kernel(int dtype, int head_dim, int block_size) {
-  return dispatch<BalancedPtrF, const void *>(dtype, head_dim, block_size, nullptr);
+const void *balanced_kernel(int dtype, int head_dim, int block_size, int append) {
+  return dispatch<BalancedPtrF, const void *>(dtype, head_dim, block_size, nullptr, append);
 }
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream) {

@@ -75,21 +75,22 @@ int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
   return nb;
 }
 
-// Workers (wavefronts) the balanced split launches on the current device:
-// kWorkerRounds times as many as the device holds at once.  0 if the device
-// cannot be queried.
+// Workers (wavefronts) the balanced split launches on the current device: as
+// many as the device holds at once.  0 if the device cannot be queried.
 int balanced_waves(const pkv_pool *p, int32_t num_seqs) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
-  const void *k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size);
+  // the fused-append instance (the larger of the two), so that the split and
+  // merge passes of either entry point agree on the worker count
+  const void *k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
   if (!k) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
   const size_t lds = align_up(pkv::balanced_lds_bytes(num_seqs), 4096);
   const int nb = kernel_blocks_per_cu(dev, k, lds);
   if (nb <= 0) return 0;
-  long long g = (long long)cus * nb * pkv::decode_waves() * pkv::kWorkerRounds;
+  long long g = (long long)cus * nb * pkv::decode_waves();
   if (g > pkv::kMaxWorkers) g = pkv::kMaxWorkers / pkv::decode_waves() * pkv::decode_waves();
   return (int)g;
 }
@@ -115,14 +116,14 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
     // work-balanced split; the cost space (chunks) must stay far below 2^47
     const int tc = pkv::decode_chunk_tokens(p->head_dim);
-    const int64_t row_cost = (ctx + tc - 1) / tc + pkv::kPieceChunks;
-    const double cost = (double)num_seqs * num_heads * (double)row_cost;
+    const int64_t row_chunks = (ctx + tc - 1) / tc;
+    const double cost = (double)num_seqs * num_heads * (double)row_chunks;
     if (cost >= 1.0e12) return PKV_ERR_SHAPE;
     lay->balanced = true;
     // a worker's slice is at least kMinWorkerChunks long, which bounds the
     // workers; each (worker, row) pair it touches can hold a partial
-    const int64_t workers =
-        ((int64_t)num_seqs * num_heads * row_cost + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
+    const int64_t most = (int64_t)num_seqs * num_heads * row_chunks;
+    const int64_t workers = (most + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
     const int64_t units = workers + (int64_t)num_seqs * num_heads;
     lay->units = units;
     const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);

@@ -19,24 +19,9 @@ namespace pkv {
 constexpr int kDecodeLoads = PKV_DECODE_LOADS;
 // Largest number of table entries one fixed partition stages in LDS.
 constexpr int kTabMax = 512;
-// Table entries one wavefront stages per LDS window in the balanced split.
-constexpr int kTabWindow = 64;
-// Balanced split: the work of a (sequence, head) is counted in chunks (one
-// wavefront step), plus a fixed overhead of kPieceChunks chunks per piece.
-#ifndef PKV_PIECE_CHUNKS
-#define PKV_PIECE_CHUNKS 1
-#endif
-constexpr int kPieceChunks = PKV_PIECE_CHUNKS;
 // Balanced split: smallest slice a worker gets, in chunks (this also bounds
 // the number of workers, hence of partial results, independently of the GPU).
 constexpr int kMinWorkerChunks = 8;
-// Balanced split: workers launched per wavefront the GPU holds at once; with
-// more than one round the hardware dispatcher balances rounds as slots free
-// up (build-time setting).
-#ifndef PKV_WORKER_ROUNDS
-#define PKV_WORKER_ROUNDS 1
-#endif
-constexpr int kWorkerRounds = PKV_WORKER_ROUNDS;
 // Balanced split: most sequences (the per-workgroup cost prefix lives in LDS).
 constexpr int kBalancedMaxSeqs = 4096;
 // Balanced split: most wavefronts launched.
@@ -54,7 +39,7 @@ struct DecodeParams {
   float *ws_m;             // partial maxima
   float *ws_l;             // partial sums
   float *ws_o;             // partial weighted V sums, D per partial
-  int64_t *ws_cum;         // balanced split: cost prefix over sequences [S + 1]
+  int64_t *ws_cum;         // balanced split: chunk prefix over sequences [S + 1]
   float scale_log2;        // scale * log2(e)
   int64_t num_blocks;      // N
   int32_t S, H, Hkv, maxb, B, D, P, MP;
@@ -76,8 +61,8 @@ int decode_waves();
 int decode_chunk_tokens(int head_dim);
 // Dynamic LDS of the balanced kernel for num_seqs sequences.
 size_t balanced_lds_bytes(int num_seqs);
-// The balanced kernel instance for (dtype, D, B), for occupancy queries.
-const void *balanced_kernel(int dtype, int head_dim, int block_size);
+// The balanced kernel instance for (dtype, D, B, append), for occupancy queries.
+const void *balanced_kernel(int dtype, int head_dim, int block_size, int append);
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
