@@ -145,8 +145,8 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
  *  - partition_size > 0: fixed partitions of P tokens, partition p holding
  *    tokens [p*P, min((p+1)*P, L)).  P must be a multiple of B and of the 16
  *    (D = 128) or 32 (D = 64) tokens one wavefront step covers, with P / B <= 512.
- *  - partition_size == 0: a work-balanced split.  All (sequence, head, token)
- *    work, each (sequence, head) also costing a fixed overhead, is cut into
+ *  - partition_size == 0: a work-balanced split.  All the batch's chunks of
+ *    16 (D = 128) or 32 (D = 64) tokens of one (sequence, head) are cut into
  *    equal slices, one per wavefront, with as many wavefronts as the device
  *    holds at once, so batches with very different context lengths keep
  *    every compute unit busy.  The cut points depend on the context lengths
@@ -166,8 +166,9 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
  *   [ m: U floats ][ l: U floats ][ o: U * D floats ], each section starting on
  *   a 256-byte boundary.  m is the partition's largest score z = scale * q.k
  *   (natural-log units), l = sum exp(z - m), o = sum exp(z - m) * v.
- * The balanced split's workspace holds a cost prefix and per-piece partial
- * results in the same (m, l, o) form; its layout is internal.  One call at a
+ * The balanced split's workspace holds a chunk prefix over sequences and
+ * per-piece partial results in the same (m, l, o) form; its layout is
+ * internal.  One call at a
  * time may use a workspace.
  */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
