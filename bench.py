@@ -52,6 +52,9 @@ def parse(argv=None):
                     help="append with pkv_slot_mapping + pkv_reshape_and_cache, then decode")
     ap.add_argument("--duplicate-shared", action="store_true",
                     help="shared workload: give every sibling private copies of the prefix blocks (control)")
+    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
+                    help="decode (the hot path, default) or the batched block copy of copy-on-write")
+    ap.add_argument("--copy-pairs", type=int, default=1024, help="block pairs per copy launch (--op copy_blocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args(argv)
@@ -85,6 +88,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
 
     t = build_tables(args.config, block_size=args.block_size)
+    if args.op == "copy_blocks":
+        return bench_copy_blocks(args, t, pkv, lib, dev)
     dup = None
     if args.duplicate_shared:
         dup_tab, copies, n_total = duplicate_shared(t)
@@ -245,6 +250,73 @@ def main(argv=None) -> int:
                      "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_copy_blocks(args, t, pkv, lib, dev) -> int:
+    """Batched block copy (copy-on-write): `--copy-pairs` random (src, dst)
+    pairs of the workload's pool per launch, both pools; bytes = every copied
+    block read once and written once."""
+    import numpy as np
+    import torch
+
+    from synth import make_pools
+
+    kp, vp = make_pools(t, dev, poison=False)
+    n = args.copy_pairs
+    if 2 * n > t.num_blocks:
+        print(f"--copy-pairs {n} needs {2 * n} distinct blocks; the pool has {t.num_blocks}", file=sys.stderr)
+        return 2
+    rng = np.random.default_rng(7)
+    sets = []
+    for r in range(args.replicas):  # different pairs per launch, so no launch finds the last one's blocks cached
+        perm = rng.permutation(t.num_blocks)
+        sets.append(torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)).to(dev))
+    desc = pkv.pool_desc_of(kp)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+    dref = ctypes.byref(desc)
+
+    def step(i):
+        st = lib.pkv_copy_blocks(kp.data_ptr(), vp.data_ptr(), sets[i % len(sets)].data_ptr(), n, dref, sp)
+        if st != 0:
+            raise RuntimeError(pkv.status_string(st))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(args.warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    block_bytes = t.num_heads * t.block_size * t.head_dim * 2
+    nbytes = 2 * 2 * n * block_bytes + n * 16  # both pools, read + write, and the pairs
+    kern_mean_ms = float(np.mean(kern_ms))
+    line = {
+        "metric": "batched block copy (copy-on-write) achieved HBM GB/s, read + write",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.config} pool ({t.num_blocks} blocks of {t.num_heads} x {t.block_size} x "
+                               f"{t.head_dim}): {n} random block pairs per launch, K and V",
+                   "block_pairs": n, "block_bytes": block_bytes, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "copy_blocks_kernel", "bound": "hbm",
+                     "achieved": round(nbytes / (kern_mean_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (kern_mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": nbytes, "mean_launch_us": round(kern_mean_ms * 1e3, 2)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -137,6 +137,23 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
                                  const pkv_pool *p, void *stream);
 
 /*
+ * pkv_copy_blocks -- copy whole pool blocks (every head, every slot) of both
+ * pools in one launch: for each pair i, with (src, dst) = block_pairs[i],
+ *   k_pool[dst][:][:][:] = k_pool[src][:][:][:],  v_pool likewise.
+ * This is the copy of copy-on-write: a sequence about to append into a
+ * partly filled block it shares with other sequences first gets a private
+ * copy ("PagedAttention 完全拆解", 内存共享 / Figure 8 and the fork / append
+ * primitives).  The copy is bit-exact.
+ *
+ *   block_pairs  int64 [num_pairs][2] (src, dst), device memory, 8-byte aligned
+ * Pairs with src or dst outside [0, N) are skipped.  The copies run
+ * concurrently: a dst must appear once, and no dst may be the src of another
+ * pair in the same call.  num_pairs == 0 is a no-op.
+ */
+pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pairs, int32_t num_pairs,
+                           const pkv_pool *p, void *stream);
+
+/*
  * How the context is split, and the workspace.
  *
  * partition_size selects how each sequence's context is cut into pieces that

@@ -60,6 +60,7 @@ __all__ = [
     "slot_of",
     "slot_mapping",
     "reshape_and_cache",
+    "copy_blocks",
     "gather",
     "attend",
     "decode",
@@ -177,6 +178,28 @@ def reshape_and_cache(k_bits, v_bits, k_pool_bits, v_pool_bits, slots, block_siz
         for h in range(k_bits.shape[1]):
             k_pool_bits[blk, h, off, :] = k_bits[t, h, :]
             v_pool_bits[blk, h, off, :] = v_bits[t, h, :]
+
+
+def copy_blocks(k_pool_bits, v_pool_bits, pairs) -> None:
+    """Copy whole pool blocks, in place: ``pool[dst] = pool[src]`` for every
+    (src, dst) pair, every head and every slot, in both pools.
+
+    [PA] 内存共享 (Figure 8) and the fork / append primitives: before a
+    sequence writes into a partly filled block it shares, that block is copied
+    to a private block and the writer's table is redirected to the copy.  The
+    sources are read as they were before the call (no destination is also a
+    source).  Pairs with an index outside the pool are skipped.  Bit patterns
+    are moved, so the copy is exact.
+    """
+    num_blocks = k_pool_bits.shape[0]
+    k_src = k_pool_bits.copy()
+    v_src = v_pool_bits.copy()
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if not (0 <= src < num_blocks and 0 <= dst < num_blocks):
+            continue
+        k_pool_bits[dst] = k_src[src]
+        v_pool_bits[dst] = v_src[src]
 
 
 # ----------------------------------------------------------------------------

@@ -7,7 +7,7 @@ it plus byte accounting for the roofline.  Build the library with
 """
 
 from ._binding import (EXPORTS, LIB_PATH, PagedKVError, PoolDesc, alloc_workspace,  # noqa: F401
-                       decode_merge, decode_partition_size, decode_partitions, decode_workspace_bytes,
+                       copy_blocks, decode_merge, decode_partition_size, decode_partitions, decode_workspace_bytes,
                        load_library, make_pool_desc, paged_attention_decode, paged_attention_decode_append, pool_bytes, pool_desc_of,
                        pool_index, reshape_and_cache, slot_mapping, status_string, version,
                        workspace_views)

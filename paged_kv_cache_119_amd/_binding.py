@@ -26,6 +26,7 @@ EXPORTS = (
     "pkv_pool_index",
     "pkv_slot_mapping",
     "pkv_reshape_and_cache",
+    "pkv_copy_blocks",
     "pkv_decode_partition_size",
     "pkv_decode_workspace_bytes",
     "pkv_paged_attention_decode",
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_pool_index": (i64, [pool, i64, i32, i32, i32]),
         "pkv_slot_mapping": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, i32, pool, vp]),
         "pkv_reshape_and_cache": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, i32, pool, vp]),
+        "pkv_copy_blocks": (ctypes.c_int, [vp, vp, vp, i32, pool, vp]),
         "pkv_decode_partition_size": (i32, [i32, i32, i32, pool, i32]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, pool, i32]),
         "pkv_paged_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
@@ -229,6 +231,21 @@ def reshape_and_cache(k, v, k_pool, v_pool, slot_mapping):
     _check(st, "pkv_reshape_and_cache")
 
 
+def copy_blocks(k_pool, v_pool, block_pairs):
+    """Copy whole pool blocks: ``block_pairs`` is int64 ``[n, 2]`` of (src, dst)."""
+    torch = _torch()
+    lib = load_library()
+    desc = _check_pools(k_pool, v_pool)
+    dev = k_pool.device
+    _need(block_pairs, "block_pairs", dtype=torch.int64, ndim=2, device=dev)
+    if block_pairs.shape[1] != 2 or not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be a contiguous [n, 2] tensor")
+    n = int(block_pairs.shape[0])
+    st = lib.pkv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), block_pairs.data_ptr(), n, ctypes.byref(desc),
+                             _stream_ptr(dev))
+    _check(st, "pkv_copy_blocks")
+
+
 def decode_partition_size(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size=0) -> int:
     desc = pool_desc_of(k_pool)
     return int(load_library().pkv_decode_partition_size(int(num_seqs), int(num_heads), int(max_blocks_per_seq),
@@ -242,9 +259,8 @@ def decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, part
 
 
 def alloc_workspace(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size=0):
-    """A caller-owned workspace tensor of the size the decode call needs,
-    zero-filled (the balanced split's counters must start at zero; every call
-    leaves them zero again)."""
+    """A caller-owned workspace tensor of the size the decode call needs
+    (zero-filled, which the kernels do not require)."""
     torch = _torch()
     n = decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size)
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=k_pool.device)

@@ -9,6 +9,12 @@
 //
 // Slot translation (iaim.asia block-table article, "KV Cache 如何按块分配",
 // BLOCK_SIZE=16 table): slot = block_tables[s][pos / B] * B + pos % B.
+//
+// Block copy ("PagedAttention 完全拆解", 内存共享 and Figure 8: a sequence about
+// to write into a block it shares first gets a private copy of it): a batch
+// of (src, dst) pairs is copied in one launch.  A pool block holds all heads
+// ([Hkv][B][D]), so each copy is one contiguous run per pool; each thread
+// moves one 16-byte piece of K and the same piece of V.
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -60,7 +66,40 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(int64_t *__restrict__
   slots[t] = out;
 }
 
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *__restrict__ kp,
+                                                          uint16_t *__restrict__ vp,
+                                                          const int64_t *__restrict__ pairs,
+                                                          int64_t pieces,  // 16-byte pieces per block
+                                                          int64_t total, int64_t num_blocks) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t i = idx / pieces;
+  const int64_t piece = idx - i * pieces;
+  const int64_t src = pairs[2 * i];
+  const int64_t dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t so = (src * pieces + piece) * 8;
+  const int64_t d_o = (dst * pieces + piece) * 8;
+  const u32x4 kv = *reinterpret_cast<const u32x4 *>(kp + so);
+  const u32x4 vv = *reinterpret_cast<const u32x4 *>(vp + so);
+  *reinterpret_cast<u32x4 *>(kp + d_o) = kv;
+  *reinterpret_cast<u32x4 *>(vp + d_o) = vv;
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
+                              int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
+                              hipStream_t stream) {
+  const int64_t pieces = (int64_t)Hkv * B * D / 8;
+  const int64_t total = (int64_t)n * pieces;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<uint16_t *>(k_pool), reinterpret_cast<uint16_t *>(v_pool), pairs,
+                     pieces, total, num_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, const void *v,
                                     int64_t k_stride, int64_t v_stride, const int64_t *slots,

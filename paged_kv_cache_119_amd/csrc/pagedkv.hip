@@ -316,6 +316,21 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
                                                   p->num_blocks, (hipStream_t)stream));
 }
 
+pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pairs, int32_t num_pairs,
+                           const pkv_pool *p, void *stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !block_pairs) return PKV_ERR_NULL;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_pairs, 8)) return PKV_ERR_SHAPE;
+  if ((int64_t)num_pairs * p->num_kv_heads * p->block_size * (p->head_dim / 8) > ((int64_t)1 << 40))
+    return PKV_ERR_SHAPE;
+  return hip_status(pkv::launch_copy_blocks(k_pool, v_pool, block_pairs, num_pairs, p->num_kv_heads,
+                                            p->block_size, p->head_dim, p->num_blocks,
+                                            (hipStream_t)stream));
+}
+
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                   const pkv_pool *p, int32_t partition_size) {
   Layout lay;

@@ -72,6 +72,10 @@ hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, c
                                     int32_t T, int32_t Hkv, int32_t B, int32_t D,
                                     int64_t num_blocks, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
+                              int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
+                              hipStream_t stream);
+
 hipError_t launch_slot_mapping(int64_t *slots, const int32_t *tables, int32_t S, int32_t maxb,
                                const int32_t *seq, const int32_t *pos, int32_t T, int32_t B,
                                int64_t num_blocks, hipStream_t stream);

@@ -112,3 +112,103 @@ def test_append_full_size_llama13b_new_tokens():
     v0[blk, :, off, :] = vnew
     assert torch.equal(kp.view(torch.int16), k0.view(torch.int16))
     assert torch.equal(vp.view(torch.int16), v0.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Block copy (copy-on-write)
+# ---------------------------------------------------------------------------
+
+def _pairs_tensor(pairs):
+    return torch.tensor(np.array(pairs, np.int64).reshape(-1, 2), dtype=torch.int64, device=DEV)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64)])
+def test_copy_blocks_copy_on_write_then_decode(dtype, D):
+    """Forked samples write into their shared, partly filled last block: the
+    allocator's copies run through pkv_copy_blocks (whole pools bit-exact
+    against the oracle's copy), each sample appends its token, and decoding
+    every sample matches the oracle."""
+    from synth import BlockAllocator
+    from .gpu_util import assert_close
+    log(f"copy_blocks: copy-on-write of forked samples {dtype} D={D}")
+    rng = np.random.default_rng(31)
+    N, H, B = 300, 4, 16
+    a = BlockAllocator.create(N, B, pop_order=list(rng.permutation(N)))
+    samples = []
+    for _ in range(10):
+        p = a.new_seq()
+        a.append_tokens(p, int(rng.integers(1, 120)))
+        samples += [p] + [a.fork(p) for _ in range(int(rng.integers(1, 4)))]
+    new_slots = {}
+    for sid in samples:
+        e = a.append(sid)
+        new_slots[sid] = e.block * B + e.filled - 1
+    a.check()
+    assert a.copies, "the scenario must trigger copy-on-write"
+    kp = normal_16bit((N, H, B, D), dtype, DEV, 301)
+    vp = normal_16bit((N, H, B, D), dtype, DEV, 302)
+    kb, vb = to_bits(kp), to_bits(vp)
+    pkv.copy_blocks(kp, vp, _pairs_tensor(a.copies))
+    po.copy_blocks(kb, vb, a.copies)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kp), kb) and np.array_equal(to_bits(vp), vb)
+    # each sample appends one token, then every sample decodes
+    S = len(samples)
+    knew = normal_16bit((S, H, D), dtype, DEV, 303)
+    vnew = normal_16bit((S, H, D), dtype, DEV, 304)
+    slots = np.array([new_slots[sid] for sid in samples], np.int64)
+    pkv.reshape_and_cache(knew, vnew, kp, vp, torch.from_numpy(slots).to(DEV))
+    po.reshape_and_cache(to_bits(knew), to_bits(vnew), kb, vb, slots, B)
+    maxb = max(len(a.tables[sid]) for sid in samples)
+    tables = np.full((S, maxb), -1, np.int32)
+    lens = np.zeros(S, np.int32)
+    for i, sid in enumerate(samples):
+        ids = a.block_ids(sid)
+        tables[i, :len(ids)] = ids
+        lens[i] = (len(ids) - 1) * B + a.tables[sid][-1].filled
+    q = normal_16bit((S, H, D), dtype, DEV, 305)
+    out = pkv.paged_attention_decode(q, kp, vp, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV),
+                                     D ** -0.5)
+    ref = po.decode(to_bits(q), kb, vb, tables, lens, D ** -0.5, B, dtype)
+    assert_close(to_bits(out), ref, dtype, f"copy-on-write decode {dtype}")
+
+
+def test_copy_blocks_exact_skips_invalid_pairs_and_empty_calls():
+    log("copy_blocks: random pairs, invalid pairs, empty call")
+    rng = np.random.default_rng(32)
+    N, H, B, D = 64, 8, 32, 128
+    kp = normal_16bit((N, H, B, D), "f16", DEV, 311)
+    vp = normal_16bit((N, H, B, D), "f16", DEV, 312)
+    kb, vb = to_bits(kp), to_bits(vp)
+    perm = rng.permutation(N)
+    pairs = [(int(perm[i]), int(perm[20 + i])) for i in range(20)]  # sources and destinations disjoint
+    pairs += [(-1, int(perm[50])), (int(perm[51]), N), (N + 5, -2)]
+    pkv.copy_blocks(kp, vp, _pairs_tensor(pairs))
+    po.copy_blocks(kb, vb, pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kp), kb) and np.array_equal(to_bits(vp), vb)
+    pkv.copy_blocks(kp, vp, torch.empty((0, 2), dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kp), kb)
+    with pytest.raises((TypeError, ValueError)):
+        pkv.copy_blocks(kp, vp, _pairs_tensor(pairs).to(torch.int32))
+
+
+def test_copy_blocks_full_size_llama13b():
+    """4096 copies in the 3.3 GB bf16 pools: every destination equals its
+    source, every other block is unchanged."""
+    log("copy_blocks llama13b full size: 4096 pairs")
+    t = build_tables("llama13b")
+    kp, vp = make_pools(t, DEV, poison=False)
+    rng = np.random.default_rng(33)
+    perm = rng.permutation(t.num_blocks)
+    src, dst = perm[:4096], perm[4096:8192]
+    k0, v0 = kp.clone(), vp.clone()
+    pkv.copy_blocks(kp, vp, _pairs_tensor(np.stack([src, dst], 1)))
+    torch.cuda.synchronize()
+    s_t = torch.from_numpy(src).to(DEV)
+    d_t = torch.from_numpy(dst).to(DEV)
+    k0[d_t] = k0[s_t]
+    v0[d_t] = v0[s_t]
+    assert torch.equal(kp.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(vp.view(torch.int16), v0.view(torch.int16))

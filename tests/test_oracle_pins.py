@@ -358,6 +358,80 @@ def test_append_writes_exact_rows_and_nothing_else():
     assert np.array_equal(vp[untouched], vp0[untouched])
 
 
+def _fig8_copy_on_write_holds(copy_fn, golden_dir) -> bool:
+    """Figure 8 of [PA] 内存共享 run through the allocator and the oracle's
+    append: after A1's copy-on-write (done by ``copy_fn``) and one new token per
+    sample, both samples read the prompt's 7 rows unchanged and their own
+    eighth row."""
+    with open(os.path.join(golden_dir, "fig8_copy_on_write.json")) as f:
+        g = json.load(f)
+    B, H, D, N = g["block_size"], 2, 8, 16
+    head = g["pop_order_head"]
+    a = BlockAllocator.create(N, B, pop_order=list(head) + [b for b in range(N) if b not in head])
+    rng = np.random.default_rng(24)
+    kp = np.full((N, H, B, D), 0x7E55, np.uint16)
+    vp = kp.copy()
+    a1 = a.new_seq()
+    prompt_k = rng.integers(0, 0x7C00, size=(g["prompt_tokens"], H, D)).astype(np.uint16)
+    prompt_v = rng.integers(0, 0x7C00, size=(g["prompt_tokens"], H, D)).astype(np.uint16)
+    slots = []
+    for _ in range(g["prompt_tokens"]):
+        e = a.append(a1)
+        slots.append(e.block * B + e.filled - 1)
+    po.reshape_and_cache(prompt_k, prompt_v, kp, vp, np.array(slots, np.int64), B)
+    a2 = a.fork(a1)
+    new = {}
+    for sid in (a1, a2):
+        e = a.append(sid)
+        copy_fn(kp, vp, list(a.copies))
+        a.copies.clear()
+        k = rng.integers(0, 0x7C00, size=(1, H, D)).astype(np.uint16)
+        v = rng.integers(0, 0x7C00, size=(1, H, D)).astype(np.uint16)
+        po.reshape_and_cache(k, v, kp, vp, np.array([e.block * B + e.filled - 1], np.int64), B)
+        new[sid] = (k[0], v[0])
+    L = g["prompt_tokens"] + 1
+    for sid in (a1, a2):
+        row = np.array(a.block_ids(sid) + [-1] * 4, np.int32)
+        for h in range(H):
+            K = po.gather(kp, row, L, B, h)
+            V = po.gather(vp, row, L, B, h)
+            if not (np.array_equal(K[:-1], prompt_k[:, h]) and np.array_equal(V[:-1], prompt_v[:, h])):
+                return False
+            if not (np.array_equal(K[-1], new[sid][0][h]) and np.array_equal(V[-1], new[sid][1][h])):
+                return False
+    return True
+
+
+def test_copy_blocks_completes_fig8_copy_on_write(golden_dir):
+    assert _fig8_copy_on_write_holds(po.copy_blocks, golden_dir)
+
+
+def test_copy_blocks_pin_catches_planted_mistakes(golden_dir):
+    def no_copy(kp, vp, pairs):
+        pass
+
+    def swapped(kp, vp, pairs):
+        po.copy_blocks(kp, vp, [(d, s_) for s_, d in pairs])
+
+    assert not _fig8_copy_on_write_holds(no_copy, golden_dir)
+    assert not _fig8_copy_on_write_holds(swapped, golden_dir)
+
+
+def test_copy_blocks_exact_and_skips_invalid_pairs():
+    rng = np.random.default_rng(25)
+    N, H, B, D = 9, 2, 4, 8
+    kp = rng.integers(0, 0x7C00, size=(N, H, B, D)).astype(np.uint16)
+    vp = rng.integers(0, 0x7C00, size=(N, H, B, D)).astype(np.uint16)
+    kp0, vp0 = kp.copy(), vp.copy()
+    pairs = [(0, 5), (5, 6), (-1, 7), (2, N), (3, 8)]  # 5 is read before it is overwritten
+    po.copy_blocks(kp, vp, pairs)
+    for b in range(N):
+        want = {5: 0, 6: 5, 8: 3}.get(b, b)
+        assert np.array_equal(kp[b], kp0[want]) and np.array_equal(vp[b], vp0[want])
+    po.copy_blocks(kp, vp, [])
+    assert np.array_equal(kp[0], kp0[0])
+
+
 def test_slot_mapping_padding():
     tab = np.array([[4, 2], [0, 1]], np.int32)
     got = po.slot_mapping(tab, [0, -1, 1, 1], [5, 3, -2, 4], 4)
