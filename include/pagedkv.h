@@ -211,7 +211,14 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *                 ceil(L / B) entries of a row are read
  *   context_lens  int32 [num_seqs]
  *   scale         float32, normally 1 / sqrt(D)
- *   num_heads     query heads; must equal Hkv in this version
+ *   num_heads     query heads, a multiple of Hkv; query head h reads KV head
+ *                 h / (num_heads / Hkv) (grouped-query attention, the
+ *                 Llama-2-70B shape of the iaim.asia block-table article,
+ *                 "末尾块的内部碎片").  With more than one query head per KV
+ *                 head the matrix-core kernel runs: head_dim 128,
+ *                 partition_size 0 and at most 16 query heads per KV head,
+ *                 else PKV_ERR_UNSUPPORTED; the fused-append entry points
+ *                 need num_heads == Hkv.
  *   out           must be 16-byte aligned
  *   workspace     >= pkv_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                 may be NULL only when that size is 0
@@ -308,6 +315,35 @@ pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_
                             int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
                             int32_t partition_size, const void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * pkv_paged_attention_multi -- several query tokens per sequence over paged
+ * K/V, causal: query i (0 <= i < num_queries) of sequence s sits at position
+ * L - num_queries + i (the last num_queries tokens of the context, already
+ * appended) and attends over tokens 0 .. L - num_queries + i, with the same
+ * attention equation and rules as pkv_paged_attention_decode (the per-token
+ * equation of "PagedAttention 完全拆解", 背景, for each query row; a query
+ * attends to itself).  This serves chunked prefill and the verification of
+ * several candidate tokens in one step.
+ *
+ *   out, q        [num_seqs][num_queries][num_heads][head_dim], element type of
+ *                 the pool; out 16-byte aligned
+ *   num_heads     a multiple of Hkv (as above); (num_heads / Hkv) *
+ *                 num_queries <= 16 query rows per KV head, head_dim 128,
+ *                 else PKV_ERR_UNSUPPORTED
+ *   workspace     >= pkv_multi_workspace_bytes(...) bytes, 256-byte aligned
+ * Rows of a sequence with 0 < L < num_queries (or an invalid L) are NaN (the
+ * queries must be part of the context); L == 0 gives zero rows.  Runs a split
+ * pass and a merge pass (balanced split) on `stream`.
+ * pkv_multi_workspace_bytes returns 0 for invalid or unsupported arguments.
+ */
+size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                 int32_t max_blocks_per_seq, const pkv_pool *p);
+pkv_status pkv_paged_attention_multi(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                     int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
+                                     size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

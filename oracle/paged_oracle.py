@@ -65,9 +65,11 @@ __all__ = [
     "attend",
     "decode",
     "decode_one",
+    "decode_rows",
     "partials",
     "lse_merge",
     "decode_partitioned",
+    "dense_causal",
     "dense_causal_last_row",
 ]
 
@@ -270,6 +272,40 @@ def decode(q_bits, k_pool_bits, v_pool_bits, block_tables, context_lens,
     return out
 
 
+def decode_rows(q_bits, k_pool_bits, v_pool_bits, block_tables, context_lens,
+                scale: float, block_size: int, dtype: str) -> np.ndarray:
+    """Float64 attention of several query rows per sequence: ``q_bits`` is
+    ``[S, Q, H, D]`` over pools ``[N, Hkv, B, D]``; returns ``[S, Q, H, D]``.
+
+    * Query head h reads KV head ``h // (H // Hkv)``: grouped-query attention,
+      where a group of query heads shares one KV head (the Llama-2-70B shape of
+      [GA] "末尾块的内部碎片", 8 KV heads).
+    * Query i of sequence s is the token at position ``L - Q + i`` (the last Q
+      tokens of the context) and attends over tokens ``0 .. L - Q + i``: the
+      per-token equation of [PA] 背景, whose sum runs up to the query's own
+      position.  With Q = 1 and H = Hkv this is ``decode``.
+
+    Each row walks the table, gathers its visible K and V rows and attends.
+    """
+    S, Q, H, D = q_bits.shape
+    Hkv = k_pool_bits.shape[1]
+    G = H // Hkv
+    out = np.zeros((S, Q, H, D), dtype=np.float64)
+    scale64 = float(np.float32(scale))
+    for s in range(S):
+        L = int(context_lens[s])
+        row = np.asarray(block_tables)[s]
+        for i in range(Q):
+            visible = L - Q + 1 + i if L > 0 else 0
+            for h in range(H):
+                kvh = h // G
+                K = bits_to_f64(gather(k_pool_bits, row, visible, block_size, kvh), dtype)
+                V = bits_to_f64(gather(v_pool_bits, row, visible, block_size, kvh), dtype)
+                o, _, _, _ = attend(bits_to_f64(q_bits[s, i, h], dtype), K, V, scale64)
+                out[s, i, h] = o
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Split context: partial results and the log-sum-exp merge
 # ----------------------------------------------------------------------------
@@ -339,8 +375,8 @@ def decode_partitioned(q_bits, k_pool_bits, v_pool_bits, block_tables, context_l
 # Brute force: dense causal attention over an unpaged sequence
 # ----------------------------------------------------------------------------
 
-def dense_causal_last_row(Q64: np.ndarray, K64: np.ndarray, V64: np.ndarray, scale64: float) -> np.ndarray:
-    """Full T x T causal attention for one head, returning row T-1.
+def dense_causal(Q64: np.ndarray, K64: np.ndarray, V64: np.ndarray, scale64: float) -> np.ndarray:
+    """Full T x T causal attention for one head, every row: ``[T, D]``.
 
     [PA] 背景: position i attends to positions 1..i.  Scores above the diagonal
     are set to -inf before a row softmax; written with explicit loops so it
@@ -363,4 +399,9 @@ def dense_causal_last_row(Q64: np.ndarray, K64: np.ndarray, V64: np.ndarray, sca
         for j in range(T):
             if ex[j] != 0.0:
                 out[i] += (ex[j] / tot) * V64[j]
-    return out[T - 1]
+    return out
+
+
+def dense_causal_last_row(Q64: np.ndarray, K64: np.ndarray, V64: np.ndarray, scale64: float) -> np.ndarray:
+    """Row T-1 of ``dense_causal``: what a decode step of the last token sees."""
+    return dense_causal(Q64, K64, V64, scale64)[Q64.shape[0] - 1]

@@ -34,6 +34,8 @@ EXPORTS = (
     "pkv_decode_partitions_append",
     "pkv_decode_partitions",
     "pkv_decode_merge",
+    "pkv_multi_workspace_bytes",
+    "pkv_paged_attention_multi",
 )
 
 
@@ -86,6 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_decode_partitions": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32,
                                                  pool, i32, vp, sz, vp]),
         "pkv_decode_merge": (ctypes.c_int, [vp, vp, i32, i32, i32, pool, i32, vp, sz, vp]),
+        "pkv_multi_workspace_bytes": (sz, [i32, i32, i32, i32, pool]),
+        "pkv_paged_attention_multi": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32,
+                                                     pool, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -306,6 +311,45 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
                                         maxb, ctypes.byref(desc), int(partition_size), ws_ptr, ws_bytes,
                                         _stream_ptr(k_pool.device))
     _check(st, "pkv_paged_attention_decode")
+    return out
+
+
+def multi_workspace_bytes(num_seqs, num_queries, num_heads, max_blocks_per_seq, k_pool) -> int:
+    desc = pool_desc_of(k_pool)
+    return int(load_library().pkv_multi_workspace_bytes(int(num_seqs), int(num_queries), int(num_heads),
+                                                        int(max_blocks_per_seq), ctypes.byref(desc)))
+
+
+def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, workspace=None):
+    """Several query tokens per sequence over paged K/V: ``q`` is [S, Q, H, D];
+    query i of sequence s sits at position context_lens[s] - Q + i and attends
+    causally.  Returns ``out`` [S, Q, H, D]."""
+    torch = _torch()
+    lib = load_library()
+    desc = _check_pools(k_pool, v_pool)
+    dev = k_pool.device
+    _need(q, "q", dtype=k_pool.dtype, ndim=4, device=dev)
+    S, Q, H, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {desc.head_dim}")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("q, block_tables and context_lens disagree on the number of sequences")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, ndim=4, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    maxb = int(block_tables.shape[1])
+    need = multi_workspace_bytes(S, Q, H, maxb, k_pool)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.pkv_paged_attention_multi(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, Q, H, maxb,
+                                       ctypes.byref(desc), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    _check(st, "pkv_paged_attention_multi")
     return out
 
 

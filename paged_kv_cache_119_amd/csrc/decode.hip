@@ -42,6 +42,7 @@
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_split.h"
 
 namespace pkv {
 
@@ -399,65 +400,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // the cache), so the compiler's waits stay exact.  A wavefront lowers its
 // priority as it progresses through its slice, so wavefronts that share a
 // SIMD finish together instead of in order of age.
-
-// Chunks of a row of L tokens; invalid and empty contexts have none.
-template <int TC>
-__device__ __forceinline__ int row_chunks(int L, int maxb, int B) {
-  return (L > 0 && L <= maxb * B) ? (L + TC - 1) / TC : 0;
-}
-
-// floor(x / d) for d >= 1 without the slow 64-bit integer division: a double
-// estimate corrected to the exact quotient with 64-bit multiplies.
-__device__ __forceinline__ uint64_t udiv64(uint64_t x, uint64_t d) {
-  uint64_t q = (uint64_t)((double)x / (double)d);
-  while (q > 0 && q * d > x) --q;
-  while ((q + 1) * d <= x) ++q;
-  return q;
-}
-
-__device__ __forceinline__ uint64_t uni64(uint64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Workers share the cost space in equal slices: worker w owns positions
-// [min(total, w * slice), min(total, (w + 1) * slice)).  At most G workers,
-// each slice at least kMinWorkerChunks long.
-__device__ __forceinline__ uint64_t slice_of(uint64_t total, int G) {
-  const uint64_t want = total / (uint64_t)kMinWorkerChunks;  // constant divisor
-  const uint64_t workers = max((uint64_t)1, min((uint64_t)G, want));
-  return max((uint64_t)1, udiv64(total + workers - 1, workers));
-}
-
-// Prefix of the chunk count over sequences into LDS (cum[0] = 0, cum[S] =
-// total) and a copy of the context lengths, computed by one wavefront: each
-// lane sums a contiguous run, then a scan.
-template <int TC>
-__device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int64_t *cum, int32_t *lens, int lane) {
-  const int S = a.S;
-  const int per = (S + 63) / 64;
-  const int s0 = min(S, lane * per);
-  const int s1 = min(S, s0 + per);
-  int64_t run = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int L = a.lens[s];
-    lens[s] = L;
-    run += (int64_t)a.H * row_chunks<TC>(L, a.maxb, a.B);
-  }
-  int64_t incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  int64_t x = incl - run;  // exclusive prefix of this lane's run
-  if (lane == 0) cum[0] = 0;
-  for (int s = s0; s < s1; ++s) {
-    x += (int64_t)a.H * row_chunks<TC>(lens[s], a.maxb, a.B);
-    cum[s + 1] = x;
-  }
-}
 
 // One chunk of the stream: chunk c of row (s, h), in the piece [cb, ce) of
 // that row the slice covers.  `valid` is false once the stream has ended;
@@ -837,7 +779,7 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) build_cost_prefix<TC>(a, cum, lens, lane);
+  if (wave == 0) build_cost_prefix<TC>(a, a.H, cum, lens, lane);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];

@@ -1,0 +1,565 @@
+// Paged attention for several query rows per KV head, on the matrix cores.
+//
+// Two cases share one kernel: grouped-query decode (G query heads read the
+// same KV head, the Llama-2-70B shape of the iaim.asia block-table article,
+// "末尾块的内部碎片") and multi-token queries (the last Q tokens of each
+// sequence attend causally over its paged context, as when several new
+// tokens are verified or prefilled in one step).  A KV head's row of the
+// batch is streamed once for all its M = G * Q query rows (M <= 16), so the
+// K/V bytes per query row drop by M, and the per-chunk products become small
+// real contractions:
+//   S^T (16 tokens x 16 rows) = K (16 x 128) * Q^T (128 x 16)  -- 4 x v_mfma_f32_16x16x32
+//   O^T (128 dims x 16 rows) += V^T (128 x 16 tokens) * P^T   -- 8 x v_mfma_f32_16x16x16
+// What is computed is the attention equation of "PagedAttention 完全拆解",
+// 背景, per query row, over the tokens its position may see.
+//
+// Register layouts (checked on the device):
+//  * K: lane l holds token l%16, dims 32j + 8(l/16) .. +8 of load j -- exactly
+//    the 16x16x32 A operand (row l%16, k-group l/16) for k-slice j.
+//  * Q: lane l holds query row l%16, the same dims -- the B operand of Q^T.
+//  * S^T result: lane l holds tokens 4(l/16) .. +4 of row l%16 -- the B
+//    operand P^T of the 16x16x16 product (k = tokens 4(l/16) .. +4).
+//  * V: lane l loads tokens 4(l/16) + t (t < 4), dims 8(l%16) .. +8; element
+//    s of those four rows is the A operand V^T for output dims 8r + s.
+//  * O^T result for slice s: lane l holds dims 8(4(l/16) + i) + s of row l%16,
+//    so a lane ends with four runs of 8 consecutive dims of its row.
+// Each row's online softmax (max, sum) lives in the four lanes holding it.
+// The work split, the pipeline (table entries two chunks ahead, K/V/Q one
+// chunk ahead, arithmetic on the current chunk) and the partial results /
+// merge follow the balanced decode kernel; rows are (sequence, KV head).
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+#include "pkv_split.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kGroupWaves = PKV_DECODE_WAVES;
+constexpr int GD = 128;  // head_dim of this path
+constexpr int GTC = 16;  // tokens per chunk
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+// S^T += K * Q^T for one 32-dim slice (operands as loaded: 8 elements a lane).
+template <int DT>
+__device__ __forceinline__ f4_t mfma_qk(const u32x4 &k, const u32x4 &q, f4_t c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k), __builtin_bit_cast(half8_t, q),
+                                                  c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, k), __builtin_bit_cast(bf8_t, q), c,
+                                                   0, 0, 0);
+}
+
+// f32 pair -> packed 16-bit pair of the element type, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)to16<DT>(a) | ((uint32_t)to16<DT>(b) << 16);
+}
+
+// O^T += V^T * P^T for one 16-dim slice; p holds 4 weights as two packed
+// 16-bit pairs (f16: one product; bf16: the weights are split into a bf16
+// high part and a bf16 remainder, two products, so the weights keep 16 bits).
+template <int DT>
+__device__ __forceinline__ f4_t mfma_pv(uint32_t v01, uint32_t v23, uint32_t p01, uint32_t p23, uint32_t r01,
+                                        uint32_t r23, f4_t c) {
+  const uint32_t va[2] = {v01, v23};
+  if constexpr (DT == DT_F16) {
+    const uint32_t pa[2] = {p01, p23};
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, va), __builtin_bit_cast(half4_t, pa), c,
+                                                 0, 0, 0);
+  } else {
+    const uint32_t pa[2] = {p01, p23};
+    const uint32_t ra[2] = {r01, r23};
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, va), __builtin_bit_cast(short4_t, pa),
+                                                  c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, va),
+                                                     __builtin_bit_cast(short4_t, ra), c, 0, 0, 0);
+  }
+}
+
+// One chunk of the stream: chunk c of row (s, kv head h), piece [cb, ce).
+struct GChunk {
+  int s, h, L, c, cb, ce;
+  bool valid;
+};
+
+template <int DT, int B>
+struct GroupStream {
+  static constexpr int NE = GTC >= B ? GTC / B : 1;  // table entries per chunk
+
+  struct Buf {
+    u32x4 k[4], v[4], q[4];
+    bool bad;
+  };
+
+  // constants of the call
+  const uint16_t *kp;
+  const uint16_t *vp;
+  const uint16_t *qp;
+  const int32_t *tables;
+  uint16_t *outp;
+  float *ws_m;
+  float *ws_l;
+  float *ws_o;
+  const int64_t *cum;
+  const int32_t *lens;
+  int64_t blk_stride, num_blocks;
+  int S, Hkv, H, maxb, nq, gq, M;
+  float scale_log2;
+  int lane, g, r;
+  int64_t worker;
+  // producer
+  uint64_t it_hi;
+  int cs_, ch_, cL, cn, cc, ccb, cce;
+  uint64_t cseg;
+  bool cvalid;
+  GChunk last;
+  // running state of the current piece (row r of this lane)
+  f4_t acc[8];
+  float m, lp;
+  bool bad;
+
+  __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_, int lane_) {
+    kp = reinterpret_cast<const uint16_t *>(a.k_pool);
+    vp = reinterpret_cast<const uint16_t *>(a.v_pool);
+    qp = reinterpret_cast<const uint16_t *>(a.q);
+    tables = a.tables;
+    outp = reinterpret_cast<uint16_t *>(a.out);
+    ws_m = a.ws_m;
+    ws_l = a.ws_l;
+    ws_o = a.ws_o;
+    cum = cum_;
+    lens = lens_;
+    blk_stride = (int64_t)a.Hkv * B * GD;
+    num_blocks = a.num_blocks;
+    S = a.S;
+    Hkv = a.Hkv;
+    H = a.H;
+    maxb = a.maxb;
+    nq = a.nq;
+    gq = a.H / a.Hkv;
+    M = gq * nq;
+    scale_log2 = a.scale_log2;
+    lane = lane_;
+    g = lane >> 4;
+    r = lane & 15;
+    cvalid = false;
+  }
+
+  __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
+  __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
+
+  // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
+  __device__ __forceinline__ int find_seq(uint64_t p) const {
+    int base = 0, span = S;
+    while (span > 1) {
+      const int step = (span + 63) >> 6;
+      const int idx = base + lane * step;
+      const bool ok = idx < base + span && (uint64_t)cum[idx] <= p;
+      const uint64_t mask = __ballot(ok);
+      const int j = __builtin_amdgcn_readfirstlane(__popcll(mask)) - 1;
+      base += j * step;
+      span = min(step, span - j * step);
+    }
+    return base;
+  }
+
+  __device__ __forceinline__ void enter(uint64_t lo, uint64_t hi) {
+    it_hi = hi;
+    const int s = find_seq(lo);
+    const uint64_t base = cum_at(s);
+    cs_ = s;
+    cL = len_at(s);
+    cn = (cL + GTC - 1) / GTC;
+    const uint64_t off = lo - base;  // < Hkv * cn
+    const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
+    ch_ = (int)h;
+    cseg = base + (uint64_t)h * cn;
+    ccb = (int)(lo - cseg);
+    cc = ccb;
+    cce = (int)min((uint64_t)cn, hi - cseg);
+    cvalid = true;
+  }
+
+  __device__ __forceinline__ void next_row() {
+    const uint64_t pos = cseg + cn;
+    if (pos >= it_hi) {
+      cvalid = false;
+      return;
+    }
+    if (ch_ + 1 < Hkv) {
+      ++ch_;
+    } else {
+      int s = cs_ + 1;
+      while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
+      cs_ = s;
+      ch_ = 0;
+      cL = len_at(s);
+      cn = (cL + GTC - 1) / GTC;
+    }
+    cseg = pos;
+    ccb = 0;
+    cc = 0;
+    cce = (int)min((uint64_t)cn, it_hi - cseg);
+  }
+
+  __device__ __forceinline__ GChunk produce() {
+    if (!cvalid) {
+      GChunk none = last;
+      none.valid = false;
+      return none;
+    }
+    GChunk ch;
+    ch.s = cs_;
+    ch.h = ch_;
+    ch.L = cL;
+    ch.c = cc;
+    ch.cb = ccb;
+    ch.ce = cce;
+    ch.valid = true;
+    last = ch;
+    if (cc + 1 < cce) ++cc;
+    else next_row();
+    return ch;
+  }
+
+  __device__ __forceinline__ static int first_block(int c) { return GTC >= B ? c * (GTC / B) : c / (B / GTC); }
+  __device__ __forceinline__ static int last_block(const GChunk &d) { return (min(d.L, d.ce * GTC) - 1) / B; }
+
+  // Stage 1: this lane's table entry of chunk d (clamped to the piece's last
+  // block; tokens past it are masked).
+  __device__ __forceinline__ uint32_t load_entries(const GChunk &d) const {
+    const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
+    return (uint32_t)tables[(int64_t)d.s * maxb + lb];
+  }
+
+  // Base element offset of token t of chunk d (its block from the entries).
+  __device__ __forceinline__ int64_t token_base(const GChunk &d, uint32_t e, int t, bool &bd) const {
+    int blk, off;
+    if constexpr (GTC >= B) {
+      const int b0 = __builtin_amdgcn_readlane((int)e, 0);
+      const int b1 = __builtin_amdgcn_readlane((int)e, NE - 1);
+      blk = (t / B == 0) ? b0 : b1;  // NE <= 2 for the block sizes served (8, 16)
+      off = t % B;
+    } else {
+      blk = __builtin_amdgcn_readlane((int)e, 0);
+      off = (d.c % (B / GTC)) * GTC + t;
+    }
+    if (blk < 0 || (int64_t)blk >= num_blocks) {
+      bd = true;
+      blk = 0;
+    }
+    return (int64_t)blk * blk_stride + (int64_t)d.h * B * GD + (int64_t)off * GD;
+  }
+
+  // Stage 2: K rows (token r), V rows (tokens 4g .. 4g+3) and the query rows
+  // of chunk d; the same loads for every chunk.
+  __device__ __forceinline__ void load_kv(const GChunk &d, uint32_t e, Buf &b) const {
+    bool bd = false;
+    const int64_t kb = token_base(d, e, r, bd) + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.k[j] = *reinterpret_cast<const u32x4 *>(kp + kb + 32 * j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t vb = token_base(d, e, 4 * g + t, bd) + 8 * r;
+      b.v[t] = *reinterpret_cast<const u32x4 *>(vp + vb);
+    }
+    b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
+    // query row r of this KV head (rows >= M read row 0 and are zeroed)
+    const int rr = r < M ? r : 0;
+    const int qi = rr / gq, gi = rr - (rr / gq) * gq;
+    const int64_t qb = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qb + 32 * j);
+  }
+
+  // Stage 3: scores, online softmax and the weighted V sum of chunk d.
+  __device__ __forceinline__ void consume(const GChunk &d, Buf &b) {
+    if (d.c == d.cb) {
+      m = kNegInf;
+      lp = 0.f;
+#pragma unroll
+      for (int s_ = 0; s_ < 8; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
+      bad = false;
+    }
+    bad = bad || b.bad;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    f4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st = mfma_qk<DT>(b.k[j], r < M ? b.q[j] : zero, st);
+    // row r sees tokens [t_lo, min(t_hi, its causal limit))
+    const int t_lo = d.cb * GTC;
+    const int t_hi = min(d.L, d.ce * GTC);
+    const int lim = r < M ? d.L - nq + 1 + r / gq : 0;
+    const int t_row = min(t_hi, lim);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = d.c * GTC + 4 * g + i;
+      sc[i] = (tok >= t_lo && tok < t_row) ? st[i] * scale_log2 : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
+    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mref);  // -inf gives 0
+    lp = lp * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    m = mnew;
+    uint32_t p01, p23, r01 = 0, r23 = 0;
+    if constexpr (DT == DT_F16) {
+      p01 = pack2<DT>(p[0], p[1]);
+      p23 = pack2<DT>(p[2], p[3]);
+    } else {
+      p01 = pack2<DT>(p[0], p[1]);
+      p23 = pack2<DT>(p[2], p[3]);
+      r01 = pack2<DT>(p[0] - lo16<DT>(p01), p[1] - hi16<DT>(p01));
+      r23 = pack2<DT>(p[2] - lo16<DT>(p23), p[3] - hi16<DT>(p23));
+    }
+    // V rows of tokens outside [t_lo, t_hi) are zeroed (unused slots may hold NaN)
+    u32x4 v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = d.c * GTC + 4 * g + t;
+      v[t] = (tok >= t_lo && tok < t_hi) ? b.v[t] : zero;
+    }
+#pragma unroll
+    for (int s_ = 0; s_ < 8; ++s_) {
+      acc[s_] *= alpha;
+      // element s_ of the four V rows: dword s_/2, low or high half
+      const uint32_t sel = (s_ & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t v01 = __builtin_amdgcn_perm(v[1][s_ >> 1], v[0][s_ >> 1], sel);
+      const uint32_t v23 = __builtin_amdgcn_perm(v[3][s_ >> 1], v[2][s_ >> 1], sel);
+      acc[s_] = mfma_pv<DT>(v01, v23, p01, p23, r01, r23, acc[s_]);
+    }
+    if (d.c == d.ce - 1) finish_piece(d);
+  }
+
+  __device__ __forceinline__ void finish_piece(const GChunk &d) {
+    lp += __shfl_xor(lp, 16);
+    lp += __shfl_xor(lp, 32);
+    if (r >= M) return;
+    const int qi = r / gq, gi = r - (r / gq) * gq;
+    const float nanv = bad ? __builtin_nanf("") : 0.f;
+    if (d.cb == 0 && d.ce * GTC >= d.L) {
+      // the whole row: final output, four runs of 8 dims per lane
+      uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
+      const float inv = 1.f / lp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 w;
+        w.x = pack2<DT>(acc[0][i] * inv + nanv, acc[1][i] * inv + nanv);
+        w.y = pack2<DT>(acc[2][i] * inv + nanv, acc[3][i] * inv + nanv);
+        w.z = pack2<DT>(acc[4][i] * inv + nanv, acc[5][i] * inv + nanv);
+        w.w = pack2<DT>(acc[6][i] * inv + nanv, acc[7][i] * inv + nanv);
+        *reinterpret_cast<u32x4 *>(o + 8 * (4 * g + i)) = w;
+      }
+    } else {
+      const int64_t u = (worker + (int64_t)d.s * Hkv + d.h) * M + r;
+      float *o = ws_o + u * GD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int s_ = 0; s_ < 8; ++s_) o[8 * (4 * g + i) + s_] = acc[s_][i] + nanv;
+      }
+      if (g == 0) {
+        ws_m[u] = m * kLn2 + nanv;  // natural-log units
+        ws_l[u] = lp + nanv;
+      }
+    }
+  }
+
+  // The stream, as in the balanced decode kernel (stage 1 of chunk n + 2,
+  // stage 2 of chunk n + 1, stage 3 of chunk n; the same loads every step).
+  __device__ __forceinline__ void run(int th1, int th2, int th3) {
+    GChunk d0 = produce();
+    if (!d0.valid) return;
+    int done = 0;
+    Buf ba, bb;
+    uint32_t ea = load_entries(d0);
+    GChunk d1 = produce();
+    uint32_t eb = load_entries(d1);
+    load_kv(d0, ea, ba);
+    for (;;) {
+      const GChunk d2 = produce();
+      ea = load_entries(d2);
+      load_kv(d1, eb, bb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d0, ba);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d1.valid) break;
+      const GChunk d3 = produce();
+      eb = load_entries(d3);
+      load_kv(d2, ea, ba);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d1, bb);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d2.valid) break;
+      d0 = d2;
+      d1 = d3;
+    }
+  }
+};
+
+template <int DT, int B, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
+  using ST = GroupStream<DT, B>;
+  extern __shared__ int64_t lds[];
+  int64_t *cum = lds;                                         // [S + 1]
+  int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) build_cost_prefix<GTC>(a, a.Hkv, cum, lens, lane, a.nq);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
+  }
+  const uint64_t total = uni64((uint64_t)cum[a.S]);
+  if (total == 0) return;
+  const uint64_t slice = slice_of(total, a.G);
+  const int w = blockIdx.x * NW + wave;
+  const uint64_t lo = min(total, (uint64_t)w * slice);
+  const uint64_t hi = min(total, lo + slice);
+  if (lo >= hi) return;
+
+  ST st;
+  st.init(a, cum, lens, lane);
+  st.worker = w;
+  st.enter(lo, hi);
+  const int n = (int)(hi - lo);
+  __builtin_amdgcn_s_setprio(3);
+  st.run(n / 4, n / 2, (3 * n) / 4);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One wavefront per (sequence, KV head, query row): rows of empty or invalid
+// contexts, and the LSE merge of rows cut over several workers.
+template <int DT>
+__global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
+  const int lane = threadIdx.x & 63;
+  const int gq = a.H / a.Hkv;
+  const int M = gq * a.nq;
+  const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (s * Hkv + h) * M + row
+  if (id >= (int64_t)a.S * a.Hkv * M) return;
+  const int64_t grow = id / M;
+  const int rr = (int)(id - grow * M);
+  const int s = (int)(grow / a.Hkv);
+  const int h = (int)(grow - (int64_t)s * a.Hkv);
+  const int qi = rr / gq, gi = rr - (rr / gq) * gq;
+  const int L = a.lens[s];
+  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + (((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi) * GD;
+  if (L <= 0 || L > a.maxb * a.B || L < a.nq) {
+    const uint16_t v = (L == 0) ? uint16_t(0) : to16<DT>(__builtin_nanf(""));
+    for (int d = lane; d < GD; d += 64) out_row[d] = v;
+    return;
+  }
+  const int nch = (L + GTC - 1) / GTC;
+  const uint64_t seg = (uint64_t)a.ws_cum[s] + (uint64_t)h * nch;
+  const uint64_t end = seg + nch;
+  const uint64_t slice = slice_of((uint64_t)a.ws_cum[a.S], a.G);
+  const int64_t t_a = (int64_t)udiv64(seg, slice);
+  const int64_t n = (int64_t)udiv64(end - 1, slice) - t_a + 1;
+  if (n <= 1) return;  // one piece: it wrote the row
+  auto slot = [&](int64_t j) { return (t_a + j + grow) * M + rr; };
+  float M_ = kNegInf;
+  for (int64_t j0 = 0; j0 < n; j0 += 64) {
+    const int64_t j = j0 + lane;
+    if (j < n) M_ = fmaxf(M_, a.ws_m[slot(j)]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M_ = fmaxf(M_, __shfl_xor(M_, off));
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int64_t j0 = 0; j0 < n; j0 += 64) {
+    const int64_t j = j0 + lane;
+    float f = 0.f, lw = 0.f;
+    if (j < n) {
+      const float mj = a.ws_m[slot(j)];
+      f = (mj == kNegInf) ? 0.f : fast_exp2((mj - M_) * kLog2e);
+      lw = a.ws_l[slot(j)];
+    }
+    const int cnt = (int)min((int64_t)64, n - j0);
+    for (int q = 0; q < cnt; ++q) {  // pieces in worker order
+      const float fq = __shfl(f, q);
+      const int64_t u = slot(j0 + q);
+      lsum += fq * __shfl(lw, q);
+      o0 += fq * a.ws_o[u * GD + lane];
+      o1 += fq * a.ws_o[u * GD + lane + 64];
+    }
+  }
+  out_row[lane] = to16<DT>(o0 / lsum);
+  out_row[lane + 64] = to16<DT>(o1 / lsum);
+}
+
+template <int DT, int B>
+hipError_t launch_group(const DecodeParams &a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves>), dim3(a.G / kGroupWaves), dim3(kGroupWaves * 64),
+                     group_lds_bytes(a.S), st, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+const void *group_ptr(int B) {
+  switch (B) {
+    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves>);
+    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves>);
+    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves>);
+    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves>);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+size_t group_lds_bytes(int num_seqs) {
+  return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
+}
+
+const void *group_kernel(int dtype, int block_size) {
+  return dtype == DT_F16 ? group_ptr<DT_F16>(block_size) : group_ptr<DT_BF16>(block_size);
+}
+
+hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream) {
+  if (a.S == 0 || a.G == 0) return hipSuccess;
+#define PKV_G(DT)                                   \
+  switch (a.B) {                                    \
+    case 8: return launch_group<DT, 8>(a, stream);   \
+    case 16: return launch_group<DT, 16>(a, stream); \
+    case 32: return launch_group<DT, 32>(a, stream); \
+    case 64: return launch_group<DT, 64>(a, stream); \
+    default: return hipErrorInvalidValue;           \
+  }
+  if (a.dtype == DT_F16) { PKV_G(DT_F16) }
+  PKV_G(DT_BF16)
+#undef PKV_G
+}
+
+hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream) {
+  if (a.S == 0) return hipSuccess;
+  const int64_t rows = (int64_t)a.S * a.Hkv * (a.H / a.Hkv) * a.nq;
+  const int grid = (int)((rows + 3) / 4);
+  if (a.dtype == DT_F16)
+    hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

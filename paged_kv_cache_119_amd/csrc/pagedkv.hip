@@ -77,17 +77,19 @@ int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
 
 // Workers (wavefronts) the balanced split launches on the current device: as
 // many as the device holds at once.  0 if the device cannot be queried.
-int balanced_waves(const pkv_pool *p, int32_t num_seqs) {
+int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
   // the fused-append instance (the larger of the two), so that the split and
   // merge passes of either entry point agree on the worker count
-  const void *k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
+  const void *k = group ? pkv::group_kernel(p->dtype, p->block_size)
+                        : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
   if (!k) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
-  const size_t lds = align_up(pkv::balanced_lds_bytes(num_seqs), 4096);
+  const size_t lds =
+      align_up(group ? pkv::group_lds_bytes(num_seqs) : pkv::balanced_lds_bytes(num_seqs), 4096);
   const int nb = kernel_blocks_per_cu(dev, k, lds);
   if (nb <= 0) return 0;
   long long g = (long long)cus * nb * pkv::decode_waves();
@@ -97,22 +99,45 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs) {
 
 struct Layout {
   bool balanced;
+  bool group;  // several query rows per KV head (matrix-core kernel)
   int32_t P, MP;
   int64_t units;
   size_t off_m, off_l, off_o, off_cum, bytes;
 };
 
 pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks,
-                         const pkv_pool *p, int32_t partition_size, Layout *lay) {
+                         const pkv_pool *p, int32_t partition_size, int32_t num_queries, Layout *lay) {
   if (!p) return PKV_ERR_NULL;
   if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
+  if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || num_queries < 1) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks * p->block_size > (1 << 30)) return PKV_ERR_SHAPE;
-  if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
+  if (num_heads % p->num_kv_heads != 0) return PKV_ERR_UNSUPPORTED;
   if (partition_size < 0) return PKV_ERR_UNSUPPORTED;
   const int64_t ctx = (int64_t)max_blocks * p->block_size;
   const int unit = partition_unit(p);
   *lay = Layout{};
+  const int32_t rows = (num_heads / p->num_kv_heads) * num_queries;  // query rows per KV head
+  if (rows > 1) {
+    // several query rows per KV head: the matrix-core kernel, balanced split only
+    if (rows > 16 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
+      return PKV_ERR_UNSUPPORTED;
+    const int64_t row_chunks = (ctx + 15) / 16;
+    const int64_t most = (int64_t)num_seqs * p->num_kv_heads * row_chunks;
+    if ((double)most >= 1.0e12) return PKV_ERR_SHAPE;
+    lay->balanced = true;
+    lay->group = true;
+    const int64_t workers = (most + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
+    const int64_t units = (workers + (int64_t)num_seqs * p->num_kv_heads) * rows;
+    lay->units = units;
+    const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
+    const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
+    lay->off_cum = 0;
+    lay->off_m = cum;
+    lay->off_l = cum + sec;
+    lay->off_o = cum + 2 * sec;
+    lay->bytes = cum + 2 * sec + align_up((size_t)units * p->head_dim * sizeof(float), kAlign);
+    return PKV_OK;
+  }
   if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
     // work-balanced split; the cost space (chunks) must stay far below 2^47
     const int tc = pkv::decode_chunk_tokens(p->head_dim);
@@ -158,27 +183,24 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
                        const int32_t *block_tables, const int32_t *context_lens, float scale,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
                        int32_t partition_size, const void *workspace, size_t workspace_bytes,
-                       bool need_inputs, pkv::DecodeParams *a) {
+                       bool need_inputs, pkv::DecodeParams *a, int32_t num_queries = 1) {
   if (num_seqs == 0) {  // nothing to do; still validate the static arguments
-    if (!p) return PKV_ERR_NULL;
-    if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
-    if (num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
-    if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
+    Layout lay;
+    const pkv_status st = decode_layout(0, num_heads, max_blocks, p, partition_size, num_queries, &lay);
     *a = pkv::DecodeParams{};
-    return PKV_OK;
+    return st;
   }
   if (num_seqs < 0) return PKV_ERR_SHAPE;
   if (!p) return PKV_ERR_NULL;
   if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
   if (num_heads < 1 || max_blocks < 1) return PKV_ERR_SHAPE;
-  if (num_heads != p->num_kv_heads) return PKV_ERR_UNSUPPORTED;
   if (!out || !context_lens) return PKV_ERR_NULL;
   if (need_inputs && (!q || !k_pool || !v_pool || !block_tables)) return PKV_ERR_NULL;
   if (need_inputs && (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16)))
     return PKV_ERR_SHAPE;
   if (!aligned(out, 16)) return PKV_ERR_SHAPE;
   Layout lay;
-  const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, &lay);
+  const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, num_queries, &lay);
   if (st != PKV_OK) return st;
   if (lay.bytes > 0) {
     if (!workspace || workspace_bytes < lay.bytes || !aligned(workspace, kAlign))
@@ -199,9 +221,11 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
     a->ws_cum = lay.balanced ? (int64_t *)(ws + lay.off_cum) : nullptr;
   }
   if (lay.balanced) {
-    a->G = balanced_waves(p, num_seqs);
+    a->G = balanced_waves(p, num_seqs, lay.group);
     if (a->G == 0) return PKV_ERR_HIP;
   }
+  a->nq = num_queries;
+  a->group = lay.group ? 1 : 0;
   a->scale_log2 = scale * 1.4426950408889634f;
   a->num_blocks = p->num_blocks;
   a->S = num_seqs;
@@ -220,6 +244,14 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+hipError_t launch_split(const pkv::DecodeParams &a, hipStream_t stream) {
+  return a.group ? pkv::launch_group_decode(a, stream) : pkv::launch_decode_partitions(a, stream);
+}
+
+hipError_t launch_merge(const pkv::DecodeParams &a, hipStream_t stream) {
+  return a.group ? pkv::launch_group_merge(a, stream) : pkv::launch_decode_merge(a, stream);
+}
+
 // Validation and parameters shared by the two fused-append entry points.
 pkv_status fill_append(void *out, const void *q, const void *k_new, const void *v_new,
                        int64_t new_token_stride, void *k_pool, void *v_pool,
@@ -231,6 +263,7 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, a);
   if (st != PKV_OK || num_seqs == 0) return st;
+  if (a->group) return PKV_ERR_UNSUPPORTED;  // one query row per KV head only
   if (!k_new || !v_new) return PKV_ERR_NULL;
   const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
   if (new_token_stride == 0) new_token_stride = row;
@@ -334,7 +367,7 @@ pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pair
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                   const pkv_pool *p, int32_t partition_size) {
   Layout lay;
-  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, &lay) != PKV_OK)
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, 1, &lay) != PKV_OK)
     return -1;
   return lay.balanced ? 0 : lay.P;
 }
@@ -342,7 +375,7 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_heads, int32_t m
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                                   const pkv_pool *p, int32_t partition_size) {
   Layout lay;
-  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, &lay) != PKV_OK)
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, 1, &lay) != PKV_OK)
     return 0;
   return lay.bytes;
 }
@@ -358,7 +391,7 @@ pkv_status pkv_decode_partitions(void *out, const void *q, const void *k_pool, c
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, &a);
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
+  return hip_status(launch_split(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_seqs,
@@ -370,7 +403,7 @@ pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, false, &a);
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_decode_merge(a, (hipStream_t)stream));
+  return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const void *k_new,
@@ -388,9 +421,9 @@ pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const voi
                                     max_blocks_per_seq, p, partition_size, workspace,
                                     workspace_bytes, &a);
   if (st != PKV_OK) return st;
-  const pkv_status s1 = hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
-  return hip_status(pkv::launch_decode_merge(a, (hipStream_t)stream));
+  return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_decode_partitions_append(void *out, const void *q, const void *k_new,
@@ -406,7 +439,7 @@ pkv_status pkv_decode_partitions_append(void *out, const void *q, const void *k_
                                     max_blocks_per_seq, p, partition_size, workspace,
                                     workspace_bytes, &a);
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
+  return hip_status(launch_split(a, (hipStream_t)stream));
 }
 
 pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_pool,
@@ -420,9 +453,31 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, &a);
   if (st != PKV_OK) return st;
-  const pkv_status s1 = hip_status(pkv::launch_decode_partitions(a, (hipStream_t)stream));
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
-  return hip_status(pkv::launch_decode_merge(a, (hipStream_t)stream));
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                 int32_t max_blocks_per_seq, const pkv_pool *p) {
+  Layout lay;
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, 0, num_queries, &lay) != PKV_OK) return 0;
+  return lay.bytes;
+}
+
+pkv_status pkv_paged_attention_multi(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                     int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale, num_seqs,
+                                    num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, true, &a,
+                                    num_queries);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -54,6 +54,11 @@ struct DecodeParams {
   const void *k_new;
   const void *v_new;
   int64_t new_stride;
+  // Query rows per KV head: H / Hkv query heads times nq query tokens per
+  // sequence (q and out are [S][nq][H][D]); group != 0 selects the
+  // matrix-core kernel for more than one row.
+  int32_t nq;
+  int32_t group;
 };
 
 int decode_waves();
@@ -65,6 +70,11 @@ size_t balanced_lds_bytes(int num_seqs);
 const void *balanced_kernel(int dtype, int head_dim, int block_size, int append);
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
+// Several query rows per KV head (grouped-query heads, multi-token queries).
+size_t group_lds_bytes(int num_seqs);
+const void *group_kernel(int dtype, int block_size);
+hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream);
+hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, const void *v,

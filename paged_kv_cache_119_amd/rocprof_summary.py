@@ -23,7 +23,7 @@ import os
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("paged_kv_cache_119_amd/csrc/decode.hip", "paged_kv_cache_119_amd/csrc/pkv_device.h",
-                  "paged_kv_cache_119_amd/csrc/pkv_launch.h")
+                  "paged_kv_cache_119_amd/csrc/pkv_launch.h", "paged_kv_cache_119_amd/csrc/pkv_split.h")
 COPY_BYTES_KIB = (1 << 30) / 1024.0
 
 

@@ -71,7 +71,10 @@ def test_partition_size_rules(lib):
     assert f(8, 4, 128, ctypes.byref(_desc(B=64)), 32) == -1       # not a multiple of B
     assert f(8, 4, 128, ctypes.byref(_desc(D=64)), 48) == -1       # D = 64 steps are 32 tokens
     assert f(8, 4, 128, ctypes.byref(_desc(B=8)), 8192) == -1      # P / B > 512
-    assert f(8, 5, 128, ctypes.byref(d), 256) == -1                # heads != kv heads
+    assert f(8, 5, 128, ctypes.byref(d), 256) == -1                # heads not a multiple of kv heads
+    assert f(8, 8, 128, ctypes.byref(d), 0) == 0                   # 2 query heads per kv head: balanced
+    assert f(8, 8, 128, ctypes.byref(d), 256) == -1                # ... and never fixed partitions
+    assert f(8, 68, 128, ctypes.byref(d), 0) == -1                 # 17 query heads per kv head
     assert f(8, 4, 128, ctypes.byref(d), -16) == -1
     # more than 4096 sequences: the balanced split falls back to fixed 512
     assert f(5000, 4, 128, ctypes.byref(d), 0) == 512
@@ -100,9 +103,16 @@ def test_validation_returns_status_before_any_launch(lib):
     st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, -1, 4, 8, ctypes.byref(d), 0,
                                         nul, 0, nul)
     assert st == 2                                                  # PKV_ERR_SHAPE
-    st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 8, 8, ctypes.byref(d), 0,
+    p16 = ctypes.c_void_p(1 << 20)  # never dereferenced: these calls fail validation
+    st = lib.pkv_paged_attention_decode(p16, p16, p16, p16, p16, p16, 1.0, 4, 6, 8, ctypes.byref(d), 0,
                                         nul, 0, nul)
-    assert st == 3                                                  # GQA not supported yet
+    assert st == 3                                                  # 6 query heads over 4 KV heads
+    st = lib.pkv_paged_attention_decode(p16, p16, p16, p16, p16, p16, 1.0, 4, 8, 8, ctypes.byref(d), 64,
+                                        nul, 0, nul)
+    assert st == 3                                                  # grouped rows: balanced split only
+    st = lib.pkv_paged_attention_decode(p16, p16, p16, p16, p16, p16, 1.0, 4, 8, 8, ctypes.byref(_desc(D=64)),
+                                        0, nul, 0, nul)
+    assert st == 3                                                  # grouped rows: head_dim 128 only
     bad = _desc(B=12)
     st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, ctypes.byref(bad), 0,
                                         nul, 0, nul)

@@ -1,0 +1,162 @@
+"""GPU: several query rows per KV head (grouped-query decode, multi-token
+queries) on the matrix-core kernel, against the float64 oracle."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_119_amd as pkv  # noqa: E402
+from oracle import paged_oracle as po  # noqa: E402
+from synth import nan_bits, normal_16bit, to_bits  # noqa: E402
+
+from .gpu_util import DEV, assert_close, log  # noqa: E402
+
+D = 128
+
+
+def _case(lengths, Hkv, B, dtype, seed, slack=3, poison=True):
+    """Pools [N, Hkv, B, D] with random values, a random block placement for
+    the given context lengths, and the unused slots (free blocks, tails of last
+    blocks) set to the NaN pattern."""
+    rng = np.random.default_rng(seed)
+    nb = [-(-L // B) for L in lengths]
+    N = sum(nb) + slack
+    perm = rng.permutation(N)
+    maxb = max(max(nb), 1)
+    tables = np.full((len(lengths), maxb), -1, np.int32)
+    live = np.zeros((N, B), bool)
+    c = 0
+    for s, L in enumerate(lengths):
+        tables[s, :nb[s]] = perm[c:c + nb[s]]
+        for j in range(L):
+            live[perm[c + j // B], j % B] = True
+        c += nb[s]
+    kp = normal_16bit((N, Hkv, B, D), dtype, DEV, seed * 4 + 1)
+    vp = normal_16bit((N, Hkv, B, D), dtype, DEV, seed * 4 + 2)
+    if poison:
+        dead = torch.from_numpy(~live).to(DEV)[:, None, :, None].expand(kp.shape)
+        nb_ = nan_bits(dtype)
+        for pool in (kp, vp):
+            pool.view(torch.int16).masked_fill_(dead, nb_ - 0x10000 if nb_ >= 0x8000 else nb_)
+    return dict(kp=kp, vp=vp, tables=tables, lens=np.asarray(lengths, np.int32), B=B)
+
+
+def _run(c, q, scale):
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    if q.dim() == 3:
+        return pkv.paged_attention_decode(q, c["kp"], c["vp"], tab, lens, scale)
+    return pkv.paged_attention_multi(q, c["kp"], c["vp"], tab, lens, scale)
+
+
+def _oracle(c, q, scale, dtype):
+    qb = to_bits(q)
+    if qb.ndim == 3:
+        qb = qb[:, None]
+    ref = po.decode_rows(qb, to_bits(c["kp"]), to_bits(c["vp"]), c["tables"], c["lens"], scale, c["B"], dtype)
+    return ref[:, 0] if q.dim() == 3 else ref
+
+
+LENGTHS = [1, 15, 16, 17, 31, 33, 64, 100, 255, 256, 257, 511, 700, 1025, 40, 3]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+@pytest.mark.parametrize("G,Q", [(8, 1), (4, 1), (16, 1), (1, 4), (2, 4), (1, 16), (3, 2)])
+def test_rows_per_kv_head_small_shapes(dtype, B, G, Q):
+    Hkv = 2
+    lengths = [max(L, Q) for L in LENGTHS]
+    c = _case(lengths, Hkv, B, dtype, seed=1000 + 10 * B + G + 100 * Q)
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 77 + G + Q)
+    out = _run(c, q, D ** -0.5)
+    torch.cuda.synchronize()
+    ref = _oracle(c, q, D ** -0.5, dtype)
+    assert_close(to_bits(out), ref, dtype, f"rows G={G} Q={Q} {dtype} B={B}")
+
+
+def test_grouped_query_llama70b_shape_sampled():
+    """64 sequences, 64 query heads over 8 KV heads (groups of 8), bf16, B=16,
+    lognormal context lengths (median 300, up to 2048); sampled sequences
+    against the oracle."""
+    log("gqa llama-70b shape: 64 seqs, 64 q heads / 8 kv heads, bf16")
+    rng = np.random.default_rng(51)
+    lengths = [int(x) for x in np.clip(np.rint(np.exp(rng.normal(np.log(300), 1.0, 64))), 1, 2048)]
+    c = _case(lengths, 8, 16, "bf16", seed=51)
+    q = normal_16bit((64, 64, D), "bf16", DEV, 52)
+    out = _run(c, q, D ** -0.5)
+    torch.cuda.synchronize()
+    pick = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), *[int(x) for x in rng.integers(0, 64, 6)]})
+    sub = dict(c)
+    sub["tables"] = c["tables"][pick]
+    sub["lens"] = c["lens"][pick]
+    ref = _oracle(sub, q[pick], D ** -0.5, "bf16")
+    assert_close(to_bits(out)[pick], ref, "bf16", f"gqa 64/8 ({len(pick)} sequences)")
+
+
+def test_rows_edge_cases_empty_short_and_bad_entries():
+    """L == 0 gives zeros; L < Q (queries not in the context) and a table
+    entry outside the pool give NaN rows; the other rows are unaffected; NaN
+    in unused slots never leaks."""
+    log("rows: edge cases")
+    Q, Hkv, G = 4, 2, 2
+    lengths = [0, 2, 37, 80, 5]
+    c = _case([max(L, 1) for L in lengths], Hkv, 16, "f16", seed=61)
+    c["lens"] = np.asarray(lengths, np.int32)
+    c["tables"][3, 2] = 10 ** 6  # sequence 3 reads a block outside the pool
+    q = normal_16bit((len(lengths), Q, Hkv * G, D), "f16", DEV, 62)
+    out = po.bits_to_f64(to_bits(_run(c, q, D ** -0.5)), "f16")
+    assert np.all(out[0] == 0)
+    assert np.all(np.isnan(out[1]))
+    assert np.all(np.isnan(out[3]))
+    good = [2, 4]
+    sub = dict(c)
+    sub["tables"] = c["tables"][good]
+    sub["lens"] = c["lens"][good]
+    ref = _oracle(sub, q[good], D ** -0.5, "f16")
+    assert np.all(np.isfinite(out[good]))
+    assert_close(to_bits(_run(c, q, D ** -0.5))[good], ref, "f16", "rows edge: valid sequences")
+
+
+def test_rows_placement_and_run_to_run_bitwise():
+    """The result depends only on logical positions: a permuted placement of
+    the blocks and a repeated call give identical bits."""
+    log("rows: placement invariance")
+    lengths = [300, 17, 1000, 64]
+    a = _case(lengths, 2, 16, "f16", seed=71)
+    q = normal_16bit((len(lengths), 2, 8, D), "f16", DEV, 72)
+    o1 = _run(a, q, 0.09)
+    o2 = _run(a, q, 0.09)
+    # the same logical K/V at other physical blocks
+    rng = np.random.default_rng(73)
+    N = a["kp"].shape[0]
+    perm = rng.permutation(N)
+    inv = np.argsort(perm)
+    b = dict(a)
+    b["kp"] = a["kp"][torch.from_numpy(inv).to(DEV)].contiguous()
+    b["vp"] = a["vp"][torch.from_numpy(inv).to(DEV)].contiguous()
+    b["tables"] = np.where(a["tables"] >= 0, perm[np.maximum(a["tables"], 0)], -1).astype(np.int32)
+    o3 = _run(b, q, 0.09)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_rows_unsupported_shapes_are_rejected():
+    c = _case([20, 30], 2, 16, "f16", seed=81)
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    q = normal_16bit((2, 34, D), "f16", DEV, 82)  # 17 query heads per KV head
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_decode(q, c["kp"], c["vp"], tab, lens, 0.1)
+    q = normal_16bit((2, 4, D), "f16", DEV, 83)
+    with pytest.raises(pkv.PagedKVError):  # fixed partitions are not served for grouped rows
+        pkv.paged_attention_decode(q, c["kp"], c["vp"], tab, lens, 0.1, partition_size=64)
+    kn = normal_16bit((2, 2, D), "f16", DEV, 84)
+    with pytest.raises(pkv.PagedKVError):  # the fused append needs one row per KV head
+        pkv.paged_attention_decode_append(q, kn, kn, c["kp"], c["vp"], tab, lens, 0.1)
+    q = normal_16bit((2, 2, 3, D), "f16", DEV, 85)
+    with pytest.raises(pkv.PagedKVError):  # 3 query heads over 2 KV heads
+        pkv.paged_attention_multi(q, c["kp"], c["vp"], tab, lens, 0.1)

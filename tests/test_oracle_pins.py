@@ -432,6 +432,68 @@ def test_copy_blocks_exact_and_skips_invalid_pairs():
     assert np.array_equal(kp[0], kp0[0])
 
 
+# ---------------------------------------------------------------------------
+# grouped-query heads and multi-token queries
+# ---------------------------------------------------------------------------
+
+def _gqa_pools(rng, S, L_max, Hkv, D, B, dtype):
+    lengths = [int(x) for x in rng.integers(1, L_max, size=S)]
+    c = _paged_case(lengths, Hkv, D, B, dtype, rng)
+    return c, lengths
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_grouped_query_equals_mha_over_repeated_kv_heads(G):
+    """Query head h of a group reads KV head h // G: the same result as plain
+    multi-head decode over a pool in which every KV head is repeated G times."""
+    rng = np.random.default_rng(40 + G)
+    Hkv, D, B = 2, 8, 4
+    c, lengths = _gqa_pools(rng, 5, 40, Hkv, D, B, "f16")
+    q = _bits(rng.standard_normal((5, 1, Hkv * G, D)), "f16")
+    got = po.decode_rows(q, c["kp"], c["vp"], c["tables"], c["lens"], 0.3, B, "f16")[:, 0]
+    kr = np.repeat(c["kp"], G, axis=1)
+    vr = np.repeat(c["vp"], G, axis=1)
+    ref = po.decode(q[:, 0], kr, vr, c["tables"], c["lens"], 0.3, B, "f16")
+    assert np.array_equal(got, ref)
+    # planted mistake: heads interleaved over KV heads instead of grouped
+    bad = po.decode(q[:, 0], np.tile(c["kp"], (1, G, 1, 1)), np.tile(c["vp"], (1, G, 1, 1)), c["tables"],
+                    c["lens"], 0.3, B, "f16")
+    assert not np.allclose(bad, ref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multi_token_queries_match_dense_causal_brute_force(dtype):
+    """The last Q tokens of a sequence, attending causally, equal the last Q
+    rows of dense causal attention over the unpaged sequence."""
+    rng = np.random.default_rng(44)
+    H, D, B, Q = 2, 8, 4, 5
+    lengths = [5, 9, 23]
+    c = _paged_case(lengths, H, D, B, dtype, rng)
+    qb = _bits(rng.standard_normal((len(lengths), Q, H, D)), dtype)
+    got = po.decode_rows(qb, c["kp"], c["vp"], c["tables"], c["lens"], 0.35, B, dtype)
+    s64 = float(np.float32(0.35))
+    for s, L in enumerate(lengths):
+        for h in range(H):
+            Qfull = np.zeros((L, D))
+            Qfull[L - Q:] = po.bits_to_f64(qb[s, :, h], dtype)
+            ref = po.dense_causal(Qfull, po.bits_to_f64(c["kl"][s][:, h], dtype),
+                                  po.bits_to_f64(c["vl"][s][:, h], dtype), s64)[L - Q:]
+            assert np.allclose(got[s, :, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_token_query_i_equals_decode_over_its_prefix():
+    rng = np.random.default_rng(45)
+    H, D, B, Q = 3, 8, 4, 4
+    lengths = [4, 11, 30]
+    c = _paged_case(lengths, H, D, B, "f16", rng)
+    qb = _bits(rng.standard_normal((len(lengths), Q, H, D)), "f16")
+    got = po.decode_rows(qb, c["kp"], c["vp"], c["tables"], c["lens"], 0.35, B, "f16")
+    for i in range(Q):
+        lens_i = c["lens"] - Q + 1 + i
+        ref = po.decode(qb[:, i], c["kp"], c["vp"], c["tables"], lens_i, 0.35, B, "f16")
+        assert np.array_equal(got[:, i], ref)
+
+
 def test_slot_mapping_padding():
     tab = np.array([[4, 2], [0, 1]], np.int32)
     got = po.slot_mapping(tab, [0, -1, 1, 1], [5, 3, -2, 4], 4)
