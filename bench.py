@@ -52,8 +52,12 @@ def parse(argv=None):
                     help="append with pkv_slot_mapping + pkv_reshape_and_cache, then decode")
     ap.add_argument("--duplicate-shared", action="store_true",
                     help="shared workload: give every sibling private copies of the prefix blocks (control)")
-    ap.add_argument("--op", choices=("decode", "copy_blocks"), default="decode",
-                    help="decode (the hot path, default) or the batched block copy of copy-on-write")
+    ap.add_argument("--op", choices=("decode", "copy_blocks", "rows"), default="decode",
+                    help="decode (the hot path, default), the batched block copy of copy-on-write, or "
+                         "several query rows per KV head (grouped-query heads, multi-token queries)")
+    ap.add_argument("--group", type=int, default=None,
+                    help="--op rows: query heads per KV head (default: the workload's query_heads / heads)")
+    ap.add_argument("--queries", type=int, default=1, help="--op rows: query tokens per sequence")
     ap.add_argument("--copy-pairs", type=int, default=1024, help="block pairs per copy launch (--op copy_blocks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -90,6 +94,8 @@ def main(argv=None) -> int:
     t = build_tables(args.config, block_size=args.block_size)
     if args.op == "copy_blocks":
         return bench_copy_blocks(args, t, pkv, lib, dev)
+    if args.op == "rows":
+        return bench_rows(args, t, pkv, lib, dev)
     dup = None
     if args.duplicate_shared:
         dup_tab, copies, n_total = duplicate_shared(t)
@@ -253,6 +259,112 @@ def main(argv=None) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def bench_rows(args, t, pkv, lib, dev) -> int:
+    """Several query rows per KV head on the matrix-core kernel: G query heads
+    per KV head (grouped-query decode) and/or Q query tokens per sequence.
+    One step = the split pass and the merge pass of one call; the roofline
+    times the split pass (for Q > 1, the whole call)."""
+    import numpy as np
+    import torch
+
+    from synth import make_pools, normal_16bit
+
+    Hkv, D, B, S = t.num_heads, t.head_dim, t.block_size, t.num_seqs
+    G = args.group or config_query_heads(t) // Hkv
+    Q = args.queries
+    H = G * Hkv
+    dsize = 2
+    tab = torch.from_numpy(t.block_tables).to(dev)
+    lens = torch.from_numpy(t.context_lens).to(dev)
+    reps = []
+    for r in range(args.replicas):
+        t.seed += 1000 * r
+        kp, vp = make_pools(t, dev)
+        t.seed -= 1000 * r
+        shape = (S, H, D) if Q == 1 else (S, Q, H, D)
+        q = normal_16bit(shape, t.dtype, dev, t.seed * 16 + 20 + r)
+        reps.append((kp, vp, q, torch.empty_like(q)))
+    desc = pkv.pool_desc_of(reps[0][0])
+    dref = ctypes.byref(desc)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+    if Q == 1:
+        wsb = pkv.decode_workspace_bytes(S, H, t.max_blocks, reps[0][0], 0)
+    else:
+        wsb = pkv.multi_workspace_bytes(S, Q, H, t.max_blocks, reps[0][0])
+    if wsb == 0:
+        print("unsupported shape for the matrix-core path", file=sys.stderr)
+        return 2
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {pkv.status_string(st)}")
+
+    def step(i, ev=None):
+        kp, vp, q, out = reps[i % len(reps)]
+        if ev is not None:
+            ev[0].record(stream)
+        if Q == 1:
+            check(lib.pkv_decode_partitions(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), tab.data_ptr(),
+                                            lens.data_ptr(), ctypes.c_float(D ** -0.5), S, H, t.max_blocks, dref, 0,
+                                            ws.data_ptr(), wsb, sp), "decode_partitions")
+            if ev is not None:
+                ev[1].record(stream)
+            check(lib.pkv_decode_merge(out.data_ptr(), lens.data_ptr(), S, H, t.max_blocks, dref, 0, ws.data_ptr(),
+                                       wsb, sp), "decode_merge")
+        else:
+            check(lib.pkv_paged_attention_multi(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                tab.data_ptr(), lens.data_ptr(), ctypes.c_float(D ** -0.5), S, Q, H,
+                                                t.max_blocks, dref, ws.data_ptr(), wsb, sp), "paged_attention_multi")
+            if ev is not None:
+                ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    L = t.context_lens.astype(np.int64)
+    kv = int(L.sum()) * Hkv * D * 2 * dsize
+    nbytes = kv + 2 * S * Q * H * D * dsize + int((-(-L // B)).sum()) * 4 + S * 4
+    kern_mean_ms = float(np.mean(kern_ms))
+    achieved = nbytes / (kern_mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged attention, several query rows per KV head: achieved HBM GB/s + KV tokens/s",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.config}: {S} seqs, {H} query heads over {Hkv} KV heads x {D}, {Q} query "
+                               f"token(s) per sequence, B={B}, context_len {describe_lengths(t)}",
+                   "global_batch": S, "kv_tokens": t.kv_tokens(), "query_rows_per_kv_head": G * Q,
+                   "parallelism": "none (1 GPU)"},
+        "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "decode_group_kernel" + (" + merge" if Q > 1 else ""), "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                     "mean_launch_us": round(kern_mean_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def config_query_heads(t) -> int:
+    from synth.configs import CONFIGS
+    return int(CONFIGS.get(t.name, {}).get("query_heads", t.num_heads))
 
 
 def bench_copy_blocks(args, t, pkv, lib, dev) -> int:

@@ -62,6 +62,11 @@ CONFIGS = {
     "longctx": dict(index=5, num_heads=96, head_dim=128, dtype="f16", block_size=16, num_seqs=16,
                     lengths=("uniform", 8192, 32768), pool=("slack", 1.2), tables="permute",
                     max_len=32768, partition_size=512),
+    # grouped-query layer of the Llama-2-70B shape: the pool holds 8 KV heads,
+    # 64 query heads read them in groups of 8
+    "llama70b": dict(index=6, num_heads=8, head_dim=128, dtype="bf16", block_size=16, num_seqs=256,
+                     lengths=("uniform", 1, 2048), pool=("slack", 1.2), tables="permute", max_len=2048,
+                     query_heads=64),
 }
 
 
