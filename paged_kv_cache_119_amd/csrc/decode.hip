@@ -401,14 +401,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // priority as it progresses through its slice, so wavefronts that share a
 // SIMD finish together instead of in order of age.
 
-// One chunk of the stream: chunk c of row (s, h), in the piece [cb, ce) of
-// that row the slice covers.  `valid` is false once the stream has ended;
-// the other fields then repeat the last chunk.
-struct Chunk {
-  int s, h, L, c, cb, ce;
-  bool valid;
-};
-
 template <int DT, int D, int B, bool APP>
 struct Stream {
   using G = Geo<D>;
@@ -434,19 +426,12 @@ struct Stream {
   float *ws_m;
   float *ws_l;
   float *ws_o;
-  const int64_t *cum;
-  const int32_t *lens;
   int64_t blk_stride, num_blocks, new_stride;
   int S, H, maxb;
   float scale_log2;
   int lane, lane_off, row, qoff;
   int64_t worker;
-  // producer (cursor over the slice)
-  uint64_t it_hi;
-  int cs_, ch_, cL, cn, cc, ccb, cce;  // s, h, L, chunks of row, chunk, piece [cb, ce)
-  uint64_t cseg;                      // cost position of chunk 0 of row (s, h)
-  bool cvalid;
-  Chunk last;
+  ChunkCursor<TC> cur;  // the slice, chunk by chunk
   // running state of the current piece
   u32x4 qv;
   float m, l, acc[8];
@@ -464,8 +449,7 @@ struct Stream {
     ws_m = a.ws_m;
     ws_l = a.ws_l;
     ws_o = a.ws_o;
-    cum = cum_;
-    lens = lens_;
+    cur.init(cum_, lens_, a.S, a.H, lane_);
     blk_stride = (int64_t)a.Hkv * B * D;
     num_blocks = a.num_blocks;
     new_stride = a.new_stride;
@@ -477,87 +461,6 @@ struct Stream {
     lane_off = lane * 8;
     row = lane / LPT;
     qoff = (lane % LPT) * 8;
-    cvalid = false;
-  }
-
-  __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
-  __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
-
-  // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
-  __device__ __forceinline__ int find_seq(uint64_t p) const {
-    int base = 0, span = S;
-    while (span > 1) {
-      const int step = (span + 63) >> 6;
-      const int idx = base + lane * step;
-      const bool ok = idx < base + span && (uint64_t)cum[idx] <= p;
-      const uint64_t mask = __ballot(ok);
-      const int j = __builtin_amdgcn_readfirstlane(__popcll(mask)) - 1;
-      base += j * step;
-      span = min(step, span - j * step);
-    }
-    return base;
-  }
-
-  // Start the slice [lo, hi) (lo < hi <= total).
-  __device__ __forceinline__ void enter(uint64_t lo, uint64_t hi) {
-    it_hi = hi;
-    const int s = find_seq(lo);
-    const uint64_t base = cum_at(s);
-    cs_ = s;
-    cL = len_at(s);
-    cn = (cL + TC - 1) / TC;  // sequence s has chunks: cum[s + 1] > lo >= cum[s]
-    const uint64_t off = lo - base;  // < H * cn
-    const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
-    ch_ = (int)h;
-    cseg = base + (uint64_t)h * cn;
-    ccb = (int)(lo - cseg);
-    cc = ccb;
-    cce = (int)min((uint64_t)cn, hi - cseg);
-    cvalid = true;
-  }
-
-  // Move to the row after (s, h) inside the slice, or end the slice.
-  __device__ __forceinline__ void next_row() {
-    const uint64_t pos = cseg + cn;
-    if (pos >= it_hi) {
-      cvalid = false;
-      return;
-    }
-    if (ch_ + 1 < H) {
-      ++ch_;
-    } else {
-      int s = cs_ + 1;
-      while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
-      cs_ = s;
-      ch_ = 0;
-      cL = len_at(s);
-      cn = (cL + TC - 1) / TC;
-    }
-    cseg = pos;
-    ccb = 0;
-    cc = 0;
-    cce = (int)min((uint64_t)cn, it_hi - cseg);
-  }
-
-  // The next chunk of the stream.
-  __device__ __forceinline__ Chunk produce() {
-    if (!cvalid) {
-      Chunk none = last;
-      none.valid = false;
-      return none;
-    }
-    Chunk ch;
-    ch.s = cs_;
-    ch.h = ch_;
-    ch.L = cL;
-    ch.c = cc;
-    ch.cb = ccb;
-    ch.ce = cce;
-    ch.valid = true;
-    last = ch;
-    if (cc + 1 < cce) ++cc;
-    else next_row();
-    return ch;
   }
 
   __device__ __forceinline__ static int first_block(int c) { return TC >= B ? c * (TC / B) : c / (B / TC); }
@@ -732,16 +635,16 @@ struct Stream {
   // loads in flight.  The priority falls from 3 to 0 as the wavefront passes
   // quarters of its slice (th1..th3 chunks).
   __device__ __forceinline__ void run(int th1, int th2, int th3) {
-    Chunk d0 = produce();
+    Chunk d0 = cur.produce();
     if (!d0.valid) return;
     int done = 0;
     Buf ba, bb;
     uint32_t ea = load_entries(d0);
-    Chunk d1 = produce();
+    Chunk d1 = cur.produce();
     uint32_t eb = load_entries(d1);
     load_kv(d0, ea, ba);
     for (;;) {
-      const Chunk d2 = produce();
+      const Chunk d2 = cur.produce();
       ea = load_entries(d2);
       load_kv(d1, eb, bb);
       __builtin_amdgcn_sched_barrier(0);
@@ -751,7 +654,7 @@ struct Stream {
       if (done == th2) __builtin_amdgcn_s_setprio(1);
       if (done == th3) __builtin_amdgcn_s_setprio(0);
       if (!d1.valid) break;
-      const Chunk d3 = produce();
+      const Chunk d3 = cur.produce();
       eb = load_entries(d3);
       load_kv(d2, ea, ba);
       __builtin_amdgcn_sched_barrier(0);
@@ -796,7 +699,7 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
   ST st;
   st.init(a, cum, lens, lane);
   st.worker = w;
-  st.enter(lo, hi);
+  st.cur.enter(lo, hi);
   const int n = (int)(hi - lo);
   const int th1 = n / 4, th2 = n / 2, th3 = (3 * n) / 4;
   __builtin_amdgcn_s_setprio(3);

@@ -84,12 +84,6 @@ __device__ __forceinline__ f4_t mfma_pv(uint32_t v01, uint32_t v23, uint32_t p01
   }
 }
 
-// One chunk of the stream: chunk c of row (s, kv head h), piece [cb, ce).
-struct GChunk {
-  int s, h, L, c, cb, ce;
-  bool valid;
-};
-
 template <int DT, int B>
 struct GroupStream {
   static constexpr int NE = GTC >= B ? GTC / B : 1;  // table entries per chunk
@@ -108,19 +102,12 @@ struct GroupStream {
   float *ws_m;
   float *ws_l;
   float *ws_o;
-  const int64_t *cum;
-  const int32_t *lens;
   int64_t blk_stride, num_blocks;
   int S, Hkv, H, maxb, nq, gq, M;
   float scale_log2;
   int lane, g, r;
   int64_t worker;
-  // producer
-  uint64_t it_hi;
-  int cs_, ch_, cL, cn, cc, ccb, cce;
-  uint64_t cseg;
-  bool cvalid;
-  GChunk last;
+  ChunkCursor<GTC> cur;  // the slice, chunk by chunk
   // running state of the current piece (row r of this lane)
   f4_t acc[8];
   float m, lp;
@@ -135,8 +122,7 @@ struct GroupStream {
     ws_m = a.ws_m;
     ws_l = a.ws_l;
     ws_o = a.ws_o;
-    cum = cum_;
-    lens = lens_;
+    cur.init(cum_, lens_, a.S, a.Hkv, lane_);
     blk_stride = (int64_t)a.Hkv * B * GD;
     num_blocks = a.num_blocks;
     S = a.S;
@@ -150,98 +136,20 @@ struct GroupStream {
     lane = lane_;
     g = lane >> 4;
     r = lane & 15;
-    cvalid = false;
-  }
-
-  __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
-  __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
-
-  // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
-  __device__ __forceinline__ int find_seq(uint64_t p) const {
-    int base = 0, span = S;
-    while (span > 1) {
-      const int step = (span + 63) >> 6;
-      const int idx = base + lane * step;
-      const bool ok = idx < base + span && (uint64_t)cum[idx] <= p;
-      const uint64_t mask = __ballot(ok);
-      const int j = __builtin_amdgcn_readfirstlane(__popcll(mask)) - 1;
-      base += j * step;
-      span = min(step, span - j * step);
-    }
-    return base;
-  }
-
-  __device__ __forceinline__ void enter(uint64_t lo, uint64_t hi) {
-    it_hi = hi;
-    const int s = find_seq(lo);
-    const uint64_t base = cum_at(s);
-    cs_ = s;
-    cL = len_at(s);
-    cn = (cL + GTC - 1) / GTC;
-    const uint64_t off = lo - base;  // < Hkv * cn
-    const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
-    ch_ = (int)h;
-    cseg = base + (uint64_t)h * cn;
-    ccb = (int)(lo - cseg);
-    cc = ccb;
-    cce = (int)min((uint64_t)cn, hi - cseg);
-    cvalid = true;
-  }
-
-  __device__ __forceinline__ void next_row() {
-    const uint64_t pos = cseg + cn;
-    if (pos >= it_hi) {
-      cvalid = false;
-      return;
-    }
-    if (ch_ + 1 < Hkv) {
-      ++ch_;
-    } else {
-      int s = cs_ + 1;
-      while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
-      cs_ = s;
-      ch_ = 0;
-      cL = len_at(s);
-      cn = (cL + GTC - 1) / GTC;
-    }
-    cseg = pos;
-    ccb = 0;
-    cc = 0;
-    cce = (int)min((uint64_t)cn, it_hi - cseg);
-  }
-
-  __device__ __forceinline__ GChunk produce() {
-    if (!cvalid) {
-      GChunk none = last;
-      none.valid = false;
-      return none;
-    }
-    GChunk ch;
-    ch.s = cs_;
-    ch.h = ch_;
-    ch.L = cL;
-    ch.c = cc;
-    ch.cb = ccb;
-    ch.ce = cce;
-    ch.valid = true;
-    last = ch;
-    if (cc + 1 < cce) ++cc;
-    else next_row();
-    return ch;
   }
 
   __device__ __forceinline__ static int first_block(int c) { return GTC >= B ? c * (GTC / B) : c / (B / GTC); }
-  __device__ __forceinline__ static int last_block(const GChunk &d) { return (min(d.L, d.ce * GTC) - 1) / B; }
+  __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * GTC) - 1) / B; }
 
   // Stage 1: this lane's table entry of chunk d (clamped to the piece's last
   // block; tokens past it are masked).
-  __device__ __forceinline__ uint32_t load_entries(const GChunk &d) const {
+  __device__ __forceinline__ uint32_t load_entries(const Chunk &d) const {
     const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
     return (uint32_t)tables[(int64_t)d.s * maxb + lb];
   }
 
   // Base element offset of token t of chunk d (its block from the entries).
-  __device__ __forceinline__ int64_t token_base(const GChunk &d, uint32_t e, int t, bool &bd) const {
+  __device__ __forceinline__ int64_t token_base(const Chunk &d, uint32_t e, int t, bool &bd) const {
     int blk, off;
     if constexpr (GTC >= B) {
       const int b0 = __builtin_amdgcn_readlane((int)e, 0);
@@ -261,7 +169,7 @@ struct GroupStream {
 
   // Stage 2: K rows (token r), V rows (tokens 4g .. 4g+3) and the query rows
   // of chunk d; the same loads for every chunk.
-  __device__ __forceinline__ void load_kv(const GChunk &d, uint32_t e, Buf &b) const {
+  __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     bool bd = false;
     const int64_t kb = token_base(d, e, r, bd) + 8 * g;
 #pragma unroll
@@ -281,7 +189,7 @@ struct GroupStream {
   }
 
   // Stage 3: scores, online softmax and the weighted V sum of chunk d.
-  __device__ __forceinline__ void consume(const GChunk &d, Buf &b) {
+  __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
     if (d.c == d.cb) {
       m = kNegInf;
       lp = 0.f;
@@ -345,7 +253,7 @@ struct GroupStream {
     if (d.c == d.ce - 1) finish_piece(d);
   }
 
-  __device__ __forceinline__ void finish_piece(const GChunk &d) {
+  __device__ __forceinline__ void finish_piece(const Chunk &d) {
     lp += __shfl_xor(lp, 16);
     lp += __shfl_xor(lp, 32);
     if (r >= M) return;
@@ -382,16 +290,16 @@ struct GroupStream {
   // The stream, as in the balanced decode kernel (stage 1 of chunk n + 2,
   // stage 2 of chunk n + 1, stage 3 of chunk n; the same loads every step).
   __device__ __forceinline__ void run(int th1, int th2, int th3) {
-    GChunk d0 = produce();
+    Chunk d0 = cur.produce();
     if (!d0.valid) return;
     int done = 0;
     Buf ba, bb;
     uint32_t ea = load_entries(d0);
-    GChunk d1 = produce();
+    Chunk d1 = cur.produce();
     uint32_t eb = load_entries(d1);
     load_kv(d0, ea, ba);
     for (;;) {
-      const GChunk d2 = produce();
+      const Chunk d2 = cur.produce();
       ea = load_entries(d2);
       load_kv(d1, eb, bb);
       __builtin_amdgcn_sched_barrier(0);
@@ -401,7 +309,7 @@ struct GroupStream {
       if (done == th2) __builtin_amdgcn_s_setprio(1);
       if (done == th3) __builtin_amdgcn_s_setprio(0);
       if (!d1.valid) break;
-      const GChunk d3 = produce();
+      const Chunk d3 = cur.produce();
       eb = load_entries(d3);
       load_kv(d2, ea, ba);
       __builtin_amdgcn_sched_barrier(0);
@@ -443,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   ST st;
   st.init(a, cum, lens, lane);
   st.worker = w;
-  st.enter(lo, hi);
+  st.cur.enter(lo, hi);
   const int n = (int)(hi - lo);
   __builtin_amdgcn_s_setprio(3);
   st.run(n / 4, n / 2, (3 * n) / 4);

@@ -68,4 +68,116 @@ __device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int row
   }
 }
 
+// One chunk of a stream: chunk c of row (s, h), in the piece [cb, ce) of that
+// row the slice covers.  `valid` is false once the stream has ended; the
+// other fields then repeat the last chunk (so its loads stay in bounds).
+struct Chunk {
+  int s, h, L, c, cb, ce;
+  bool valid;
+};
+
+// Walks a wavefront's slice of the cost space chunk by chunk: sequences of
+// `rows` rows of ceil(L / TC) chunks each, with the chunk prefix `cum` and the
+// lengths `lens` in LDS.
+template <int TC>
+struct ChunkCursor {
+  const int64_t *cum;
+  const int32_t *lens;
+  int S, rows, lane;
+  uint64_t it_hi;
+  int cs_, ch_, cL, cn, cc, ccb, cce;  // s, h, L, chunks of row, chunk, piece [cb, ce)
+  uint64_t cseg;                      // cost position of chunk 0 of row (s, h)
+  bool cvalid;
+  Chunk last;
+
+  __device__ __forceinline__ void init(const int64_t *cum_, const int32_t *lens_, int S_, int rows_, int lane_) {
+    cum = cum_;
+    lens = lens_;
+    S = S_;
+    rows = rows_;
+    lane = lane_;
+    cvalid = false;
+  }
+
+  __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
+  __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
+
+  // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
+  __device__ __forceinline__ int find_seq(uint64_t p) const {
+    int base = 0, span = S;
+    while (span > 1) {
+      const int step = (span + 63) >> 6;
+      const int idx = base + lane * step;
+      const bool ok = idx < base + span && (uint64_t)cum[idx] <= p;
+      const uint64_t mask = __ballot(ok);
+      const int j = __builtin_amdgcn_readfirstlane(__popcll(mask)) - 1;
+      base += j * step;
+      span = min(step, span - j * step);
+    }
+    return base;
+  }
+
+  // Start the slice [lo, hi) (lo < hi <= total).
+  __device__ __forceinline__ void enter(uint64_t lo, uint64_t hi) {
+    it_hi = hi;
+    const int s = find_seq(lo);
+    const uint64_t base = cum_at(s);
+    cs_ = s;
+    cL = len_at(s);
+    cn = (cL + TC - 1) / TC;  // sequence s has chunks: cum[s + 1] > lo >= cum[s]
+    const uint64_t off = lo - base;  // < rows * cn
+    const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
+    ch_ = (int)h;
+    cseg = base + (uint64_t)h * cn;
+    ccb = (int)(lo - cseg);
+    cc = ccb;
+    cce = (int)min((uint64_t)cn, hi - cseg);
+    cvalid = true;
+  }
+
+  // Move to the row after (s, h) inside the slice, or end the slice.
+  __device__ __forceinline__ void next_row() {
+    const uint64_t pos = cseg + cn;
+    if (pos >= it_hi) {
+      cvalid = false;
+      return;
+    }
+    if (ch_ + 1 < rows) {
+      ++ch_;
+    } else {
+      int s = cs_ + 1;
+      while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
+      cs_ = s;
+      ch_ = 0;
+      cL = len_at(s);
+      cn = (cL + TC - 1) / TC;
+    }
+    cseg = pos;
+    ccb = 0;
+    cc = 0;
+    cce = (int)min((uint64_t)cn, it_hi - cseg);
+  }
+
+  // The next chunk of the stream.
+  __device__ __forceinline__ Chunk produce() {
+    if (!cvalid) {
+      Chunk none = last;
+      none.valid = false;
+      return none;
+    }
+    Chunk ch;
+    ch.s = cs_;
+    ch.h = ch_;
+    ch.L = cL;
+    ch.c = cc;
+    ch.cb = ccb;
+    ch.ce = cce;
+    ch.valid = true;
+    last = ch;
+    if (cc + 1 < cce) ++cc;
+    else next_row();
+    return ch;
+  }
+};
+
 }  // namespace pkv
