@@ -71,6 +71,11 @@ __all__ = [
     "decode_partitioned",
     "dense_causal",
     "dense_causal_last_row",
+    "e4m3_to_f64",
+    "f64_to_e4m3",
+    "quantize_e4m3",
+    "reshape_and_cache_fp8",
+    "decode_rows_fp8",
 ]
 
 
@@ -122,6 +127,101 @@ def f64_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
             flat_out[i] = best
         return out
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ----------------------------------------------------------------------------
+# 8-bit floating point (OCP e4m3) codes <-> float64
+# ----------------------------------------------------------------------------
+#
+# [PA] 总结 item 6 names an FP8-quantised KV cache as a later layer on top of
+# the paged cache; none of the pages fixes its format.  The reading taken: the
+# OCP 8-bit "e4m3" format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+# bits, no infinities, one NaN pattern per sign: exponent and mantissa all
+# ones; largest finite magnitude 448) and one float32 scale per pool, a code c
+# standing for e4m3(c) * scale.
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3 code, exactly, as float64 (NaN for 0x7F / 0xFF)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * 2.0 ** -6
+    val = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+# Magnitudes of the 127 non-negative finite codes 0x00 .. 0x7E, increasing.
+_E4M3_MAGS = None
+
+
+def _e4m3_mags() -> np.ndarray:
+    global _E4M3_MAGS
+    if _E4M3_MAGS is None:
+        _E4M3_MAGS = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    return _E4M3_MAGS
+
+
+def f64_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """The e4m3 code nearest to each value: round to nearest, ties to the code
+    with an even mantissa (the even code), saturating (a magnitude past 448,
+    infinities included, takes the largest finite code), NaN to 0x7F.  The
+    sign is kept, also for values that round to zero.
+
+    Written as the definition: the nearest of the 127 finite magnitudes found
+    by comparing against every one of them.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    mags = _e4m3_mags()
+    codes = np.arange(0x7F)
+    step = 1 << 16
+    for i0 in range(0, flat.size, step):
+        xs = flat[i0:i0 + step]
+        a = np.abs(xs)
+        finite = np.isfinite(a)
+        a_f = np.where(finite, a, 0.0)
+        dist = np.abs(a_f[:, None] - mags[None, :])
+        best = dist.min(axis=1, keepdims=True)
+        cand = dist == best  # one code, or two on a tie
+        # on a tie prefer the even code: rank odd codes after every even one
+        rank = np.where(cand, (codes[None, :] & 1) * 256 + codes[None, :], 1 << 20)
+        c = rank.argmin(axis=1).astype(np.uint8)
+        c = np.where(finite, c, np.uint8(0x7E))  # +-inf saturate
+        c = np.where(np.signbit(xs), c | np.uint8(0x80), c)
+        c = np.where(np.isnan(xs), np.uint8(0x7F), c)
+        out[i0:i0 + step] = c
+    return out.reshape(x.shape)
+
+
+def quantize_e4m3(bits, dtype: str, scale: float) -> np.ndarray:
+    """Codes of 16-bit values under a per-pool scale: code = e4m3(x * r) with
+    r = 1 / scale rounded to float32 and the product rounded to float32 before
+    the rounding to e4m3 (the decision is taken in float32, the precision the
+    cache append computes in)."""
+    x32 = bits_to_f64(bits, dtype).astype(np.float32)
+    r = np.float32(1.0) / np.float32(scale)
+    return f64_to_e4m3((x32 * r).astype(np.float64))
+
+
+def reshape_and_cache_fp8(k_bits, v_bits, k_pool_codes, v_pool_codes, slots, block_size: int,
+                          dtype: str, k_scale: float, v_scale: float) -> None:
+    """The cache append of ``reshape_and_cache`` into e4m3 pools: each new row
+    is quantised (``quantize_e4m3`` with the K or V scale) and written to its
+    slot; negative slots and slots past the pool are skipped."""
+    kq = quantize_e4m3(k_bits, dtype, k_scale)
+    vq = quantize_e4m3(v_bits, dtype, v_scale)
+    num_blocks = k_pool_codes.shape[0]
+    for t in range(len(slots)):
+        slot = int(slots[t])
+        if slot < 0 or slot >= num_blocks * block_size:
+            continue
+        blk, off = divmod(slot, block_size)
+        k_pool_codes[blk, :, off, :] = kq[t]
+        v_pool_codes[blk, :, off, :] = vq[t]
 
 
 # ----------------------------------------------------------------------------
@@ -301,6 +401,34 @@ def decode_rows(q_bits, k_pool_bits, v_pool_bits, block_tables, context_lens,
                 kvh = h // G
                 K = bits_to_f64(gather(k_pool_bits, row, visible, block_size, kvh), dtype)
                 V = bits_to_f64(gather(v_pool_bits, row, visible, block_size, kvh), dtype)
+                o, _, _, _ = attend(bits_to_f64(q_bits[s, i, h], dtype), K, V, scale64)
+                out[s, i, h] = o
+    return out
+
+
+def decode_rows_fp8(q_bits, k_pool_codes, v_pool_codes, block_tables, context_lens,
+                    scale: float, block_size: int, dtype: str, k_scale: float,
+                    v_scale: float) -> np.ndarray:
+    """``decode_rows`` over e4m3 pools: every gathered K row is
+    ``e4m3(code) * k_scale`` and every V row ``e4m3(code) * v_scale`` (the
+    scales taken as float32 values), exactly in float64; then the same
+    attention.  ``q_bits`` is ``[S, Q, H, D]`` 16-bit, the output float64."""
+    S, Q, H, D = q_bits.shape
+    Hkv = k_pool_codes.shape[1]
+    G = H // Hkv
+    out = np.zeros((S, Q, H, D), dtype=np.float64)
+    scale64 = float(np.float32(scale))
+    ks = float(np.float32(k_scale))
+    vs = float(np.float32(v_scale))
+    for s in range(S):
+        L = int(context_lens[s])
+        row = np.asarray(block_tables)[s]
+        for i in range(Q):
+            visible = L - Q + 1 + i if L > 0 else 0
+            for h in range(H):
+                kvh = h // G
+                K = e4m3_to_f64(gather(k_pool_codes, row, visible, block_size, kvh)) * ks
+                V = e4m3_to_f64(gather(v_pool_codes, row, visible, block_size, kvh)) * vs
                 o, _, _, _ = attend(bits_to_f64(q_bits[s, i, h], dtype), K, V, scale64)
                 out[s, i, h] = o
     return out
