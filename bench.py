@@ -55,6 +55,8 @@ def parse(argv=None):
     ap.add_argument("--op", choices=("decode", "copy_blocks", "rows"), default="decode",
                     help="decode (the hot path, default), the batched block copy of copy-on-write, or "
                          "several query rows per KV head (grouped-query heads, multi-token queries)")
+    ap.add_argument("--kv", choices=("16bit", "fp8"), default="16bit",
+                    help="--op decode: pool element type (fp8: e4m3 codes with per-pool scales)")
     ap.add_argument("--group", type=int, default=None,
                     help="--op rows: query heads per KV head (default: the workload's query_heads / heads)")
     ap.add_argument("--queries", type=int, default=1, help="--op rows: query tokens per sequence")
@@ -96,6 +98,8 @@ def main(argv=None) -> int:
         return bench_copy_blocks(args, t, pkv, lib, dev)
     if args.op == "rows":
         return bench_rows(args, t, pkv, lib, dev)
+    if args.kv == "fp8":
+        return bench_fp8(args, t, pkv, lib, dev)
     dup = None
     if args.duplicate_shared:
         dup_tab, copies, n_total = duplicate_shared(t)
@@ -360,6 +364,144 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def bench_fp8(args, t, pkv, lib, dev) -> int:
+    """Decode over an e4m3 KV cache: one step = the quantising append of the
+    batch's new tokens (slot mapping + pkv_reshape_and_cache_fp8) and
+    pkv_paged_attention_decode_fp8 (split pass + merge pass).  The roofline
+    times the decode call (both of its launches) with HIP events."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_119_amd import accounting as acc
+    from synth import make_fp8_pools, make_query, normal_16bit
+
+    S, H, D, B = t.num_seqs, t.num_heads, t.head_dim, t.block_size
+    ks = vs = 1.0 / 60
+    tab = torch.from_numpy(t.block_tables).to(dev)
+    lens = torch.from_numpy(t.context_lens).to(dev)
+    seq = torch.arange(S, dtype=torch.int32, device=dev)
+    pos = torch.from_numpy((t.context_lens - 1).astype(np.int32)).to(dev)
+    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    reps = []
+    for r in range(args.replicas):
+        t.seed += 1000 * r
+        kp, vp = make_fp8_pools(t, dev)
+        q = make_query(t, dev)
+        knew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 9)
+        vnew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 10)
+        t.seed -= 1000 * r
+        reps.append((kp, vp, q, knew, vnew, torch.empty_like(q)))
+    desc = pkv.make_pool_desc(t.num_blocks, B, H, D, t.dtype)
+    dref = ctypes.byref(desc)
+    wsb = pkv.fp8_decode_workspace_bytes(S, H, t.max_blocks, reps[0][0], t.dtype)
+    if wsb == 0:
+        print("unsupported shape for the fp8 path", file=sys.stderr)
+        return 2
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+    print(f"[bench] fp8 {args.config}: S={S} H={H} D={D} B={B} N={t.num_blocks} kv_tokens={t.kv_tokens()}",
+          file=sys.stderr, flush=True)
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {pkv.status_string(st)}")
+
+    def step(i, ev=None):
+        kp, vp, q, knew, vnew, out = reps[i % len(reps)]
+        check(lib.pkv_slot_mapping(slots.data_ptr(), tab.data_ptr(), S, t.max_blocks, seq.data_ptr(),
+                                   pos.data_ptr(), S, dref, sp), "slot_mapping")
+        check(lib.pkv_reshape_and_cache_fp8(kp.data_ptr(), vp.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0, 0,
+                                            slots.data_ptr(), S, ctypes.c_float(ks), ctypes.c_float(vs), dref, sp),
+              "reshape_and_cache_fp8")
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.pkv_paged_attention_decode_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                 tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale),
+                                                 ctypes.c_float(ks), ctypes.c_float(vs), S, H, t.max_blocks, dref,
+                                                 ws.data_ptr(), wsb, sp), "paged_attention_decode_fp8")
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(reps[0][5].float()).all().item(), "non-finite output"
+
+    dec = acc.decode_bytes(t.context_lens, H, D, 2, B, kv_dtype_bytes=1)
+    app = acc.append_bytes(S, S, H, D, 2, pool_dtype_bytes=1)
+    step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+    kern_mean_ms = float(np.mean(kern_ms))
+    achieved = dec["total"] / (kern_mean_ms * 1e-3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_fp8(t, reps[0], ks, vs, args.cpu_budget_s)
+    line = {
+        "metric": "paged decode attention over an FP8 (e4m3) KV cache: achieved HBM GB/s + KV tokens/s",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": f"{t.dtype} (K/V e4m3)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {S} seqs x {H} heads x {D}, B={B}, context_len "
+                               f"{describe_lengths(t)}, e4m3 pools (scales 1/60), one decode step: quantising "
+                               f"append of {S} tokens + attention",
+                   "global_batch": S, "kv_tokens": t.kv_tokens(), "block_size": B, "pool_blocks": t.num_blocks,
+                   "replicas": args.replicas, "parallelism": "none (1 GPU)"},
+        "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "roofline": {"kernel": "decode_fp8_kernel + decode_balanced_merge_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": dec["total"],
+                     "mean_launch_us": round(kern_mean_ms * 1e3, 2),
+                     "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_fp8(t, rep, ks, vs, budget_s: float):
+    """The oracle's e4m3 attention on host copies of one replica, one thread,
+    sequence by sequence until the time budget is used."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_oracle as po
+    from paged_kv_cache_119_amd import accounting as acc
+    from synth import to_bits
+
+    kp, vp, q, _, _, _ = rep
+    kc, vc = kp.cpu().numpy(), vp.cpu().numpy()
+    qb = to_bits(q)
+    done = []
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            s = len(done) % t.num_seqs
+            po.decode_rows_fp8(qb[s:s + 1, None], kc, vc, t.block_tables[s:s + 1], t.context_lens[s:s + 1],
+                               t.scale, t.block_size, t.dtype, ks, vs)
+            done.append(s)
+        dt = time.perf_counter() - t0
+    lens = t.context_lens[np.asarray(done)]
+    by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size, kv_dtype_bytes=1)["total"]
+    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} sequence decodes over e4m3 pools ({len(done) / t.num_seqs:.1f} passes over the "
+                      f"{t.num_seqs}-sequence batch, all {t.num_heads} heads), {int(lens.sum())} KV tokens, "
+                      f"{dt:.1f} s, numpy float64, 1 thread",
+            "kv_tokens_per_s": round(float(lens.sum()) / dt, 1)}
 
 
 def config_query_heads(t) -> int:

@@ -345,6 +345,58 @@ pkv_status pkv_paged_attention_multi(void *out, const void *q, const void *k_poo
                                      int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/*
+ * FP8 KV cache
+ * ------------
+ * "PagedAttention 完全拆解", 总结 item 6, names an FP8-quantised KV cache as a
+ * later layer on top of the paged cache; the pages fix no format.  The one
+ * served here: pools of OCP e4m3 codes (1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; largest finite magnitude 448; no infinities; 0x7F and
+ * 0xFF are NaN) in the pool layout above, ONE BYTE per element.  Each pool
+ * has one float32 scale: code c stands for e4m3(c) * scale.  The pkv_pool
+ * descriptor is unchanged; its dtype names the 16-bit type of q, out and the
+ * new K / V rows.  Half the bytes of a 16-bit cache per token.
+ */
+
+/* Bytes of ONE fp8 pool: N * Hkv * B * D.  0 if the shape is invalid. */
+size_t pkv_fp8_pool_bytes(const pkv_pool *p);
+
+/*
+ * pkv_reshape_and_cache_fp8 -- pkv_reshape_and_cache into e4m3 pools, with
+ * the same slot rules, strides and alignment.  Each element is quantised:
+ *   code = e4m3(x * r),  r = 1 / scale rounded to float32 (on the host),
+ * the product rounded to float32, then to the nearest e4m3 value, ties to
+ * the even code; magnitudes past 448 (infinities too) saturate to +-448, NaN
+ * stays NaN, the sign of a zero is kept.
+ *   k_scale, v_scale  positive, finite, with a finite reciprocal, else
+ *                     PKV_ERR_SHAPE
+ */
+pkv_status pkv_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,
+                                     int64_t k_token_stride, int64_t v_token_stride,
+                                     const int64_t *slot_mapping, int32_t num_tokens, float k_scale,
+                                     float v_scale, const pkv_pool *p, void *stream);
+
+/*
+ * pkv_paged_attention_decode_fp8 -- pkv_paged_attention_decode over e4m3
+ * pools: every K element is e4m3(code) * k_scale and every V element
+ * e4m3(code) * v_scale; the attention equation, the rules for empty, invalid
+ * and out-of-pool contexts and the output rounding are those of
+ * pkv_paged_attention_decode (balanced split, then the merge pass).
+ *   out, q        [num_seqs][num_heads][head_dim] 16-bit (p->dtype)
+ *   num_heads     == Hkv and head_dim 128, else PKV_ERR_UNSUPPORTED
+ *   k_scale, v_scale  as for pkv_reshape_and_cache_fp8
+ *   workspace     >= pkv_fp8_decode_workspace_bytes(...) bytes, 256-byte aligned
+ * pkv_fp8_decode_workspace_bytes returns 0 for invalid or unsupported
+ * arguments.
+ */
+size_t pkv_fp8_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                      const pkv_pool *p);
+pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                          const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                          float k_scale, float v_scale, int32_t num_seqs, int32_t num_heads,
+                                          int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
+                                          size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

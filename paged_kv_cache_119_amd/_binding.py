@@ -36,6 +36,10 @@ EXPORTS = (
     "pkv_decode_merge",
     "pkv_multi_workspace_bytes",
     "pkv_paged_attention_multi",
+    "pkv_fp8_pool_bytes",
+    "pkv_reshape_and_cache_fp8",
+    "pkv_fp8_decode_workspace_bytes",
+    "pkv_paged_attention_decode_fp8",
 )
 
 
@@ -91,6 +95,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_multi_workspace_bytes": (sz, [i32, i32, i32, i32, pool]),
         "pkv_paged_attention_multi": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32,
                                                      pool, vp, sz, vp]),
+        "pkv_fp8_pool_bytes": (sz, [pool]),
+        "pkv_reshape_and_cache_fp8": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, i32, ctypes.c_float,
+                                                     ctypes.c_float, pool, vp]),
+        "pkv_fp8_decode_workspace_bytes": (sz, [i32, i32, i32, pool]),
+        "pkv_paged_attention_decode_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                                          ctypes.c_float, i32, i32, i32, pool, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -350,6 +360,97 @@ def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, 
                                        ctypes.byref(desc), workspace.data_ptr(),
                                        workspace.numel() * workspace.element_size(), _stream_ptr(dev))
     _check(st, "pkv_paged_attention_multi")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) pools: one byte per element, one float32 scale per pool
+# ---------------------------------------------------------------------------
+
+def _fp8_pools(k_pool, v_pool, dtype_name):
+    torch = _torch()
+    _need(k_pool, "k_pool", ndim=4)
+    _need(v_pool, "v_pool", ndim=4, device=k_pool.device)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    if k_pool.shape != v_pool.shape:
+        raise ValueError(f"k_pool {tuple(k_pool.shape)} and v_pool {tuple(v_pool.shape)} differ")
+    N, H, B, D = (int(x) for x in k_pool.shape)
+    return make_pool_desc(N, B, H, D, dtype_name)
+
+
+def fp8_pool_bytes(num_blocks, block_size, num_kv_heads, head_dim) -> int:
+    d = make_pool_desc(num_blocks, block_size, num_kv_heads, head_dim, "f16")
+    return int(load_library().pkv_fp8_pool_bytes(ctypes.byref(d)))
+
+
+def reshape_and_cache_fp8(k, v, k_pool, v_pool, slot_mapping, k_scale, v_scale):
+    """Quantise new tokens' K/V rows ``[T, Hkv, D]`` (16-bit) to e4m3 codes
+    under the pools' scales and write them into their slots."""
+    torch = _torch()
+    lib = load_library()
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(k))
+    dev = k_pool.device
+    for name, t in (("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} must be a tensor on {dev}")
+        if t.dtype != k.dtype:
+            raise TypeError("k and v must have the same dtype")
+        if t.dim() != 3 or tuple(t.shape[1:]) != (desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [T, {desc.num_kv_heads}, {desc.head_dim}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{name} must have heads and dims contiguous")
+    _need(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1, device=dev)
+    T = int(k.shape[0])
+    if v.shape[0] != T or slot_mapping.shape[0] != T:
+        raise ValueError("k, v and slot_mapping must have the same number of tokens")
+    st = lib.pkv_reshape_and_cache_fp8(k_pool.data_ptr(), v_pool.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       int(k.stride(0)) if T > 0 else 0, int(v.stride(0)) if T > 0 else 0,
+                                       slot_mapping.data_ptr(), T, float(k_scale), float(v_scale),
+                                       ctypes.byref(desc), _stream_ptr(dev))
+    _check(st, "pkv_reshape_and_cache_fp8")
+
+
+def fp8_decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, dtype="f16") -> int:
+    N, H, B, D = (int(x) for x in k_pool.shape)
+    desc = make_pool_desc(N, B, H, D, dtype)
+    return int(load_library().pkv_fp8_decode_workspace_bytes(int(num_seqs), int(num_heads),
+                                                             int(max_blocks_per_seq), ctypes.byref(desc)))
+
+
+def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out=None,
+                               workspace=None):
+    """Single-query decode attention over e4m3 pools (K element = code value *
+    k_scale, V element = code value * v_scale); ``q`` and ``out`` [S, H, D]
+    16-bit."""
+    torch = _torch()
+    lib = load_library()
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q))
+    dev = k_pool.device
+    _need(q, "q", ndim=3, device=dev)
+    S, H, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {desc.head_dim}")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("q, block_tables and context_lens disagree on the number of sequences")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    maxb = int(block_tables.shape[1])
+    if workspace is None:
+        need = fp8_decode_workspace_bytes(S, H, maxb, k_pool, _dtype_name(q))
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.pkv_paged_attention_decode_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                                            float(k_scale), float(v_scale), S, H, maxb, ctypes.byref(desc),
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream_ptr(dev))
+    _check(st, "pkv_paged_attention_decode_fp8")
     return out
 
 

@@ -49,16 +49,19 @@ def table_bytes(max_len: int, block_size: int, requests: int = 1) -> int:
     return num_blocks_for(max_len, block_size) * TABLE_ENTRY_BYTES * requests
 
 
-def decode_bytes(context_lens, num_heads: int, head_dim: int, dtype_bytes: int, block_size: int) -> dict:
+def decode_bytes(context_lens, num_heads: int, head_dim: int, dtype_bytes: int, block_size: int,
+                 kv_dtype_bytes: int = None) -> dict:
     """Algorithmic bytes of one decode call.
 
     K and V of every live token for every head, q read once, the output written
-    once, the table entries actually needed and the context lengths.
+    once, the table entries actually needed and the context lengths.  The pools
+    may hold a narrower type than q and out (``kv_dtype_bytes``, 1 for e4m3).
     """
+    kvb = dtype_bytes if kv_dtype_bytes is None else kv_dtype_bytes
     L = np.asarray(context_lens, dtype=np.int64)
     L = np.maximum(L, 0)
     S = int(L.shape[0])
-    kv = int(L.sum()) * num_heads * head_dim * 2 * dtype_bytes
+    kv = int(L.sum()) * num_heads * head_dim * 2 * kvb
     q = S * num_heads * head_dim * dtype_bytes
     out = q
     table = int(sum(num_blocks_for(x, block_size) for x in L)) * TABLE_ENTRY_BYTES
@@ -67,12 +70,15 @@ def decode_bytes(context_lens, num_heads: int, head_dim: int, dtype_bytes: int, 
             "total": kv + q + out + table + lens, "kv_tokens": int(L.sum())}
 
 
-def append_bytes(num_valid_tokens: int, num_tokens: int, num_heads: int, head_dim: int, dtype_bytes: int) -> dict:
+def append_bytes(num_valid_tokens: int, num_tokens: int, num_heads: int, head_dim: int, dtype_bytes: int,
+                 pool_dtype_bytes: int = None) -> dict:
     """Algorithmic bytes of one cache append: read k and v of the valid tokens,
-    write them into the pools, read every slot number."""
+    write them into the pools (``pool_dtype_bytes`` per element, 1 for e4m3),
+    read every slot number."""
     row = num_heads * head_dim * dtype_bytes
+    prow = num_heads * head_dim * (dtype_bytes if pool_dtype_bytes is None else pool_dtype_bytes)
     read = 2 * num_valid_tokens * row
-    write = 2 * num_valid_tokens * row
+    write = 2 * num_valid_tokens * prow
     slots = num_tokens * SLOT_BYTES
     return {"read": read, "write": write, "slots": slots, "total": read + write + slots}
 

@@ -710,9 +710,9 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
 // One wavefront per (sequence, head): rows of empty or invalid contexts, and
 // the LSE merge of rows cut over several workers.  Lane j reads the j-th
 // worker's (m, l); the merged row then needs one pass.
-template <int DT, int D>
+// TC is the chunk length of the split pass that wrote the partials.
+template <int DT, int D, int TC>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
-  constexpr int TC = Geo<D>::TC;
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= (int64_t)a.S * a.H) return;
@@ -869,8 +869,14 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
     const int64_t segs = (int64_t)a.S * a.H;
     const int grid = (int)((segs + 3) / 4);
 #define PKV_BMERGE(DT, DD) \
-  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD>), dim3(grid), dim3(256), 0, stream, a)
-    if (a.dtype == DT_F16) {
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC>), dim3(grid), dim3(256), 0, stream, a)
+    if (a.fp8) {
+      if (a.D != 128 || fp8_chunk_tokens() != 32) return hipErrorInvalidValue;
+      if (a.dtype == DT_F16)
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32>), dim3(grid), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32>), dim3(grid), dim3(256), 0, stream, a);
+    } else if (a.dtype == DT_F16) {
       if (a.D == 64) PKV_BMERGE(DT_F16, 64);
       else PKV_BMERGE(DT_F16, 128);
     } else {

@@ -1,0 +1,416 @@
+// FP8 KV cache for gfx950: the K and V pools hold OCP e4m3 codes (one byte per
+// element) with one float32 scale per pool; a stored code c means the value
+// e4m3(c) * scale.  Half the bytes of a 16-bit cache for the same tokens.
+//
+//  * Append (the cache append of "PagedAttention 完全拆解", 原理详解（三）, item
+//    1, with a quantising store): code = e4m3(x * (1 / scale)), the product
+//    rounded in float32, saturated to +-448, then rounded to the nearest e4m3
+//    value, ties to even (v_cvt_pk_fp8_f32); NaN stays NaN.
+//  * Decode (the attention equation of the same page, 背景): the balanced
+//    split and pipelined chunk stream of the 16-bit kernel, with 32-token
+//    chunks: 8 lanes hold a token row (16 codes each), a load instruction
+//    reads 8 whole rows (1 KiB), codes are widened with v_cvt_pk_f32_fp8 and
+//    multiplied in float32.  The K scale is folded into the score scale and
+//    the V scale applied to the weighted V sum.
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+#include "pkv_split.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kFp8Waves = PKV_DECODE_WAVES;
+constexpr int FD = 128;               // head_dim of this path
+constexpr int FLPT = 8;               // lanes per token row
+constexpr int FTPI = 64 / FLPT;       // token rows per load instruction
+constexpr int FNL = 4;                // loads per tensor per chunk
+constexpr int FTC = FNL * FTPI;       // tokens per chunk
+
+typedef float f2_t __attribute__((ext_vector_type(2)));
+
+// Four codes of a dword -> four floats.
+__device__ __forceinline__ void widen4(uint32_t w, float *f) {
+  const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
+// float -> e4m3 code: saturate to +-448 (NaN passes), round to nearest even.
+__device__ __forceinline__ float sat448(float y) { return (y != y) ? y : fminf(fmaxf(y, -448.f), 448.f); }
+
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+// One thread per 16 elements of a (token, head) row: 32 bytes of 16-bit input
+// -> 16 bytes of codes, for K and for V.
+template <int DT>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    uint8_t *__restrict__ kp, uint8_t *__restrict__ vp, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, int64_t k_stride, int64_t v_stride, const int64_t *__restrict__ slots,
+    int32_t T, int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks, float k_inv, float v_inv) {
+  const int per_row = D / 16;
+  const int64_t per_tok = (int64_t)Hkv * per_row;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * per_tok) return;
+  const int t = (int)(idx / per_tok);
+  const int r = (int)(idx - (int64_t)t * per_tok);
+  const int h = r / per_row;
+  const int piece = r - h * per_row;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * B) return;
+  const int64_t blk = slot / B;
+  const int64_t off = slot - blk * B;
+  const int64_t dst = ((blk * Hkv + h) * B + off) * D + piece * 16;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t *src = (which == 0 ? k + (int64_t)t * k_stride : v + (int64_t)t * v_stride) + h * D + piece * 16;
+    const float inv = which == 0 ? k_inv : v_inv;
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(src);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = quant4(lo16<DT>(w[2 * j]) * inv, hi16<DT>(w[2 * j]) * inv, lo16<DT>(w[2 * j + 1]) * inv,
+                    hi16<DT>(w[2 * j + 1]) * inv);
+    const u32x4 ov = {o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<u32x4 *>((which == 0 ? kp : vp) + dst) = ov;
+  }
+}
+
+template <int DT, int B>
+struct Fp8Stream {
+  static constexpr int NE = FTC >= B ? FTC / B : 1;  // table entries per chunk
+  static_assert(B % FTPI == 0, "a load must not straddle two blocks");
+
+  struct Buf {
+    u32x4 k[FNL], v[FNL];
+    u32x4 q0, q1;
+    bool bad;
+  };
+
+  const uint8_t *kp;
+  const uint8_t *vp;
+  const uint16_t *qp;
+  const int32_t *tables;
+  uint16_t *outp;
+  float *ws_m;
+  float *ws_l;
+  float *ws_o;
+  int64_t blk_stride, num_blocks;
+  int H, maxb;
+  float scale_log2, v_scale;
+  int lane, lane_off, row, qoff;
+  int64_t worker;
+  ChunkCursor<FTC> cur;
+  float qf[16];
+  float m, l, acc[16];
+  bool bad;
+
+  __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_, int lane_) {
+    kp = reinterpret_cast<const uint8_t *>(a.k_pool);
+    vp = reinterpret_cast<const uint8_t *>(a.v_pool);
+    qp = reinterpret_cast<const uint16_t *>(a.q);
+    tables = a.tables;
+    outp = reinterpret_cast<uint16_t *>(a.out);
+    ws_m = a.ws_m;
+    ws_l = a.ws_l;
+    ws_o = a.ws_o;
+    blk_stride = (int64_t)a.Hkv * B * FD;
+    num_blocks = a.num_blocks;
+    H = a.H;
+    maxb = a.maxb;
+    scale_log2 = a.scale_log2;
+    v_scale = a.v_scale;
+    lane = lane_;
+    lane_off = lane * 16;
+    row = lane / FLPT;
+    qoff = (lane % FLPT) * 16;
+    cur.init(cum_, lens_, a.S, a.H, lane_);
+  }
+
+  __device__ __forceinline__ static int first_block(int c) { return FTC >= B ? c * (FTC / B) : c / (B / FTC); }
+  __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * FTC) - 1) / B; }
+
+  __device__ __forceinline__ uint32_t load_entries(const Chunk &d) const {
+    const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
+    return (uint32_t)tables[(int64_t)d.s * maxb + lb];
+  }
+
+  __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
+    const int64_t head_base = (int64_t)d.h * B * FD;
+    bool bd = false;
+#pragma unroll
+    for (int i = 0; i < FNL; ++i) {
+      int ei, off;
+      if constexpr (FTC >= B) {
+        ei = (i * FTPI) / B;
+        off = (i * FTPI) % B;
+      } else {
+        ei = 0;
+        off = (d.c % (B / FTC)) * FTC + i * FTPI;
+      }
+      int blk = __builtin_amdgcn_readlane((int)e, ei);
+      if (blk < 0 || (int64_t)blk >= num_blocks) {
+        bd = true;
+        blk = 0;
+      }
+      const int64_t base = (int64_t)blk * blk_stride + head_base + (int64_t)off * FD;
+      b.k[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
+      b.v[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+    }
+    b.bad = bd;
+    const uint16_t *q = qp + ((int64_t)d.s * H + d.h) * FD + qoff;
+    b.q0 = *reinterpret_cast<const u32x4 *>(q);
+    b.q1 = *reinterpret_cast<const u32x4 *>(q + 8);
+  }
+
+  __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
+    if (d.c == d.cb) {
+      const uint32_t w[8] = {b.q0.x, b.q0.y, b.q0.z, b.q0.w, b.q1.x, b.q1.y, b.q1.z, b.q1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qf[2 * j] = lo16<DT>(w[j]);
+        qf[2 * j + 1] = hi16<DT>(w[j]);
+      }
+      m = kNegInf;
+      l = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+      bad = false;
+    }
+    bad = bad || b.bad;
+    const int t_lo = d.cb * FTC;
+    const int t_hi = min(d.L, d.ce * FTC);
+    float z[FNL];
+#pragma unroll
+    for (int i = 0; i < FNL; ++i) {
+      const int tok = d.c * FTC + i * FTPI + row;
+      const bool valid = tok >= t_lo && tok < t_hi;
+      const uint32_t w[4] = {b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w};
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f[4];
+        widen4(w[j], f);
+        dot = fmaf(qf[4 * j], f[0], dot);
+        dot = fmaf(qf[4 * j + 1], f[1], dot);
+        dot = fmaf(qf[4 * j + 2], f[2], dot);
+        dot = fmaf(qf[4 * j + 3], f[3], dot);
+      }
+      const float dd = group_sum<FLPT>(dot) * scale_log2;
+      z[i] = valid ? dd : kNegInf;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      b.v[i] = valid ? b.v[i] : zero;
+    }
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < FNL; ++i) mx = fmaxf(mx, z[i]);
+    const float mnew = fmaxf(m, mx);
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = fast_exp2(m - mref);
+    float pz[FNL];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < FNL; ++i) {
+      pz[i] = fast_exp2(z[i] - mref);
+      psum += pz[i];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] *= alpha;
+#pragma unroll
+    for (int i = 0; i < FNL; ++i) {
+      const uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f[4];
+        widen4(w[j], f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(pz[i], f[e], acc[4 * j + e]);
+      }
+    }
+    m = mnew;
+    if (d.c == d.ce - 1) finish_piece(d);
+  }
+
+  __device__ __forceinline__ void finish_piece(const Chunk &d) {
+#pragma unroll
+    for (int off = FLPT; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off);
+      const float l2 = __shfl_xor(l, off);
+      const float mm = fmaxf(m, m2);
+      const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
+      const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
+      l = l * f1 + l2 * f2;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float o2 = __shfl_xor(acc[j], off);
+        acc[j] = acc[j] * f1 + o2 * f2;
+      }
+      m = mm;
+    }
+    const int64_t g = (int64_t)d.s * H + d.h;
+    if (lane < FLPT) {
+      const float nanv = bad ? __builtin_nanf("") : 0.f;
+      if (d.cb == 0 && d.ce * FTC >= d.L) {
+        const float f = v_scale / l;
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          w[j] = (uint32_t)to16<DT>(acc[2 * j] * f + nanv) | ((uint32_t)to16<DT>(acc[2 * j + 1] * f + nanv) << 16);
+        uint16_t *o = outp + g * FD + qoff;
+        *reinterpret_cast<u32x4 *>(o) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4 *>(o + 8) = u32x4{w[4], w[5], w[6], w[7]};
+      } else {
+        const int64_t u = worker + g;
+        float *o = ws_o + u * FD + qoff;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] = acc[j] * v_scale + nanv;
+        if (lane == 0) {
+          ws_m[u] = m * kLn2 + nanv;  // natural-log units
+          ws_l[u] = l + nanv;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void run(int th1, int th2, int th3) {
+    Chunk d0 = cur.produce();
+    if (!d0.valid) return;
+    int done = 0;
+    Buf ba, bb;
+    uint32_t ea = load_entries(d0);
+    Chunk d1 = cur.produce();
+    uint32_t eb = load_entries(d1);
+    load_kv(d0, ea, ba);
+    for (;;) {
+      const Chunk d2 = cur.produce();
+      ea = load_entries(d2);
+      load_kv(d1, eb, bb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d0, ba);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d1.valid) break;
+      const Chunk d3 = cur.produce();
+      eb = load_entries(d3);
+      load_kv(d2, ea, ba);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(d1, bb);
+      ++done;
+      if (done == th1) __builtin_amdgcn_s_setprio(2);
+      if (done == th2) __builtin_amdgcn_s_setprio(1);
+      if (done == th3) __builtin_amdgcn_s_setprio(0);
+      if (!d2.valid) break;
+      d0 = d2;
+      d1 = d3;
+    }
+  }
+};
+
+template <int DT, int B, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
+  using ST = Fp8Stream<DT, B>;
+  extern __shared__ int64_t lds[];
+  int64_t *cum = lds;                                         // [S + 1]
+  int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) build_cost_prefix<FTC>(a, a.H, cum, lens, lane);
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
+  }
+  const uint64_t total = uni64((uint64_t)cum[a.S]);
+  if (total == 0) return;
+  const uint64_t slice = slice_of(total, a.G);
+  const int w = blockIdx.x * NW + wave;
+  const uint64_t lo = min(total, (uint64_t)w * slice);
+  const uint64_t hi = min(total, lo + slice);
+  if (lo >= hi) return;
+  ST st;
+  st.init(a, cum, lens, lane);
+  st.worker = w;
+  st.cur.enter(lo, hi);
+  const int n = (int)(hi - lo);
+  __builtin_amdgcn_s_setprio(3);
+  st.run(n / 4, n / 2, (3 * n) / 4);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+template <int DT>
+const void *fp8_ptr(int B) {
+  switch (B) {
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves>);
+    default: return nullptr;
+  }
+}
+
+template <int DT, int B>
+hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
+                     fp8_lds_bytes(a.S), st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fp8_chunk_tokens() { return FTC; }
+
+size_t fp8_lds_bytes(int num_seqs) {
+  return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
+}
+
+const void *fp8_kernel(int dtype, int block_size) {
+  return dtype == DT_F16 ? fp8_ptr<DT_F16>(block_size) : fp8_ptr<DT_BF16>(block_size);
+}
+
+hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {
+  if (a.S == 0 || a.G == 0) return hipSuccess;
+#define PKV_F(DT)                                 \
+  switch (a.B) {                                  \
+    case 8: return launch_fp8<DT, 8>(a, stream);   \
+    case 16: return launch_fp8<DT, 16>(a, stream); \
+    case 32: return launch_fp8<DT, 32>(a, stream); \
+    case 64: return launch_fp8<DT, 64>(a, stream); \
+    default: return hipErrorInvalidValue;         \
+  }
+  if (a.dtype == DT_F16) { PKV_F(DT_F16) }
+  PKV_F(DT_BF16)
+#undef PKV_F
+}
+
+hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v, int64_t k_stride,
+                                        int64_t v_stride, const int64_t *slots, int32_t T, int32_t Hkv, int32_t B,
+                                        int32_t D, int64_t num_blocks, int dtype, float k_inv, float v_inv,
+                                        hipStream_t stream) {
+  const int64_t threads = (int64_t)T * Hkv * (D / 16);
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+#define PKV_Q(DT)                                                                                             \
+  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<DT>), dim3((unsigned)grid), dim3(256), 0, stream,           \
+                     reinterpret_cast<uint8_t *>(k_pool), reinterpret_cast<uint8_t *>(v_pool),                 \
+                     reinterpret_cast<const uint16_t *>(k), reinterpret_cast<const uint16_t *>(v), k_stride, \
+                     v_stride, slots, T, Hkv, B, D, num_blocks, k_inv, v_inv)
+  if (dtype == DT_F16) PKV_Q(DT_F16);
+  else PKV_Q(DT_BF16);
+#undef PKV_Q
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -77,19 +77,22 @@ int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
 
 // Workers (wavefronts) the balanced split launches on the current device: as
 // many as the device holds at once.  0 if the device cannot be queried.
-int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group) {
+int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
   // the fused-append instance (the larger of the two), so that the split and
   // merge passes of either entry point agree on the worker count
-  const void *k = group ? pkv::group_kernel(p->dtype, p->block_size)
-                        : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
+  const void *k = fp8     ? pkv::fp8_kernel(p->dtype, p->block_size)
+                  : group ? pkv::group_kernel(p->dtype, p->block_size)
+                          : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
   if (!k) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
-  const size_t lds =
-      align_up(group ? pkv::group_lds_bytes(num_seqs) : pkv::balanced_lds_bytes(num_seqs), 4096);
+  const size_t lds = align_up(fp8     ? pkv::fp8_lds_bytes(num_seqs)
+                              : group ? pkv::group_lds_bytes(num_seqs)
+                                      : pkv::balanced_lds_bytes(num_seqs),
+                              4096);
   const int nb = kernel_blocks_per_cu(dev, k, lds);
   if (nb <= 0) return 0;
   long long g = (long long)cus * nb * pkv::decode_waves();
@@ -105,8 +108,10 @@ struct Layout {
   size_t off_m, off_l, off_o, off_cum, bytes;
 };
 
+// fp8: e4m3 pools (head_dim 128, one query row per KV head, balanced split).
 pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks,
-                         const pkv_pool *p, int32_t partition_size, int32_t num_queries, Layout *lay) {
+                         const pkv_pool *p, int32_t partition_size, int32_t num_queries, Layout *lay,
+                         bool fp8 = false) {
   if (!p) return PKV_ERR_NULL;
   if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || num_queries < 1) return PKV_ERR_SHAPE;
@@ -117,6 +122,8 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   const int unit = partition_unit(p);
   *lay = Layout{};
   const int32_t rows = (num_heads / p->num_kv_heads) * num_queries;  // query rows per KV head
+  if (fp8 && (rows != 1 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs))
+    return PKV_ERR_UNSUPPORTED;
   if (rows > 1) {
     // several query rows per KV head: the matrix-core kernel, balanced split only
     if (rows > 16 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
@@ -140,7 +147,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   }
   if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
     // work-balanced split; the cost space (chunks) must stay far below 2^47
-    const int tc = pkv::decode_chunk_tokens(p->head_dim);
+    const int tc = fp8 ? pkv::fp8_chunk_tokens() : pkv::decode_chunk_tokens(p->head_dim);
     const int64_t row_chunks = (ctx + tc - 1) / tc;
     const double cost = (double)num_seqs * num_heads * (double)row_chunks;
     if (cost >= 1.0e12) return PKV_ERR_SHAPE;
@@ -183,10 +190,11 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
                        const int32_t *block_tables, const int32_t *context_lens, float scale,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
                        int32_t partition_size, const void *workspace, size_t workspace_bytes,
-                       bool need_inputs, pkv::DecodeParams *a, int32_t num_queries = 1) {
+                       bool need_inputs, pkv::DecodeParams *a, int32_t num_queries = 1,
+                       bool fp8 = false) {
   if (num_seqs == 0) {  // nothing to do; still validate the static arguments
     Layout lay;
-    const pkv_status st = decode_layout(0, num_heads, max_blocks, p, partition_size, num_queries, &lay);
+    const pkv_status st = decode_layout(0, num_heads, max_blocks, p, partition_size, num_queries, &lay, fp8);
     *a = pkv::DecodeParams{};
     return st;
   }
@@ -200,7 +208,7 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
     return PKV_ERR_SHAPE;
   if (!aligned(out, 16)) return PKV_ERR_SHAPE;
   Layout lay;
-  const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, num_queries, &lay);
+  const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, num_queries, &lay, fp8);
   if (st != PKV_OK) return st;
   if (lay.bytes > 0) {
     if (!workspace || workspace_bytes < lay.bytes || !aligned(workspace, kAlign))
@@ -221,11 +229,13 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
     a->ws_cum = lay.balanced ? (int64_t *)(ws + lay.off_cum) : nullptr;
   }
   if (lay.balanced) {
-    a->G = balanced_waves(p, num_seqs, lay.group);
+    a->G = balanced_waves(p, num_seqs, lay.group, fp8);
     if (a->G == 0) return PKV_ERR_HIP;
   }
   a->nq = num_queries;
   a->group = lay.group ? 1 : 0;
+  a->fp8 = fp8 ? 1 : 0;
+  a->v_scale = 1.0f;
   a->scale_log2 = scale * 1.4426950408889634f;
   a->num_blocks = p->num_blocks;
   a->S = num_seqs;
@@ -245,6 +255,7 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
 hipError_t launch_split(const pkv::DecodeParams &a, hipStream_t stream) {
+  if (a.fp8) return pkv::launch_fp8_decode(a, stream);
   return a.group ? pkv::launch_group_decode(a, stream) : pkv::launch_decode_partitions(a, stream);
 }
 
@@ -276,6 +287,8 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
   return PKV_OK;
 }
 
+// A per-pool FP8 scale: positive and finite, with a finite float32 reciprocal.
+bool fp8_scale_ok(float s) { return s > 0.f && s <= 3.0e38f && 1.0f / s > 0.f && 1.0f / s <= 3.0e38f; }
 
 }  // namespace
 
@@ -298,6 +311,11 @@ const char *pkv_status_string(int status) {
 size_t pkv_pool_bytes(const pkv_pool *p) {
   if (!pool_ok(p)) return 0;
   return (size_t)p->num_blocks * p->num_kv_heads * p->block_size * p->head_dim * 2;
+}
+
+size_t pkv_fp8_pool_bytes(const pkv_pool *p) {
+  if (!pool_ok(p)) return 0;
+  return (size_t)p->num_blocks * p->num_kv_heads * p->block_size * p->head_dim;
 }
 
 int64_t pkv_pool_index(const pkv_pool *p, int64_t block, int32_t head, int32_t offset,
@@ -475,6 +493,56 @@ pkv_status pkv_paged_attention_multi(void *out, const void *q, const void *k_poo
                                     num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, true, &a,
                                     num_queries);
   if (st != PKV_OK || num_seqs == 0) return st;
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,
+                                     int64_t k_token_stride, int64_t v_token_stride,
+                                     const int64_t *slot_mapping, int32_t num_tokens, float k_scale,
+                                     float v_scale, const pkv_pool *p, void *stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k || !v || !slot_mapping) return PKV_ERR_NULL;
+  const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
+  if (k_token_stride == 0) k_token_stride = row;
+  if (v_token_stride == 0) v_token_stride = row;
+  if (k_token_stride < row || v_token_stride < row) return PKV_ERR_SHAPE;
+  if (k_token_stride % 8 != 0 || v_token_stride % 8 != 0) return PKV_ERR_SHAPE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return PKV_ERR_SHAPE;
+  if ((int64_t)num_tokens * p->num_kv_heads * (p->head_dim / 16) > ((int64_t)1 << 40))
+    return PKV_ERR_SHAPE;
+  return hip_status(pkv::launch_reshape_and_cache_fp8(
+      k_pool, v_pool, k, v, k_token_stride, v_token_stride, slot_mapping, num_tokens, p->num_kv_heads,
+      p->block_size, p->head_dim, p->num_blocks, p->dtype, 1.0f / k_scale, 1.0f / v_scale,
+      (hipStream_t)stream));
+}
+
+size_t pkv_fp8_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                      const pkv_pool *p) {
+  Layout lay;
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, 0, 1, &lay, true) != PKV_OK) return 0;
+  return lay.bytes;
+}
+
+pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                          const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                          float k_scale, float v_scale, int32_t num_seqs, int32_t num_heads,
+                                          int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PKV_ERR_SHAPE;
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale, num_seqs,
+                                    num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, true, &a, 1,
+                                    true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

@@ -59,6 +59,11 @@ struct DecodeParams {
   // matrix-core kernel for more than one row.
   int32_t nq;
   int32_t group;
+  // FP8 pools (fp8 != 0): k_pool / v_pool hold OCP e4m3 codes, one byte per
+  // element; the K scale is folded into scale_log2 and every V sum is
+  // multiplied by v_scale.
+  int32_t fp8;
+  float v_scale;
 };
 
 int decode_waves();
@@ -76,6 +81,15 @@ const void *group_kernel(int dtype, int block_size);
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
+// FP8 (e4m3) pools, head_dim 128, one query row per KV head.
+int fp8_chunk_tokens();
+size_t fp8_lds_bytes(int num_seqs);
+const void *fp8_kernel(int dtype, int block_size);
+hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream);
+hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,
+                                        int64_t k_stride, int64_t v_stride, const int64_t *slots,
+                                        int32_t T, int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
+                                        int dtype, float k_inv, float v_inv, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, const void *v,
                                     int64_t k_stride, int64_t v_stride, const int64_t *slots,

@@ -292,6 +292,43 @@ def normal_16bit(shape, dtype: str, device, seed: int, chunk_elems: int = 1 << 2
     return out
 
 
+FP8_NAN = 0x7F  # an e4m3 NaN code (exponent and mantissa all ones)
+
+
+def random_e4m3(shape, device, seed: int, exp_lo: int = 8, exp_hi: int = 14, chunk_elems: int = 1 << 27):
+    """Random e4m3 codes (torch.uint8): uniform sign and mantissa, biased
+    exponent uniform in [exp_lo, exp_hi] (0 gives subnormals; the default
+    spreads magnitudes over 2 .. 240, about the range of N(0, 1) data
+    quantised with a scale near 1/60); never a NaN code."""
+    import torch
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    flat = out.view(-1)
+    g = _gen(device, seed)
+    n = flat.numel()
+    for lo in range(0, n, chunk_elems):
+        hi = min(n, lo + chunk_elems)
+        bits = torch.randint(0, 256, (hi - lo,), generator=g, device=device, dtype=torch.int32)
+        e = torch.randint(exp_lo, exp_hi + 1, (hi - lo,), generator=g, device=device, dtype=torch.int32)
+        code = (bits & 0x87) | (e << 3)
+        code = torch.where((code & 0x7F) == 0x7F, code - 1, code)  # NaN -> 448
+        flat[lo:hi] = code.to(torch.uint8)
+    return out
+
+
+def make_fp8_pools(t: Tables, device="cpu", salt: int = 2, poison: bool = True, **kw):
+    """e4m3 K and V pools ``[N, H, B, D]`` (uint8 codes) with every live slot
+    drawn by ``random_e4m3`` and every other slot set to the NaN code."""
+    import torch
+    shape = (t.num_blocks, t.num_heads, t.block_size, t.head_dim)
+    k = random_e4m3(shape, device, t.seed * 16 + salt, **kw)
+    v = random_e4m3(shape, device, t.seed * 16 + salt + 1, **kw)
+    if poison:
+        dead = torch.from_numpy(~t.live_mask()).to(device)[:, None, :, None].expand(shape)
+        for pool in (k, v):
+            pool.masked_fill_(dead, FP8_NAN)
+    return k, v
+
+
 def make_query(t: Tables, device="cpu", salt: int = 1):
     return normal_16bit((t.num_seqs, t.num_heads, t.head_dim), t.dtype, device, t.seed * 16 + salt)
 
