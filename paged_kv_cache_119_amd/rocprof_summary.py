@@ -72,7 +72,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--write", default=None, help="WRITE_SIZE run (omit to report fetched bytes only)")
     ap.add_argument("--config", default="opt13b")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--separate-append", action="store_true")
@@ -81,14 +81,17 @@ def main(argv=None) -> int:
     ap.add_argument("--command", action="append", required=True,
                     help="a command the profiles were taken with (repeat for each run)")
     ap.add_argument("--out", required=True)
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json"))
+    ap.add_argument("--fetch-scale", type=float, default=None,
+                    help="FETCH_SIZE scale measured in another run (when this run has no calibration copy)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json"),
+                    help="record for bench.py's traffic field ('none': write no record)")
     args = ap.parse_args(argv)
 
     stats = kernel_stats(args.trace)
     fetch = counter_means(args.fetch)
-    write = counter_means(args.write)
-    fs = copy_scale(fetch, "FETCH_SIZE")
-    ws = copy_scale(write, "WRITE_SIZE")
+    write = counter_means(args.write) if args.write else {}
+    fs = args.fetch_scale if args.fetch_scale is not None else copy_scale(fetch, "FETCH_SIZE")
+    ws = copy_scale(write, "WRITE_SIZE") if args.write else None
 
     def per_dispatch(agg, counter, scale):
         out = {}
@@ -98,7 +101,7 @@ def main(argv=None) -> int:
         return out
 
     fb = per_dispatch(fetch, "FETCH_SIZE", fs)
-    wb = per_dispatch(write, "WRITE_SIZE", ws)
+    wb = per_dispatch(write, "WRITE_SIZE", ws) if args.write else {}
     main_k = [k for k in fb if args.kernel in k]
     if not main_k:
         raise RuntimeError(f"kernel {args.kernel} not in the counter output")
@@ -114,17 +117,30 @@ def main(argv=None) -> int:
         if "pkv" in r["name"]:
             lines.append(f"| `{r['name'][:100]}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
                          f"{r['max_us']:.2f} |")
-    lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
-              f"Scale factors from the 1 GiB device copy in the same runs: FETCH_SIZE x {fs:.4f}, "
-              f"WRITE_SIZE x {ws:.4f}.", "",
-              "| kernel | fetched MB | written MB |", "|---|---|---|"]
-    for k in sorted(fb):
-        lines.append(f"| `{k[:100]}` | {fb[k] / 1e6:.2f} | {wb.get(k, 0.0) / 1e6:.2f} |")
+    if args.write:
+        lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+                  f"Scale factors from the 1 GiB device copy in the same runs: FETCH_SIZE x {fs:.4f}, "
+                  f"WRITE_SIZE x {ws:.4f}.", "",
+                  "| kernel | fetched MB | written MB |", "|---|---|---|"]
+        for k in sorted(fb):
+            lines.append(f"| `{k[:100]}` | {fb[k] / 1e6:.2f} | {wb.get(k, 0.0) / 1e6:.2f} |")
+        what = "measured traffic"
+    else:
+        how = "given" if args.fetch_scale is not None else "from the 1 GiB device copy in the same run"
+        lines += ["", "## HBM bytes fetched per dispatch (rocprofv3 --pmc FETCH_SIZE)", "",
+                  f"FETCH_SIZE scale x {fs:.4f} ({how}); no WRITE_SIZE run.", "",
+                  "| kernel | fetched MB |", "|---|---|"]
+        for k in sorted(fb):
+            lines.append(f"| `{k[:100]}` | {fb[k] / 1e6:.2f} |")
+        what = "measured fetch"
     lines += ["", f"Algorithmic bytes of one `{args.kernel}` launch: {args.algorithmic_bytes / 1e6:.2f} MB; "
-              f"measured traffic {traffic / 1e6:.2f} MB ({traffic / args.algorithmic_bytes:.3f}x).", ""]
+              f"{what} {traffic / 1e6:.2f} MB ({traffic / args.algorithmic_bytes:.3f}x).", ""]
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
+    if args.traffic_json == "none":
+        print(args.out, f"traffic {traffic / 1e6:.2f} MB")
+        return 0
     rec = {"kernel": args.kernel, "config": args.config, "partition_size": args.partition_size,
            "separate_append": args.separate_append, "kernel_hash": kernel_hash(),
            "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fb[main_k[0]]),
