@@ -55,6 +55,8 @@ def parse(argv=None):
     ap.add_argument("--op", choices=("decode", "copy_blocks", "rows"), default="decode",
                     help="decode (the hot path, default), the batched block copy of copy-on-write, or "
                          "several query rows per KV head (grouped-query heads, multi-token queries)")
+    ap.add_argument("--reuse-blocks", action="store_true",
+                    help="pass the pool's reuse hint (cached K/V loads) for batches that share blocks")
     ap.add_argument("--kv", choices=("16bit", "fp8"), default="16bit",
                     help="--op decode: pool element type (fp8: e4m3 codes with per-pool scales)")
     ap.add_argument("--group", type=int, default=None,
@@ -127,7 +129,7 @@ def main(argv=None) -> int:
         vnew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 10)
         t.seed -= 1000 * r
         reps.append((kp, vp, q, knew, vnew, torch.empty_like(q)))
-    desc = pool_desc_of(reps[0][0])
+    desc = pool_desc_of(reps[0][0], args.reuse_blocks)
     P = pkv.decode_partition_size(S, H, t.max_blocks, reps[0][0], args.partition_size)
     ws = pkv.alloc_workspace(S, H, t.max_blocks, reps[0][0], args.partition_size)
     ws_bytes = ws.numel()
@@ -247,7 +249,8 @@ def main(argv=None) -> int:
         "config": {"workload": f"{args.config}: {S} seqs x {H} heads x {D}, B={B}, "
                                f"context_len {describe_lengths(t)}, one decode step: append of {S} tokens + "
                                f"attention ({'separate append' if args.separate_append else 'append fused'})"
-                               + (", prefix blocks duplicated per sibling" if dup is not None else ""),
+                               + (", prefix blocks duplicated per sibling" if dup is not None else "")
+                               + (", reuse hint (cached K/V loads)" if args.reuse_blocks else ""),
                    "global_batch": S, "kv_tokens": t.kv_tokens(), "block_size": B, "partition_size": P,
                    "pool_blocks": t.num_blocks, "replicas": args.replicas, "parallelism": "none (1 GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -290,7 +293,7 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
         shape = (S, H, D) if Q == 1 else (S, Q, H, D)
         q = normal_16bit(shape, t.dtype, dev, t.seed * 16 + 20 + r)
         reps.append((kp, vp, q, torch.empty_like(q)))
-    desc = pkv.pool_desc_of(reps[0][0])
+    desc = pkv.pool_desc_of(reps[0][0], args.reuse_blocks)
     dref = ctypes.byref(desc)
     stream = torch.cuda.current_stream(dev)
     sp = int(stream.cuda_stream)
@@ -393,7 +396,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
         vnew = normal_16bit((S, H, D), t.dtype, dev, t.seed * 16 + 10)
         t.seed -= 1000 * r
         reps.append((kp, vp, q, knew, vnew, torch.empty_like(q)))
-    desc = pkv.make_pool_desc(t.num_blocks, B, H, D, t.dtype)
+    desc = pkv.make_pool_desc(t.num_blocks, B, H, D, t.dtype, args.reuse_blocks)
     dref = ctypes.byref(desc)
     wsb = pkv.fp8_decode_workspace_bytes(S, H, t.max_blocks, reps[0][0], t.dtype)
     if wsb == 0:

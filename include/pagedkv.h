@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKV_VERSION 1
+#define PKV_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -71,6 +71,18 @@ typedef enum {
 
 typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/*
+ * Pool flags (pkv_pool.flags), a hint for the decode calls' K/V reads:
+ *   0               every pool block is read once per call (the usual decode
+ *                   batch): K/V rows are read with non-temporal loads, which
+ *                   stream past the caches;
+ *   PKV_POOL_REUSE  blocks are read by several sequences in one call (shared
+ *                   prompt prefixes, parallel samples): ordinary cached
+ *                   loads, so later readers can hit the last-level cache.
+ * The flag changes speed only, never results.  Other bits: PKV_ERR_UNSUPPORTED.
+ */
+#define PKV_POOL_REUSE 1
+
 /* Shape of one K pool (the V pool has the same shape). */
 typedef struct {
   int64_t num_blocks;   /* N >= 1                                   */
@@ -78,6 +90,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv >= 1                                 */
   int32_t head_dim;     /* D: 64 or 128                             */
   int32_t dtype;        /* pkv_dtype                                */
+  int32_t flags;        /* 0 or PKV_POOL_REUSE                      */
 } pkv_pool;
 
 /* Library ABI version (PKV_VERSION). */

@@ -54,7 +54,10 @@ class PagedKVError(RuntimeError):
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+POOL_REUSE = 1  # pkv_pool.flags: blocks read by several sequences in one call
 
 
 _lib = None
@@ -122,8 +125,10 @@ def _check(status: int, what: str) -> None:
         raise PagedKVError(status, what)
 
 
-def make_pool_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: str) -> PoolDesc:
-    return PoolDesc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim), DTYPE_CODES[dtype])
+def make_pool_desc(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: str,
+                   reuse_blocks: bool = False) -> PoolDesc:
+    return PoolDesc(int(num_blocks), int(block_size), int(num_kv_heads), int(head_dim), DTYPE_CODES[dtype],
+                    POOL_REUSE if reuse_blocks else 0)
 
 
 # ---------------------------------------------------------------------------
@@ -165,17 +170,17 @@ def _stream_ptr(device) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
-def pool_desc_of(k_pool) -> PoolDesc:
+def pool_desc_of(k_pool, reuse_blocks: bool = False) -> PoolDesc:
     N, H, B, D = (int(x) for x in k_pool.shape)
-    return make_pool_desc(N, B, H, D, _dtype_name(k_pool))
+    return make_pool_desc(N, B, H, D, _dtype_name(k_pool), reuse_blocks)
 
 
-def _check_pools(k_pool, v_pool):
+def _check_pools(k_pool, v_pool, reuse_blocks=False):
     _need(k_pool, "k_pool", ndim=4)
     _need(v_pool, "v_pool", dtype=k_pool.dtype, ndim=4, device=k_pool.device)
     if k_pool.shape != v_pool.shape:
         raise ValueError(f"k_pool {tuple(k_pool.shape)} and v_pool {tuple(v_pool.shape)} differ")
-    return pool_desc_of(k_pool)
+    return pool_desc_of(k_pool, reuse_blocks)
 
 
 # ---------------------------------------------------------------------------
@@ -281,9 +286,9 @@ def alloc_workspace(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_s
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=k_pool.device)
 
 
-def _decode_args(q, k_pool, v_pool, block_tables, context_lens, out):
+def _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks=False):
     torch = _torch()
-    desc = _check_pools(k_pool, v_pool)
+    desc = _check_pools(k_pool, v_pool, reuse_blocks)
     dev = k_pool.device
     _need(q, "q", dtype=k_pool.dtype, ndim=3, device=dev)
     S, H, D = (int(x) for x in q.shape)
@@ -311,10 +316,12 @@ def _workspace(ws, S, H, maxb, k_pool, partition_size):
 
 
 def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
-                           partition_size=0, workspace=None):
-    """Single-query decode attention over paged K/V; returns ``out`` [S, H, D]."""
+                           partition_size=0, workspace=None, reuse_blocks=False):
+    """Single-query decode attention over paged K/V; returns ``out`` [S, H, D].
+    ``reuse_blocks``: the batch reads some blocks more than once (shared
+    prefixes); K/V reads then stay cacheable (speed only)."""
     lib = load_library()
-    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
     ws_ptr, ws_bytes = _workspace(workspace, S, H, maxb, k_pool, partition_size)
     st = lib.pkv_paged_attention_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                         block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H,
@@ -330,13 +337,14 @@ def multi_workspace_bytes(num_seqs, num_queries, num_heads, max_blocks_per_seq, 
                                                         int(max_blocks_per_seq), ctypes.byref(desc)))
 
 
-def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, workspace=None):
+def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, workspace=None,
+                          reuse_blocks=False):
     """Several query tokens per sequence over paged K/V: ``q`` is [S, Q, H, D];
     query i of sequence s sits at position context_lens[s] - Q + i and attends
     causally.  Returns ``out`` [S, Q, H, D]."""
     torch = _torch()
     lib = load_library()
-    desc = _check_pools(k_pool, v_pool)
+    desc = _check_pools(k_pool, v_pool, reuse_blocks)
     dev = k_pool.device
     _need(q, "q", dtype=k_pool.dtype, ndim=4, device=dev)
     S, Q, H, D = (int(x) for x in q.shape)
@@ -367,7 +375,7 @@ def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, 
 # FP8 (e4m3) pools: one byte per element, one float32 scale per pool
 # ---------------------------------------------------------------------------
 
-def _fp8_pools(k_pool, v_pool, dtype_name):
+def _fp8_pools(k_pool, v_pool, dtype_name, reuse_blocks=False):
     torch = _torch()
     _need(k_pool, "k_pool", ndim=4)
     _need(v_pool, "v_pool", ndim=4, device=k_pool.device)
@@ -377,7 +385,7 @@ def _fp8_pools(k_pool, v_pool, dtype_name):
     if k_pool.shape != v_pool.shape:
         raise ValueError(f"k_pool {tuple(k_pool.shape)} and v_pool {tuple(v_pool.shape)} differ")
     N, H, B, D = (int(x) for x in k_pool.shape)
-    return make_pool_desc(N, B, H, D, dtype_name)
+    return make_pool_desc(N, B, H, D, dtype_name, reuse_blocks)
 
 
 def fp8_pool_bytes(num_blocks, block_size, num_kv_heads, head_dim) -> int:
@@ -420,13 +428,13 @@ def fp8_decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, 
 
 
 def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out=None,
-                               workspace=None):
+                               workspace=None, reuse_blocks=False):
     """Single-query decode attention over e4m3 pools (K element = code value *
     k_scale, V element = code value * v_scale); ``q`` and ``out`` [S, H, D]
     16-bit."""
     torch = _torch()
     lib = load_library()
-    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q))
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q), reuse_blocks)
     dev = k_pool.device
     _need(q, "q", ndim=3, device=dev)
     S, H, D = (int(x) for x in q.shape)
@@ -455,12 +463,12 @@ def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, sc
 
 
 def paged_attention_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, out=None,
-                                  partition_size=0, workspace=None):
+                                  partition_size=0, workspace=None, reuse_blocks=False):
     """One decode step with the append fused in: row s of k_new / v_new
     ([S, Hkv, D]) becomes token context_lens[s] - 1 of sequence s (written to
     its pool slot), then attention runs over the paged K/V."""
     lib = load_library()
-    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if t.dtype != k_pool.dtype or t.device != k_pool.device:
             raise TypeError(f"{name} must be a {k_pool.dtype} tensor on {k_pool.device}")
@@ -481,10 +489,10 @@ def paged_attention_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables,
 
 
 def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
-                      partition_size=0):
+                      partition_size=0, reuse_blocks=False):
     """The partition pass alone (see pkv_decode_partitions)."""
     lib = load_library()
-    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out)
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
     ws_ptr, ws_bytes = _workspace(workspace, S, H, maxb, k_pool, partition_size)
     st = lib.pkv_decode_partitions(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                    block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H, maxb,

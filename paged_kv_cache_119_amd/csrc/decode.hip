@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // priority as it progresses through its slice, so wavefronts that share a
 // SIMD finish together instead of in order of age.
 
-template <int DT, int D, int B, bool APP>
+template <int DT, int D, int B, bool APP, bool NT>
 struct Stream {
   using G = Geo<D>;
   static constexpr int LPT = G::LPT, TPI = G::TPI, NL = G::NL, TC = G::TC;
@@ -477,9 +477,12 @@ struct Stream {
   }
 
   // Stage 2: the K/V rows of chunk d, its query row and (fused append) the
-  // new-token rows of its row.
+  // new-token rows of its row.  Lanes of tokens past the context read the
+  // row of token L - 1 instead (same cache lines as a valid row: the unused
+  // tail of the last block costs no HBM traffic); their values are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     const int64_t head_base = (int64_t)d.h * B * D;
+    const int tail_off = ((d.L - 1) % B) * D + qoff;
     bool bd = false;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -496,9 +499,10 @@ struct Stream {
         bd = true;
         blk = 0;
       }
-      const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
-      b.k[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
-      b.v[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+      const int64_t base = (int64_t)blk * blk_stride + head_base;
+      const int lo = (d.c * TC + i * TPI + row < d.L) ? off * D + lane_off : tail_off;
+      b.k[i] = ld_kv<NT>(kp + base + lo);
+      b.v[i] = ld_kv<NT>(vp + base + lo);
     }
     b.bad = bd;
     // Issued for every chunk (an L2 hit after the first), so every chunk
@@ -670,9 +674,9 @@ struct Stream {
   }
 };
 
-template <int DT, int D, int B, int NW, bool APP>
+template <int DT, int D, int B, int NW, bool APP, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a) {
-  using ST = Stream<DT, D, B, APP>;
+  using ST = Stream<DT, D, B, APP, NT>;
   constexpr int TC = ST::TC;
 
   extern __shared__ int64_t lds[];
@@ -796,22 +800,31 @@ struct PartitionsF {
 
 template <int DT, int D, int B>
 struct BalancedF {
+  template <bool APP, bool NT>
+  static void go(const DecodeParams &a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, APP, NT>), dim3(a.G / kNumWaves),
+                       dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
+  }
   static hipError_t call(const DecodeParams &a, hipStream_t st) {
-    if (a.append)
-      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, true>), dim3(a.G / kNumWaves),
-                         dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
-    else
-      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, false>), dim3(a.G / kNumWaves),
-                         dim3(kNumWaves * 64), balanced_lds_bytes(a.S), st, a);
+    if (a.append) {
+      if (a.stream_kv) go<true, true>(a, st);
+      else go<true, false>(a, st);
+    } else {
+      if (a.stream_kv) go<false, true>(a, st);
+      else go<false, false>(a, st);
+    }
     return hipGetLastError();
   }
 };
 
 template <int DT, int D, int B>
 struct BalancedPtrF {
-  static const void *call(int append) {
-    return append ? reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, true>)
-                  : reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false>);
+  static const void *call(int append, int nt) {
+    if (append)
+      return nt ? reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, true, true>)
+                : reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, true, false>);
+    return nt ? reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false, true>)
+              : reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false, false>);
   }
 };
 
@@ -849,8 +862,8 @@ size_t balanced_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *balanced_kernel(int dtype, int head_dim, int block_size, int append) {
-  return dispatch<BalancedPtrF, const void *>(dtype, head_dim, block_size, nullptr, append);
+const void *balanced_kernel(int dtype, int head_dim, int block_size, int append, int nt) {
+  return dispatch<BalancedPtrF, const void *>(dtype, head_dim, block_size, nullptr, append, nt);
 }
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream) {

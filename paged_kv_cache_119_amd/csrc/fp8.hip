@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   }
 }
 
-template <int DT, int B>
+template <int DT, int B, bool NT>
 struct Fp8Stream {
   static constexpr int NE = FTC >= B ? FTC / B : 1;  // table entries per chunk
   static_assert(B % FTPI == 0, "a load must not straddle two blocks");
@@ -145,8 +145,11 @@ struct Fp8Stream {
     return (uint32_t)tables[(int64_t)d.s * maxb + lb];
   }
 
+  // Tokens past the context read the row of token L - 1 instead (cache lines
+  // already fetched); they are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     const int64_t head_base = (int64_t)d.h * B * FD;
+    const int tail_off = ((d.L - 1) % B) * FD + qoff;
     bool bd = false;
 #pragma unroll
     for (int i = 0; i < FNL; ++i) {
@@ -163,9 +166,10 @@ struct Fp8Stream {
         bd = true;
         blk = 0;
       }
-      const int64_t base = (int64_t)blk * blk_stride + head_base + (int64_t)off * FD;
-      b.k[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
-      b.v[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+      const int64_t base = (int64_t)blk * blk_stride + head_base;
+      const int lo = (d.c * FTC + i * FTPI + row < d.L) ? off * FD + lane_off : tail_off;
+      b.k[i] = ld_kv<NT>(kp + base + lo);
+      b.v[i] = ld_kv<NT>(vp + base + lo);
     }
     b.bad = bd;
     const uint16_t *q = qp + ((int64_t)d.s * H + d.h) * FD + qoff;
@@ -319,9 +323,9 @@ struct Fp8Stream {
   }
 };
 
-template <int DT, int B, int NW>
+template <int DT, int B, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
-  using ST = Fp8Stream<DT, B>;
+  using ST = Fp8Stream<DT, B, NT>;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -350,21 +354,25 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int DT>
+template <int DT, bool NT>
 const void *fp8_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves>);
-    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves>);
-    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves>);
-    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves>);
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT>);
     default: return nullptr;
   }
 }
 
 template <int DT, int B>
 hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
-                     fp8_lds_bytes(a.S), st, a);
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
+                       fp8_lds_bytes(a.S), st, a);
+  else
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false>), dim3(a.G / kFp8Waves),
+                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
   return hipGetLastError();
 }
 
@@ -376,8 +384,9 @@ size_t fp8_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *fp8_kernel(int dtype, int block_size) {
-  return dtype == DT_F16 ? fp8_ptr<DT_F16>(block_size) : fp8_ptr<DT_BF16>(block_size);
+const void *fp8_kernel(int dtype, int block_size, int nt) {
+  if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true>(block_size) : fp8_ptr<DT_BF16, true>(block_size);
+  return dtype == DT_F16 ? fp8_ptr<DT_F16, false>(block_size) : fp8_ptr<DT_BF16, false>(block_size);
 }
 
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {

@@ -84,7 +84,7 @@ __device__ __forceinline__ f4_t mfma_pv(uint32_t v01, uint32_t v23, uint32_t p01
   }
 }
 
-template <int DT, int B>
+template <int DT, int B, bool NT>
 struct GroupStream {
   static constexpr int NE = GTC >= B ? GTC / B : 1;  // table entries per chunk
 
@@ -169,15 +169,19 @@ struct GroupStream {
 
   // Stage 2: K rows (token r), V rows (tokens 4g .. 4g+3) and the query rows
   // of chunk d; the same loads for every chunk.
+  // Tokens past the context read the row of token L - 1 instead (cache
+  // lines already fetched: the unused tail of the last block costs no HBM
+  // traffic); they are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     bool bd = false;
-    const int64_t kb = token_base(d, e, r, bd) + 8 * g;
+    const int last = d.L - 1 - d.c * GTC;  // token L - 1 relative to the chunk
+    const int64_t kb = token_base(d, e, min(r, last), bd) + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b.k[j] = *reinterpret_cast<const u32x4 *>(kp + kb + 32 * j);
+    for (int j = 0; j < 4; ++j) b.k[j] = ld_kv<NT>(kp + kb + 32 * j);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int64_t vb = token_base(d, e, 4 * g + t, bd) + 8 * r;
-      b.v[t] = *reinterpret_cast<const u32x4 *>(vp + vb);
+      const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * r;
+      b.v[t] = ld_kv<NT>(vp + vb);
     }
     b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
     // query row r of this KV head (rows >= M read row 0 and are zeroed)
@@ -325,9 +329,9 @@ struct GroupStream {
   }
 };
 
-template <int DT, int B, int NW>
+template <int DT, int B, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
-  using ST = GroupStream<DT, B>;
+  using ST = GroupStream<DT, B, NT>;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -418,18 +422,22 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
 
 template <int DT, int B>
 hipError_t launch_group(const DecodeParams &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves>), dim3(a.G / kGroupWaves), dim3(kGroupWaves * 64),
-                     group_lds_bytes(a.S), st, a);
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, true>), dim3(a.G / kGroupWaves),
+                       dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
+  else
+    hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, false>), dim3(a.G / kGroupWaves),
+                       dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool NT>
 const void *group_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves>);
-    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves>);
-    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves>);
-    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves>);
+    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves, NT>);
+    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves, NT>);
+    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves, NT>);
+    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves, NT>);
     default: return nullptr;
   }
 }
@@ -440,8 +448,9 @@ size_t group_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *group_kernel(int dtype, int block_size) {
-  return dtype == DT_F16 ? group_ptr<DT_F16>(block_size) : group_ptr<DT_BF16>(block_size);
+const void *group_kernel(int dtype, int block_size, int nt) {
+  if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true>(block_size) : group_ptr<DT_BF16, true>(block_size);
+  return dtype == DT_F16 ? group_ptr<DT_F16, false>(block_size) : group_ptr<DT_BF16, false>(block_size);
 }
 
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream) {

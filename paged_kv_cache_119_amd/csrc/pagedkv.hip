@@ -24,6 +24,7 @@ bool pool_ok(const pkv_pool *p) {
   if (p->num_kv_heads < 1) return false;
   if (p->head_dim != 64 && p->head_dim != 128) return false;
   if (p->dtype != PKV_F16 && p->dtype != PKV_BF16) return false;
+  if ((p->flags & ~PKV_POOL_REUSE) != 0) return false;
   // every element index must fit in int64 (and slot numbers N * B as well)
   const double elems = (double)p->num_blocks * p->num_kv_heads * p->block_size * p->head_dim;
   return elems < 9.0e18;
@@ -82,19 +83,24 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
-  // the fused-append instance (the larger of the two), so that the split and
-  // merge passes of either entry point agree on the worker count
-  const void *k = fp8     ? pkv::fp8_kernel(p->dtype, p->block_size)
-                  : group ? pkv::group_kernel(p->dtype, p->block_size)
-                          : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1);
-  if (!k) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
   const size_t lds = align_up(fp8     ? pkv::fp8_lds_bytes(num_seqs)
                               : group ? pkv::group_lds_bytes(num_seqs)
                                       : pkv::balanced_lds_bytes(num_seqs),
                               4096);
-  const int nb = kernel_blocks_per_cu(dev, k, lds);
-  if (nb <= 0) return 0;
+  // the smallest occupancy over the instances a call may launch (fused append
+  // or not, streamed or cached K/V loads), so that the split and merge passes
+  // agree on the worker count whatever the entry point and pool flags
+  int nb = 1 << 30;
+  for (int nt = 0; nt < 2; ++nt) {
+    const void *k = fp8     ? pkv::fp8_kernel(p->dtype, p->block_size, nt)
+                    : group ? pkv::group_kernel(p->dtype, p->block_size, nt)
+                            : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1, nt);
+    if (!k) return 0;
+    const int b = kernel_blocks_per_cu(dev, k, lds);
+    if (b <= 0) return 0;
+    nb = b < nb ? b : nb;
+  }
   long long g = (long long)cus * nb * pkv::decode_waves();
   if (g > pkv::kMaxWorkers) g = pkv::kMaxWorkers / pkv::decode_waves() * pkv::decode_waves();
   return (int)g;
@@ -236,6 +242,7 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   a->group = lay.group ? 1 : 0;
   a->fp8 = fp8 ? 1 : 0;
   a->v_scale = 1.0f;
+  a->stream_kv = (p->flags & PKV_POOL_REUSE) ? 0 : 1;
   a->scale_log2 = scale * 1.4426950408889634f;
   a->num_blocks = p->num_blocks;
   a->S = num_seqs;

@@ -105,6 +105,16 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// A 16-byte piece of a K/V row, read once per call.  NT: a non-temporal
+// load (the line is streamed past the caches and does not displace reused
+// data); else an ordinary cached load, for pools whose blocks are read more
+// than once in a call (shared prefixes).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_kv(const void *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  else return *reinterpret_cast<const u32x4 *>(p);
+}
+
 // 2^x on the hardware unit (v_exp_f32); 2^0 is exactly 1 and 2^-inf is 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

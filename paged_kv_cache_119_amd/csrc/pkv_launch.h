@@ -64,6 +64,9 @@ struct DecodeParams {
   // multiplied by v_scale.
   int32_t fp8;
   float v_scale;
+  // 1: K/V loads of the stream kernels are non-temporal (blocks read once
+  // per call); 0: ordinary cached loads (blocks shared between sequences).
+  int32_t stream_kv;
 };
 
 int decode_waves();
@@ -71,20 +74,21 @@ int decode_waves();
 int decode_chunk_tokens(int head_dim);
 // Dynamic LDS of the balanced kernel for num_seqs sequences.
 size_t balanced_lds_bytes(int num_seqs);
-// The balanced kernel instance for (dtype, D, B, append), for occupancy queries.
-const void *balanced_kernel(int dtype, int head_dim, int block_size, int append);
+// The balanced kernel instance for (dtype, D, B, append, non-temporal K/V
+// loads), for occupancy queries.
+const void *balanced_kernel(int dtype, int head_dim, int block_size, int append, int nt);
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
 // Several query rows per KV head (grouped-query heads, multi-token queries).
 size_t group_lds_bytes(int num_seqs);
-const void *group_kernel(int dtype, int block_size);
+const void *group_kernel(int dtype, int block_size, int nt);
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
 // FP8 (e4m3) pools, head_dim 128, one query row per KV head.
 int fp8_chunk_tokens();
 size_t fp8_lds_bytes(int num_seqs);
-const void *fp8_kernel(int dtype, int block_size);
+const void *fp8_kernel(int dtype, int block_size, int nt);
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,
                                         int64_t k_stride, int64_t v_stride, const int64_t *slots,

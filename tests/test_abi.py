@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert pkv.version() == 1
+    assert pkv.version() == 2
     for code in range(6):
         assert len(pkv.status_string(code)) > 0
     assert pkv.status_string(99) == "unknown status"
@@ -148,6 +148,22 @@ def test_append_validation(lib):
     assert lib.pkv_slot_mapping(nul, nul, 4, 8, nul, nul, 0, ctypes.byref(d), nul) == 0
     assert lib.pkv_slot_mapping(nul, nul, 4, 8, nul, nul, 3, ctypes.byref(d), nul) == 1
     assert lib.pkv_slot_mapping(fake, fake, 4, 0, fake, fake, 3, ctypes.byref(d), nul) == 2
+
+
+def test_pool_flags(lib):
+    """Only PKV_POOL_REUSE is a valid pool flag; it changes no size."""
+    d = _desc()
+    r = pkv.make_pool_desc(100, 16, 4, 128, "f16", reuse_blocks=True)
+    assert r.flags == 1
+    assert lib.pkv_pool_bytes(ctypes.byref(r)) == lib.pkv_pool_bytes(ctypes.byref(d))
+    assert lib.pkv_decode_workspace_bytes(64, 4, 128, ctypes.byref(r), 0) == \
+        lib.pkv_decode_workspace_bytes(64, 4, 128, ctypes.byref(d), 0)
+    bad = _desc()
+    bad.flags = 2
+    assert lib.pkv_pool_bytes(ctypes.byref(bad)) == 0
+    nul = None
+    assert lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, ctypes.byref(bad), 0,
+                                          nul, 0, nul) == 3
 
 
 def test_fp8_sizes_and_validation(lib):
