@@ -371,8 +371,10 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
 
 def bench_fp8(args, t, pkv, lib, dev) -> int:
     """Decode over an e4m3 KV cache: one step = the quantising append of the
-    batch's new tokens (slot mapping + pkv_reshape_and_cache_fp8) and
-    pkv_paged_attention_decode_fp8 (split pass + merge pass).  The roofline
+    batch's new tokens and the attention -- by default one
+    pkv_paged_attention_decode_append_fp8 call (split pass with the append
+    fused in + merge pass); with --separate-append, slot mapping +
+    pkv_reshape_and_cache_fp8 + pkv_paged_attention_decode_fp8.  The roofline
     times the decode call (both of its launches) with HIP events."""
     import numpy as np
     import torch
@@ -414,17 +416,24 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
 
     def step(i, ev=None):
         kp, vp, q, knew, vnew, out = reps[i % len(reps)]
-        check(lib.pkv_slot_mapping(slots.data_ptr(), tab.data_ptr(), S, t.max_blocks, seq.data_ptr(),
-                                   pos.data_ptr(), S, dref, sp), "slot_mapping")
-        check(lib.pkv_reshape_and_cache_fp8(kp.data_ptr(), vp.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0, 0,
-                                            slots.data_ptr(), S, ctypes.c_float(ks), ctypes.c_float(vs), dref, sp),
-              "reshape_and_cache_fp8")
+        if args.separate_append:
+            check(lib.pkv_slot_mapping(slots.data_ptr(), tab.data_ptr(), S, t.max_blocks, seq.data_ptr(),
+                                       pos.data_ptr(), S, dref, sp), "slot_mapping")
+            check(lib.pkv_reshape_and_cache_fp8(kp.data_ptr(), vp.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0,
+                                                0, slots.data_ptr(), S, ctypes.c_float(ks), ctypes.c_float(vs), dref,
+                                                sp), "reshape_and_cache_fp8")
         if ev is not None:
             ev[0].record(stream)
-        check(lib.pkv_paged_attention_decode_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
-                                                 tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale),
-                                                 ctypes.c_float(ks), ctypes.c_float(vs), S, H, t.max_blocks, dref,
-                                                 ws.data_ptr(), wsb, sp), "paged_attention_decode_fp8")
+        if args.separate_append:
+            check(lib.pkv_paged_attention_decode_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                     tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale),
+                                                     ctypes.c_float(ks), ctypes.c_float(vs), S, H, t.max_blocks,
+                                                     dref, ws.data_ptr(), wsb, sp), "paged_attention_decode_fp8")
+        else:
+            check(lib.pkv_paged_attention_decode_append_fp8(
+                out.data_ptr(), q.data_ptr(), knew.data_ptr(), vnew.data_ptr(), 0, kp.data_ptr(), vp.data_ptr(),
+                tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale), ctypes.c_float(ks), ctypes.c_float(vs),
+                S, H, t.max_blocks, dref, ws.data_ptr(), wsb, sp), "paged_attention_decode_append_fp8")
         if ev is not None:
             ev[1].record(stream)
 
@@ -446,10 +455,16 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
     assert torch.isfinite(reps[0][5].float()).all().item(), "non-finite output"
 
     dec = acc.decode_bytes(t.context_lens, H, D, 2, B, kv_dtype_bytes=1)
-    app = acc.append_bytes(S, S, H, D, 2, pool_dtype_bytes=1)
-    step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+    if args.separate_append:
+        app = acc.append_bytes(S, S, H, D, 2, pool_dtype_bytes=1)
+        step_bytes = dec["total"] + app["total"] + acc.slot_mapping_bytes(S)
+        kern_bytes = dec["total"]
+    else:
+        # the new rows are read once (16-bit) and written once (codes); their
+        # codes are counted in the KV bytes
+        step_bytes = kern_bytes = dec["total"] + 2 * S * H * D * 2
     kern_mean_ms = float(np.mean(kern_ms))
-    achieved = dec["total"] / (kern_mean_ms * 1e-3) / 1e9
+    achieved = kern_bytes / (kern_mean_ms * 1e-3) / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline_fp8(t, reps[0], ks, vs, args.cpu_budget_s)
     line = {
         "metric": "paged decode attention over an FP8 (e4m3) KV cache: achieved HBM GB/s + KV tokens/s",
@@ -459,14 +474,16 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {S} seqs x {H} heads x {D}, B={B}, context_len "
                                f"{describe_lengths(t)}, e4m3 pools (scales 1/60), one decode step: quantising "
-                               f"append of {S} tokens + attention",
+                               f"append of {S} tokens + attention "
+                               f"({'separate append' if args.separate_append else 'append fused'})",
                    "global_batch": S, "kv_tokens": t.kv_tokens(), "block_size": B, "pool_blocks": t.num_blocks,
                    "replicas": args.replicas, "parallelism": "none (1 GPU)"},
         "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
-        "roofline": {"kernel": "decode_fp8_kernel + decode_balanced_merge_kernel", "bound": "hbm",
+        "roofline": {"kernel": "decode_fp8_kernel" + ("" if args.separate_append else " (append fused)")
+                     + " + decode_balanced_merge_kernel", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": dec["total"],
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": kern_bytes,
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2),
                      "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},

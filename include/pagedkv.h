@@ -410,6 +410,27 @@ pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *
                                           int32_t max_blocks_per_seq, const pkv_pool *p, void *workspace,
                                           size_t workspace_bytes, void *stream);
 
+/*
+ * pkv_paged_attention_decode_append_fp8 -- one decode step over e4m3 pools
+ * with the append fused in: for every sequence s with a valid context
+ * (0 < L <= max_blocks_per_seq * B), row s of k_new / v_new ([S][Hkv][D],
+ * 16-bit, token stride new_token_stride elements, 0 = Hkv * D, a multiple of
+ * 8; 16-byte aligned) is quantised exactly as pkv_reshape_and_cache_fp8 does
+ * and written to the slot of token L - 1; then the attention of
+ * pkv_paged_attention_decode_fp8 runs, reading that token from the pool like
+ * the others (append first, then attend: "PagedAttention 完全拆解",
+ * 原理详解（一）, Figure 6 walk-through).  A needed table entry outside the
+ * pool writes nothing and gives a NaN row.  Same restrictions, scales and
+ * workspace as pkv_paged_attention_decode_fp8; one split launch (append
+ * included) and one merge launch.
+ */
+pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const void *k_new, const void *v_new,
+                                                 int64_t new_token_stride, void *k_pool, void *v_pool,
+                                                 const int32_t *block_tables, const int32_t *context_lens,
+                                                 float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                                 int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                                 void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -7,9 +7,9 @@ it plus byte accounting for the roofline.  Build the library with
 """
 
 from ._binding import (EXPORTS, LIB_PATH, POOL_REUSE, PagedKVError, PoolDesc, alloc_workspace,  # noqa: F401
-                       copy_blocks, decode_merge, decode_partition_size, decode_partitions, decode_workspace_bytes,
-                       fp8_decode_workspace_bytes, fp8_pool_bytes, load_library, make_pool_desc,
-                       multi_workspace_bytes, paged_attention_decode, paged_attention_decode_append,
-                       paged_attention_decode_fp8, paged_attention_multi, pool_bytes, pool_desc_of, pool_index,
-                       reshape_and_cache, reshape_and_cache_fp8, slot_mapping, status_string, version,
-                       workspace_views)
+                       copy_blocks, decode_merge, decode_partition_size, decode_partitions, decode_partitions_append,
+                       decode_workspace_bytes, fp8_decode_workspace_bytes, fp8_pool_bytes, load_library,
+                       make_pool_desc, multi_workspace_bytes, paged_attention_decode, paged_attention_decode_append,
+                       paged_attention_decode_append_fp8, paged_attention_decode_fp8, paged_attention_multi,
+                       pool_bytes, pool_desc_of, pool_index, reshape_and_cache, reshape_and_cache_fp8, slot_mapping,
+                       status_string, version, workspace_views)

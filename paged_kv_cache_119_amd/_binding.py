@@ -40,6 +40,7 @@ EXPORTS = (
     "pkv_reshape_and_cache_fp8",
     "pkv_fp8_decode_workspace_bytes",
     "pkv_paged_attention_decode_fp8",
+    "pkv_paged_attention_decode_append_fp8",
 )
 
 
@@ -104,6 +105,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_fp8_decode_workspace_bytes": (sz, [i32, i32, i32, pool]),
         "pkv_paged_attention_decode_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                                           ctypes.c_float, i32, i32, i32, pool, vp, sz, vp]),
+        "pkv_paged_attention_decode_append_fp8": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
+                                                                 ctypes.c_float, ctypes.c_float, i32, i32, i32, pool,
+                                                                 vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -462,6 +466,48 @@ def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, sc
     return out
 
 
+def paged_attention_decode_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, k_scale,
+                                      v_scale, out=None, workspace=None, reuse_blocks=False):
+    """One decode step over e4m3 pools with the quantising append fused in:
+    row s of k_new / v_new ([S, Hkv, D], 16-bit) becomes token
+    context_lens[s] - 1 of sequence s, then attention runs."""
+    torch = _torch()
+    lib = load_library()
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q), reuse_blocks)
+    dev = k_pool.device
+    _need(q, "q", ndim=3, device=dev)
+    S, H, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {desc.head_dim}")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("q, block_tables and context_lens disagree on the number of sequences")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != q.dtype or t.device != dev:
+            raise TypeError(f"{name} must be a {q.dtype} tensor on {dev}")
+        if t.dim() != 3 or tuple(t.shape) != (S, desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [{S}, {desc.num_kv_heads}, {desc.head_dim}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{name} must have heads and dims contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must have the same token stride")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
+    maxb = int(block_tables.shape[1])
+    if workspace is None:
+        need = fp8_decode_workspace_bytes(S, H, maxb, k_pool, _dtype_name(q))
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.pkv_paged_attention_decode_append_fp8(
+        out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), int(k_new.stride(0)) if S > 0 else 0,
+        k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+        float(k_scale), float(v_scale), S, H, maxb, ctypes.byref(desc), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    _check(st, "pkv_paged_attention_decode_append_fp8")
+    return out
+
+
 def paged_attention_decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, out=None,
                                   partition_size=0, workspace=None, reuse_blocks=False):
     """One decode step with the append fused in: row s of k_new / v_new
@@ -499,6 +545,31 @@ def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale, out,
                                    ctypes.byref(desc), int(partition_size), ws_ptr, ws_bytes,
                                    _stream_ptr(k_pool.device))
     _check(st, "pkv_decode_partitions")
+    return out
+
+
+def decode_partitions_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale, out, workspace,
+                             partition_size=0, reuse_blocks=False):
+    """The partition pass with the append fused in, alone (see
+    pkv_decode_partitions_append); decode_merge completes the step."""
+    lib = load_library()
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != k_pool.dtype or t.device != k_pool.device:
+            raise TypeError(f"{name} must be a {k_pool.dtype} tensor on {k_pool.device}")
+        if t.dim() != 3 or tuple(t.shape) != (S, desc.num_kv_heads, desc.head_dim):
+            raise ValueError(f"{name} must be [{S}, {desc.num_kv_heads}, {desc.head_dim}], got {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != desc.head_dim:
+            raise ValueError(f"{name} must have heads and dims contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must have the same token stride")
+    ws_ptr, ws_bytes = _workspace(workspace, S, H, maxb, k_pool, partition_size)
+    st = lib.pkv_decode_partitions_append(out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                          int(k_new.stride(0)) if S > 0 else 0, k_pool.data_ptr(), v_pool.data_ptr(),
+                                          block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H, maxb,
+                                          ctypes.byref(desc), int(partition_size), ws_ptr, ws_bytes,
+                                          _stream_ptr(k_pool.device))
+    _check(st, "pkv_decode_partitions_append")
     return out
 
 

@@ -6,6 +6,10 @@
 //    1, with a quantising store): code = e4m3(x * (1 / scale)), the product
 //    rounded in float32, saturated to +-448, then rounded to the nearest e4m3
 //    value, ties to even (v_cvt_pk_fp8_f32); NaN stays NaN.
+//  * Fused append (APP): before its stream starts, each wavefront quantises
+//    and writes token L - 1 of every row whose last chunk lies in its slice;
+//    the stream then reads those codes like any other (only the owner of a
+//    row's last chunk ever reads that slot).
 //  * Decode (the attention equation of the same page, 背景): the balanced
 //    split and pipelined chunk stream of the 16-bit kernel, with 32-token
 //    chunks: 8 lanes hold a token row (16 codes each), a load instruction
@@ -135,6 +139,26 @@ struct Fp8Stream {
     row = lane / FLPT;
     qoff = (lane % FLPT) * 16;
     cur.init(cum_, lens_, a.S, a.H, lane_);
+  }
+
+  // Fused append of row (s, h): quantise token L - 1's K and V rows (k_new /
+  // v_new row s) and write the codes to its slot.  Lanes 0..31 take four K
+  // elements each, lanes 32..63 four V elements.  A table entry outside the
+  // pool writes nothing (the stream flags the row).
+  __device__ __forceinline__ void append_row(const DecodeParams &a, int s, int h, int L) {
+    const int blk = tables[(int64_t)s * maxb + (L - 1) / B];
+    if (blk < 0 || (int64_t)blk >= num_blocks) return;
+    const bool isv = lane >= 32;
+    const int dim = (lane & 31) * 4;
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(isv ? a.v_new : a.k_new) +
+                          (int64_t)s * a.new_stride + (int64_t)h * FD + dim;
+    const uint32_t w0 = reinterpret_cast<const uint32_t *>(src)[0];
+    const uint32_t w1 = reinterpret_cast<const uint32_t *>(src)[1];
+    const float inv = isv ? a.v_inv : a.k_inv;
+    const uint32_t code = quant4(lo16<DT>(w0) * inv, hi16<DT>(w0) * inv, lo16<DT>(w1) * inv, hi16<DT>(w1) * inv);
+    uint8_t *dst = const_cast<uint8_t *>(isv ? vp : kp) + (int64_t)blk * blk_stride + (int64_t)h * B * FD +
+                   ((L - 1) % B) * FD + dim;
+    *reinterpret_cast<uint32_t *>(dst) = code;
   }
 
   __device__ __forceinline__ static int first_block(int c) { return FTC >= B ? c * (FTC / B) : c / (B / FTC); }
@@ -323,7 +347,7 @@ struct Fp8Stream {
   }
 };
 
-template <int DT, int B, int NW, bool NT>
+template <int DT, int B, int NW, bool NT, bool APP>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   using ST = Fp8Stream<DT, B, NT>;
   extern __shared__ int64_t lds[];
@@ -348,6 +372,23 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   st.init(a, cum, lens, lane);
   st.worker = w;
   st.cur.enter(lo, hi);
+  if constexpr (APP) {
+    // the appends of the rows whose last chunk this slice holds, written
+    // before the stream reads them
+    bool any = false;
+    while (st.cur.cvalid) {
+      if (st.cur.cseg + st.cur.cn - 1 < st.cur.it_hi) {
+        st.append_row(a, st.cur.cs_, st.cur.ch_, st.cur.cL);
+        any = true;
+      }
+      st.cur.next_row();
+    }
+    if (any) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    st.cur.enter(lo, hi);
+  }
   const int n = (int)(hi - lo);
   __builtin_amdgcn_s_setprio(3);
   st.run(n / 4, n / 2, (3 * n) / 4);
@@ -357,22 +398,29 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
 template <int DT, bool NT>
 const void *fp8_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT>);
-    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT>);
-    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT>);
-    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT>);
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT, true>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT, true>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT, true>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT, true>);
     default: return nullptr;
   }
 }
 
+template <int DT, int B, bool NT, bool APP>
+void go_fp8(const DecodeParams &a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, NT, APP>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
+                     fp8_lds_bytes(a.S), st, a);
+}
+
 template <int DT, int B>
 hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
-  if (a.stream_kv)
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
-                       fp8_lds_bytes(a.S), st, a);
-  else
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false>), dim3(a.G / kFp8Waves),
-                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
+  if (a.append) {
+    if (a.stream_kv) go_fp8<DT, B, true, true>(a, st);
+    else go_fp8<DT, B, false, true>(a, st);
+  } else {
+    if (a.stream_kv) go_fp8<DT, B, true, false>(a, st);
+    else go_fp8<DT, B, false, false>(a, st);
+  }
   return hipGetLastError();
 }
 

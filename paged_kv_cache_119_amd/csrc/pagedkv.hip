@@ -276,10 +276,10 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
                        const int32_t *block_tables, const int32_t *context_lens, float scale,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
                        const pkv_pool *p, int32_t partition_size, void *workspace,
-                       size_t workspace_bytes, pkv::DecodeParams *a) {
+                       size_t workspace_bytes, pkv::DecodeParams *a, bool fp8 = false) {
   const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
-                                    workspace, workspace_bytes, true, a);
+                                    workspace, workspace_bytes, true, a, 1, fp8);
   if (st != PKV_OK || num_seqs == 0) return st;
   if (a->group) return PKV_ERR_UNSUPPORTED;  // one query row per KV head only
   if (!k_new || !v_new) return PKV_ERR_NULL;
@@ -550,6 +550,27 @@ pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *
   if (st != PKV_OK || num_seqs == 0) return st;
   a.scale_log2 = scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const void *k_new, const void *v_new,
+                                                 int64_t new_token_stride, void *k_pool, void *v_pool,
+                                                 const int32_t *block_tables, const int32_t *context_lens,
+                                                 float scale, float k_scale, float v_scale, int32_t num_seqs,
+                                                 int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PKV_ERR_SHAPE;
+  pkv::DecodeParams a;
+  const pkv_status st = fill_append(out, q, k_new, v_new, new_token_stride, k_pool, v_pool, block_tables,
+                                    context_lens, scale, num_seqs, num_heads, max_blocks_per_seq, p, 0, workspace,
+                                    workspace_bytes, &a, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+  a.k_inv = 1.0f / k_scale;
+  a.v_inv = 1.0f / v_scale;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

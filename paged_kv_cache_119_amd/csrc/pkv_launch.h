@@ -64,6 +64,7 @@ struct DecodeParams {
   // multiplied by v_scale.
   int32_t fp8;
   float v_scale;
+  float k_inv, v_inv;  // fused FP8 append: float32 reciprocals of the scales
   // 1: K/V loads of the stream kernels are non-temporal (blocks read once
   // per call); 0: ordinary cached loads (blocks shared between sequences).
   int32_t stream_kv;
@@ -88,6 +89,7 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
 // FP8 (e4m3) pools, head_dim 128, one query row per KV head.
 int fp8_chunk_tokens();
 size_t fp8_lds_bytes(int num_seqs);
+// The fused-append instance (for occupancy queries).
 const void *fp8_kernel(int dtype, int block_size, int nt);
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,

@@ -34,6 +34,12 @@ def test_header_and_binding_agree():
     assert _declared() == sorted(bd.EXPORTS)
 
 
+def test_every_entry_point_has_a_python_function_of_the_same_name():
+    for sym in bd.EXPORTS:
+        name = sym[len("pkv_"):]
+        assert callable(getattr(pkv, name, None)), f"no Python function {name} for {sym}"
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name

@@ -211,6 +211,47 @@ def test_fp8_append_then_decode_round_trip():
     assert_close(to_bits(out), ref[:, 0], "f16", "fp8 append then decode")
 
 
+@pytest.mark.parametrize("dtype,B", [("f16", 16), ("bf16", 8), ("f16", 64)])
+def test_fp8_fused_append_matches_oracle_and_separate_path(dtype, B):
+    """The fused step writes the same codes as the quantising append and
+    returns the oracle's append-then-attend result; it equals the separate
+    append + decode bit for bit.  L == 0 appends nothing; an out-of-pool last
+    block writes nothing and gives NaN."""
+    lengths = [1, 31, 32, 33, 200, 0, 77, 1025, 64]
+    H = 3
+    c = _case([max(L, 1) for L in lengths], H, B, seed=390 + B)
+    c["lens"] = np.asarray(lengths, np.int32)
+    c["tables"][6, (77 - 1) // B] = 10 ** 6  # sequence 6: its last block is outside the pool
+    S = len(lengths)
+    kn = normal_16bit((S, H, D), dtype, DEV, 391)
+    vn = normal_16bit((S, H, D), dtype, DEV, 392)
+    q = normal_16bit((S, H, D), dtype, DEV, 393)
+    ks, vs = 0.02, 0.03
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    kw, vw = _codes(c["kp"]).copy(), _codes(c["vp"]).copy()
+    k1, v1 = c["kp"].clone(), c["vp"].clone()
+    out = pkv.paged_attention_decode_append_fp8(q, kn, vn, k1, v1, tab, lens, D ** -0.5, ks, vs)
+    # the separate path: slots of token L - 1, the quantising append, then decode
+    k2, v2 = c["kp"].clone(), c["vp"].clone()
+    slots = np.array([int(c["tables"][s, (L - 1) // B]) * B + (L - 1) % B if L > 0 else -1
+                      for s, L in enumerate(lengths)], np.int64)
+    slots[6] = -1
+    pkv.reshape_and_cache_fp8(kn, vn, k2, v2, torch.from_numpy(slots).to(DEV), ks, vs)
+    out2 = pkv.paged_attention_decode_fp8(q, k2, v2, tab, lens, D ** -0.5, ks, vs)
+    torch.cuda.synchronize()
+    po.reshape_and_cache_fp8(to_bits(kn), to_bits(vn), kw, vw, slots, B, dtype, ks, vs)
+    assert np.array_equal(_codes(k1), kw) and np.array_equal(_codes(v1), vw)
+    assert np.array_equal(_codes(k2), kw) and np.array_equal(_codes(v2), vw)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    o = po.bits_to_f64(to_bits(out), dtype)
+    assert np.all(o[5] == 0) and np.all(np.isnan(o[6]))
+    good = [i for i in range(S) if i not in (5, 6)]
+    ref = po.decode_rows_fp8(to_bits(q)[good][:, None], kw, vw, c["tables"][good], c["lens"][good], D ** -0.5, B,
+                             dtype, ks, vs)[:, 0]
+    assert_close(to_bits(out)[good], ref, dtype, f"fp8 fused append {dtype} B={B}")
+
+
 def test_fp8_unsupported_shapes_are_rejected():
     c = _case([20, 30], 2, 16, seed=380)
     tab = torch.from_numpy(c["tables"]).to(DEV)
