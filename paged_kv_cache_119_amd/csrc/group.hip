@@ -362,62 +362,89 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   __builtin_amdgcn_s_setprio(0);
 }
 
-// One wavefront per (sequence, KV head, query row): rows of empty or invalid
-// contexts, and the LSE merge of rows cut over several workers.
+// One wavefront per (sequence, KV head), for its M query rows (16 rows x 4
+// lanes x 32 dims): rows of empty or invalid contexts, and the LSE merge of
+// rows cut over several workers.  The pieces' (m, l) and o rows are fetched
+// four pieces per round of loads.
 template <int DT>
 __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
   const int gq = a.H / a.Hkv;
   const int M = gq * a.nq;
-  const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (s * Hkv + h) * M + row
-  if (id >= (int64_t)a.S * a.Hkv * M) return;
-  const int64_t grow = id / M;
-  const int rr = (int)(id - grow * M);
+  const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hkv + h
+  if (grow >= (int64_t)a.S * a.Hkv) return;
   const int s = (int)(grow / a.Hkv);
   const int h = (int)(grow - (int64_t)s * a.Hkv);
-  const int qi = rr / gq, gi = rr - (rr / gq) * gq;
+  const int r = lane >> 2;         // this lane's query row (16 rows x 4 lanes)
+  const int d0 = (lane & 3) * 32;  // and its 32 dims
+  const bool live = r < M;
+  const int qi = r / gq, gi = r - (r / gq) * gq;
+  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) +
+                      (((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi) * GD + d0;
   const int L = a.lens[s];
-  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + (((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi) * GD;
+  const uint64_t cum_s = (uint64_t)a.ws_cum[s];
+  const uint64_t total = (uint64_t)a.ws_cum[a.S];
   if (L <= 0 || L > a.maxb * a.B || L < a.nq) {
-    const uint16_t v = (L == 0) ? uint16_t(0) : to16<DT>(__builtin_nanf(""));
-    for (int d = lane; d < GD; d += 64) out_row[d] = v;
+    const uint32_t v = (L == 0) ? 0u : 0x00010001u * to16<DT>(__builtin_nanf(""));
+    if (live) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{v, v, v, v};
+    }
     return;
   }
   const int nch = (L + GTC - 1) / GTC;
-  const uint64_t seg = (uint64_t)a.ws_cum[s] + (uint64_t)h * nch;
+  const uint64_t seg = cum_s + (uint64_t)h * nch;
   const uint64_t end = seg + nch;
-  const uint64_t slice = slice_of((uint64_t)a.ws_cum[a.S], a.G);
+  const uint64_t slice = slice_of(total, a.G);
   const int64_t t_a = (int64_t)udiv64(seg, slice);
   const int64_t n = (int64_t)udiv64(end - 1, slice) - t_a + 1;
-  if (n <= 1) return;  // one piece: it wrote the row
-  auto slot = [&](int64_t j) { return (t_a + j + grow) * M + rr; };
-  float M_ = kNegInf;
-  for (int64_t j0 = 0; j0 < n; j0 += 64) {
-    const int64_t j = j0 + lane;
-    if (j < n) M_ = fmaxf(M_, a.ws_m[slot(j)]);
+  if (n <= 1 || !live) return;  // one piece: it wrote the rows
+  auto slot = [&](int64_t j) { return (t_a + j + grow) * M + r; };
+  // the row's max over its pieces, four pieces per round of loads
+  float mx = kNegInf;
+  for (int64_t j0 = 0; j0 < n; j0 += 4) {
+    float mv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mv[q] = a.ws_m[slot(min(j0 + q, n - 1))];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
+  }
+  // pieces combined in worker order
+  float lsum = 0.f;
+  f4 o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t j0 = 0; j0 < n; j0 += 4) {
+    float mv[4], lv[4];
+    f4 ov[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t u = slot(min(j0 + q, n - 1));
+      mv[q] = a.ws_m[u];
+      lv[q] = a.ws_l[u];
+      const f4 *src = reinterpret_cast<const f4 *>(a.ws_o + u * GD + d0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ov[q][k] = src[k];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (j0 + q >= n) break;
+      const float f = (mv[q] == kNegInf) ? 0.f : fast_exp2((mv[q] - mx) * kLog2e);
+      lsum += f * lv[q];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] += f * ov[q][k];
+    }
+  }
+  uint32_t w[16];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[2 * k] = (uint32_t)to16<DT>(o[k][0] / lsum) | ((uint32_t)to16<DT>(o[k][1] / lsum) << 16);
+    w[2 * k + 1] = (uint32_t)to16<DT>(o[k][2] / lsum) | ((uint32_t)to16<DT>(o[k][3] / lsum) << 16);
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M_ = fmaxf(M_, __shfl_xor(M_, off));
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int64_t j0 = 0; j0 < n; j0 += 64) {
-    const int64_t j = j0 + lane;
-    float f = 0.f, lw = 0.f;
-    if (j < n) {
-      const float mj = a.ws_m[slot(j)];
-      f = (mj == kNegInf) ? 0.f : fast_exp2((mj - M_) * kLog2e);
-      lw = a.ws_l[slot(j)];
-    }
-    const int cnt = (int)min((int64_t)64, n - j0);
-    for (int q = 0; q < cnt; ++q) {  // pieces in worker order
-      const float fq = __shfl(f, q);
-      const int64_t u = slot(j0 + q);
-      lsum += fq * __shfl(lw, q);
-      o0 += fq * a.ws_o[u * GD + lane];
-      o1 += fq * a.ws_o[u * GD + lane + 64];
-    }
-  }
-  out_row[lane] = to16<DT>(o0 / lsum);
-  out_row[lane + 64] = to16<DT>(o1 / lsum);
+  for (int k = 0; k < 4; ++k)
+    reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
 }
 
 template <int DT, int B>
@@ -470,8 +497,8 @@ hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream) {
 
 hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream) {
   if (a.S == 0) return hipSuccess;
-  const int64_t rows = (int64_t)a.S * a.Hkv * (a.H / a.Hkv) * a.nq;
-  const int grid = (int)((rows + 3) / 4);
+  const int64_t groups = (int64_t)a.S * a.Hkv;  // one wavefront per (sequence, KV head)
+  const int grid = (int)((groups + 3) / 4);
   if (a.dtype == DT_F16)
     hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16>), dim3(grid), dim3(256), 0, stream, a);
   else
