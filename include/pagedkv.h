@@ -421,8 +421,8 @@ pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *
  * the others (append first, then attend: "PagedAttention 完全拆解",
  * 原理详解（一）, Figure 6 walk-through).  A needed table entry outside the
  * pool writes nothing and gives a NaN row.  Same restrictions, scales and
- * workspace as pkv_paged_attention_decode_fp8; one split launch (append
- * included) and one merge launch.
+ * workspace as pkv_paged_attention_decode_fp8.  Three launches: the append
+ * (slots from the table, no slot list), the split pass and the merge pass.
  */
 pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const void *k_new, const void *v_new,
                                                  int64_t new_token_stride, void *k_pool, void *v_pool,

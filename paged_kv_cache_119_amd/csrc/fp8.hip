@@ -6,10 +6,11 @@
 //    1, with a quantising store): code = e4m3(x * (1 / scale)), the product
 //    rounded in float32, saturated to +-448, then rounded to the nearest e4m3
 //    value, ties to even (v_cvt_pk_fp8_f32); NaN stays NaN.
-//  * Fused append (APP): before its stream starts, each wavefront quantises
-//    and writes token L - 1 of every row whose last chunk lies in its slice;
-//    the stream then reads those codes like any other (only the owner of a
-//    row's last chunk ever reads that slot).
+//  * Append of each sequence's new token: the same quantising write, with
+//    the slot of token L - 1 taken from the block table (the decode step's
+//    append, one launch, no slot list).  Kept out of the decode kernel:
+//    stores into the pool from inside the long stream kernel measured far
+//    slower than this separate launch on large pools.
 //  * Decode (the attention equation of the same page, 背景): the balanced
 //    split and pipelined chunk stream of the 16-bit kernel, with 32-token
 //    chunks: 8 lanes hold a token row (16 codes each), a load instruction
@@ -53,8 +54,29 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// One thread per 16 elements of a (token, head) row: 32 bytes of 16-bit input
-// -> 16 bytes of codes, for K and for V.
+// 16 elements of a K row and of a V row (16-bit, 32 bytes each) -> 16 codes
+// each, written at element offset dst of the pools.
+template <int DT>
+__device__ __forceinline__ void quantise_piece(uint8_t *kp, uint8_t *vp, const uint16_t *ksrc, const uint16_t *vsrc,
+                                               int64_t dst, float k_inv, float v_inv) {
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t *src = which == 0 ? ksrc : vsrc;
+    const float inv = which == 0 ? k_inv : v_inv;
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(src);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = quant4(lo16<DT>(w[2 * j]) * inv, hi16<DT>(w[2 * j]) * inv, lo16<DT>(w[2 * j + 1]) * inv,
+                    hi16<DT>(w[2 * j + 1]) * inv);
+    const u32x4 ov = {o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<u32x4 *>((which == 0 ? kp : vp) + dst) = ov;
+  }
+}
+
+// One thread per 16 elements of a (token, head) row, slots from a list.
 template <int DT>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     uint8_t *__restrict__ kp, uint8_t *__restrict__ vp, const uint16_t *__restrict__ k,
@@ -73,21 +95,34 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   const int64_t blk = slot / B;
   const int64_t off = slot - blk * B;
   const int64_t dst = ((blk * Hkv + h) * B + off) * D + piece * 16;
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const uint16_t *src = (which == 0 ? k + (int64_t)t * k_stride : v + (int64_t)t * v_stride) + h * D + piece * 16;
-    const float inv = which == 0 ? k_inv : v_inv;
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(src);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = quant4(lo16<DT>(w[2 * j]) * inv, hi16<DT>(w[2 * j]) * inv, lo16<DT>(w[2 * j + 1]) * inv,
-                    hi16<DT>(w[2 * j + 1]) * inv);
-    const u32x4 ov = {o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<u32x4 *>((which == 0 ? kp : vp) + dst) = ov;
-  }
+  quantise_piece<DT>(kp, vp, k + (int64_t)t * k_stride + h * D + piece * 16, v + (int64_t)t * v_stride + h * D + piece * 16,
+                     dst, k_inv, v_inv);
+}
+
+// The decode step's append: row s of k_new / v_new becomes token L - 1 of
+// sequence s, its slot from the block table.  One thread per 16 elements of
+// a (sequence, head) row; invalid contexts and out-of-pool entries write
+// nothing.
+template <int DT>
+__global__ __launch_bounds__(256) void append_last_fp8_kernel(DecodeParams a, float k_inv, float v_inv) {
+  const int per_row = FD / 16;
+  const int64_t per_seq = (int64_t)a.Hkv * per_row;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.S * per_seq) return;
+  const int s = (int)(idx / per_seq);
+  const int r = (int)(idx - (int64_t)s * per_seq);
+  const int h = r / per_row;
+  const int piece = r - h * per_row;
+  const int L = a.lens[s];
+  if (L <= 0 || L > a.maxb * a.B) return;
+  const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
+  const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * FD + piece * 16;
+  const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * FD + piece * 16;
+  quantise_piece<DT>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)),
+                     reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)),
+                     reinterpret_cast<const uint16_t *>(a.k_new) + src,
+                     reinterpret_cast<const uint16_t *>(a.v_new) + src, dst, k_inv, v_inv);
 }
 
 template <int DT, int B, bool NT>
@@ -139,26 +174,6 @@ struct Fp8Stream {
     row = lane / FLPT;
     qoff = (lane % FLPT) * 16;
     cur.init(cum_, lens_, a.S, a.H, lane_);
-  }
-
-  // Fused append of row (s, h): quantise token L - 1's K and V rows (k_new /
-  // v_new row s) and write the codes to its slot.  Lanes 0..31 take four K
-  // elements each, lanes 32..63 four V elements.  A table entry outside the
-  // pool writes nothing (the stream flags the row).
-  __device__ __forceinline__ void append_row(const DecodeParams &a, int s, int h, int L) {
-    const int blk = tables[(int64_t)s * maxb + (L - 1) / B];
-    if (blk < 0 || (int64_t)blk >= num_blocks) return;
-    const bool isv = lane >= 32;
-    const int dim = (lane & 31) * 4;
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(isv ? a.v_new : a.k_new) +
-                          (int64_t)s * a.new_stride + (int64_t)h * FD + dim;
-    const uint32_t w0 = reinterpret_cast<const uint32_t *>(src)[0];
-    const uint32_t w1 = reinterpret_cast<const uint32_t *>(src)[1];
-    const float inv = isv ? a.v_inv : a.k_inv;
-    const uint32_t code = quant4(lo16<DT>(w0) * inv, hi16<DT>(w0) * inv, lo16<DT>(w1) * inv, hi16<DT>(w1) * inv);
-    uint8_t *dst = const_cast<uint8_t *>(isv ? vp : kp) + (int64_t)blk * blk_stride + (int64_t)h * B * FD +
-                   ((L - 1) % B) * FD + dim;
-    *reinterpret_cast<uint32_t *>(dst) = code;
   }
 
   __device__ __forceinline__ static int first_block(int c) { return FTC >= B ? c * (FTC / B) : c / (B / FTC); }
@@ -347,7 +362,7 @@ struct Fp8Stream {
   }
 };
 
-template <int DT, int B, int NW, bool NT, bool APP>
+template <int DT, int B, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   using ST = Fp8Stream<DT, B, NT>;
   extern __shared__ int64_t lds[];
@@ -372,23 +387,6 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   st.init(a, cum, lens, lane);
   st.worker = w;
   st.cur.enter(lo, hi);
-  if constexpr (APP) {
-    // the appends of the rows whose last chunk this slice holds, written
-    // before the stream reads them
-    bool any = false;
-    while (st.cur.cvalid) {
-      if (st.cur.cseg + st.cur.cn - 1 < st.cur.it_hi) {
-        st.append_row(a, st.cur.cs_, st.cur.ch_, st.cur.cL);
-        any = true;
-      }
-      st.cur.next_row();
-    }
-    if (any) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
-    st.cur.enter(lo, hi);
-  }
   const int n = (int)(hi - lo);
   __builtin_amdgcn_s_setprio(3);
   st.run(n / 4, n / 2, (3 * n) / 4);
@@ -398,29 +396,22 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
 template <int DT, bool NT>
 const void *fp8_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT, true>);
-    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT, true>);
-    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT, true>);
-    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT, true>);
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT>);
     default: return nullptr;
   }
 }
 
-template <int DT, int B, bool NT, bool APP>
-void go_fp8(const DecodeParams &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, NT, APP>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
-                     fp8_lds_bytes(a.S), st, a);
-}
-
 template <int DT, int B>
 hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
-  if (a.append) {
-    if (a.stream_kv) go_fp8<DT, B, true, true>(a, st);
-    else go_fp8<DT, B, false, true>(a, st);
-  } else {
-    if (a.stream_kv) go_fp8<DT, B, true, false>(a, st);
-    else go_fp8<DT, B, false, false>(a, st);
-  }
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
+                       fp8_lds_bytes(a.S), st, a);
+  else
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false>), dim3(a.G / kFp8Waves),
+                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
   return hipGetLastError();
 }
 
@@ -450,6 +441,18 @@ hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {
   if (a.dtype == DT_F16) { PKV_F(DT_F16) }
   PKV_F(DT_BF16)
 #undef PKV_F
+}
+
+hipError_t launch_append_last_fp8(const DecodeParams &a, float k_inv, float v_inv, hipStream_t stream) {
+  const int64_t threads = (int64_t)a.S * a.Hkv * (FD / 16);
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  if (a.dtype == DT_F16)
+    hipLaunchKernelGGL((append_last_fp8_kernel<DT_F16>), dim3((unsigned)grid), dim3(256), 0, stream, a, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL((append_last_fp8_kernel<DT_BF16>), dim3((unsigned)grid), dim3(256), 0, stream, a, k_inv,
+                       v_inv);
+  return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v, int64_t k_stride,

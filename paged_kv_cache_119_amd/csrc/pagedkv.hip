@@ -569,8 +569,10 @@ pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const
   if (st != PKV_OK || num_seqs == 0) return st;
   a.scale_log2 = scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
-  a.k_inv = 1.0f / k_scale;
-  a.v_inv = 1.0f / v_scale;
+  // the append as its own launch (slots from the table), then the decode passes
+  const pkv_status s0 = hip_status(pkv::launch_append_last_fp8(a, 1.0f / k_scale, 1.0f / v_scale, (hipStream_t)stream));
+  if (s0 != PKV_OK) return s0;
+  a.append = 0;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

@@ -64,7 +64,6 @@ struct DecodeParams {
   // multiplied by v_scale.
   int32_t fp8;
   float v_scale;
-  float k_inv, v_inv;  // fused FP8 append: float32 reciprocals of the scales
   // 1: K/V loads of the stream kernels are non-temporal (blocks read once
   // per call); 0: ordinary cached loads (blocks shared between sequences).
   int32_t stream_kv;
@@ -89,8 +88,10 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
 // FP8 (e4m3) pools, head_dim 128, one query row per KV head.
 int fp8_chunk_tokens();
 size_t fp8_lds_bytes(int num_seqs);
-// The fused-append instance (for occupancy queries).
 const void *fp8_kernel(int dtype, int block_size, int nt);
+// The decode step's append into e4m3 pools: token L - 1 of every sequence
+// from k_new / v_new (a.append fields), slots from the block table.
+hipError_t launch_append_last_fp8(const DecodeParams &a, float k_inv, float v_inv, hipStream_t stream);
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, const void *v,
                                         int64_t k_stride, int64_t v_stride, const int64_t *slots,

@@ -252,6 +252,36 @@ def test_fp8_fused_append_matches_oracle_and_separate_path(dtype, B):
     assert_close(to_bits(out)[good], ref, dtype, f"fp8 fused append {dtype} B={B}")
 
 
+def test_fp8_fused_append_many_short_rows():
+    """Short contexts put many rows' last chunks into one wavefront's slice
+    (a slice is at least 8 chunks): more appends than a wavefront stages, so
+    the extra ones take the direct-write path.  Same checks as above."""
+    rng = np.random.default_rng(395)
+    lengths = [int(x) for x in rng.integers(1, 41, 48)]
+    H, B, dtype = 4, 16, "bf16"
+    c = _case(lengths, H, B, seed=396)
+    S = len(lengths)
+    kn = normal_16bit((S, H, D), dtype, DEV, 397)
+    vn = normal_16bit((S, H, D), dtype, DEV, 398)
+    q = normal_16bit((S, H, D), dtype, DEV, 399)
+    ks, vs = 0.05, 0.04
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    kw, vw = _codes(c["kp"]).copy(), _codes(c["vp"]).copy()
+    k1, v1 = c["kp"].clone(), c["vp"].clone()
+    out = pkv.paged_attention_decode_append_fp8(q, kn, vn, k1, v1, tab, lens, 0.09, ks, vs)
+    k2, v2 = c["kp"].clone(), c["vp"].clone()
+    slots = np.array([int(c["tables"][s, (L - 1) // B]) * B + (L - 1) % B for s, L in enumerate(lengths)], np.int64)
+    pkv.reshape_and_cache_fp8(kn, vn, k2, v2, torch.from_numpy(slots).to(DEV), ks, vs)
+    out2 = pkv.paged_attention_decode_fp8(q, k2, v2, tab, lens, 0.09, ks, vs)
+    torch.cuda.synchronize()
+    po.reshape_and_cache_fp8(to_bits(kn), to_bits(vn), kw, vw, slots, B, dtype, ks, vs)
+    assert np.array_equal(_codes(k1), kw) and np.array_equal(_codes(v1), vw)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    ref = po.decode_rows_fp8(to_bits(q)[:, None], kw, vw, c["tables"], c["lens"], 0.09, B, dtype, ks, vs)[:, 0]
+    assert_close(to_bits(out), ref, dtype, "fp8 fused append, short rows")
+
+
 def test_fp8_unsupported_shapes_are_rejected():
     c = _case([20, 30], 2, 16, seed=380)
     tab = torch.from_numpy(c["tables"]).to(DEV)
