@@ -712,17 +712,22 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
 }
 
 // One wavefront per (sequence, head): rows of empty or invalid contexts, and
-// the LSE merge of rows cut over several workers.  Lane j reads the j-th
-// worker's (m, l); the merged row then needs one pass.
+// the LSE merge of rows cut over several workers.  Two rounds of loads: the
+// length and the chunk prefix; then every piece's (m, l) (lane j: piece j)
+// together with the o rows of the first four pieces.  Pieces are combined in
+// worker order.
 // TC is the chunk length of the split pass that wrote the partials.
 template <int DT, int D, int TC>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
+  constexpr int V = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= (int64_t)a.S * a.H) return;
   const int s = (int)(g / a.H);
   const int h = (int)(g - (int64_t)s * a.H);
   const int L = a.lens[s];
+  const uint64_t cum_s = (uint64_t)a.ws_cum[s];
+  const uint64_t total = (uint64_t)a.ws_cum[a.S];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;
   if (L <= 0 || L > a.maxb * a.B) {
     const uint16_t v = (L == 0) ? uint16_t(0) : to16<DT>(__builtin_nanf(""));
@@ -730,57 +735,78 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
     return;
   }
   const int nch = (L + TC - 1) / TC;
-  const uint64_t seg = (uint64_t)a.ws_cum[s] + (uint64_t)h * nch;
+  const uint64_t seg = cum_s + (uint64_t)h * nch;
   const uint64_t end = seg + nch;  // the row's chunks are [seg, end)
-  const uint64_t slice = slice_of((uint64_t)a.ws_cum[a.S], a.G);
+  const uint64_t slice = slice_of(total, a.G);
   const int64_t t_a = (int64_t)udiv64(seg, slice);
   const int64_t n = (int64_t)udiv64(end - 1, slice) - t_a + 1;
   if (n <= 1) return;  // one piece: it wrote the row
 
-  auto item_at = [&](int64_t j) { return t_a + j; };
-  float M = kNegInf;
-  for (int64_t j0 = 0; j0 < n; j0 += 64) {
+  auto item = [&](int64_t j) { return t_a + j + g; };  // partial slot of piece j
+  float m0 = kNegInf, l0 = 0.f;
+  if (lane < n) {
+    m0 = a.ws_m[item(lane)];
+    l0 = a.ws_l[item(lane)];
+  }
+  float pre[4][V];  // o rows of pieces 0..3 (n >= 2; indexes past n repeat the last)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t u = item(min((int64_t)q, n - 1));
+#pragma unroll
+    for (int k = 0; k < V; ++k) pre[q][k] = a.ws_o[u * D + lane + 64 * k];
+  }
+  float M = m0;
+  for (int64_t j0 = 64; j0 < n; j0 += 64) {
     const int64_t j = j0 + lane;
-    if (j < n) M = fmaxf(M, a.ws_m[item_at(j) + g]);
+    if (j < n) M = fmaxf(M, a.ws_m[item(j)]);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float lsum = 0.f;
-  float o[D / 64];
+  float o[V];
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) o[j] = 0.f;
+  for (int k = 0; k < V; ++k) o[k] = 0.f;
   for (int64_t j0 = 0; j0 < n; j0 += 64) {
     const int64_t j = j0 + lane;
     float f = 0.f, lw = 0.f;
-    if (j < n) {
-      const int64_t u = item_at(j) + g;
-      f = fast_exp2((a.ws_m[u] - M) * kLog2e);
-      lw = a.ws_l[u];
+    if (j0 == 0) {
+      if (lane < n) {
+        f = fast_exp2((m0 - M) * kLog2e);
+        lw = l0;
+      }
+    } else if (j < n) {
+      f = fast_exp2((a.ws_m[item(j)] - M) * kLog2e);
+      lw = a.ws_l[item(j)];
     }
     const int cnt = (int)min((int64_t)64, n - j0);
     // workers in increasing order; their o rows are fetched 4 at a time
     for (int q0 = 0; q0 < cnt; q0 += 4) {
-      float fj[4], vj[4][D / 64];
+      float fj[4], vj[4][V];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int jj = min(q0 + q, cnt - 1);
         fj[q] = (q0 + q < cnt) ? __shfl(f, jj) : 0.f;
-        const int64_t u = item_at(j0 + jj) + g;
+        if (j0 == 0 && q0 == 0) {
 #pragma unroll
-        for (int k = 0; k < D / 64; ++k) vj[q][k] = a.ws_o[u * D + lane + 64 * k];
+          for (int k = 0; k < V; ++k) vj[q][k] = pre[q][k];
+        } else {
+          const int64_t u = item(j0 + jj);
+#pragma unroll
+          for (int k = 0; k < V; ++k) vj[q][k] = a.ws_o[u * D + lane + 64 * k];
+        }
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (q0 + q >= cnt) break;
         lsum += fj[q] * __shfl(lw, q0 + q);
 #pragma unroll
-        for (int k = 0; k < D / 64; ++k) o[k] += fj[q] * vj[q][k];
+        for (int k = 0; k < V; ++k) o[k] += fj[q] * vj[q][k];
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) out_row[lane + 64 * j] = to16<DT>(o[j] / lsum);
+  for (int k = 0; k < V; ++k) out_row[lane + 64 * k] = to16<DT>(o[k] / lsum);
 }
 
 // ---------------------------------------------------------------------------
