@@ -58,8 +58,9 @@ struct Geo {
   static constexpr int TC = NL * TPI;        // tokens per chunk
 };
 
-// One wavefront's online softmax over part of one (sequence, head).
-template <int DT, int D, int B>
+// One wavefront's online softmax over part of one (sequence, head).  NT:
+// K/V rows are read with non-temporal loads.
+template <int DT, int D, int B, bool NT>
 struct WaveAttn {
   using G = Geo<D>;
   static constexpr int LPT = G::LPT, TPI = G::TPI, NL = G::NL, TC = G::TC;
@@ -148,8 +149,8 @@ struct WaveAttn {
         blk = 0;
       }
       const int64_t base = (int64_t)blk * blk_stride + head_base + off * D;
-      kr[i] = *reinterpret_cast<const u32x4 *>(kp + base + lane_off);
-      vr[i] = *reinterpret_cast<const u32x4 *>(vp + base + lane_off);
+      kr[i] = ld_kv<NT>(kp + base + lane_off);
+      vr[i] = ld_kv<NT>(vp + base + lane_off);
     }
   }
 
@@ -259,9 +260,9 @@ struct WaveAttn {
 // Fixed partitions
 // ---------------------------------------------------------------------------
 
-template <int DT, int D, int B, int NW>
+template <int DT, int D, int B, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeParams a) {
-  using WA = WaveAttn<DT, D, B>;
+  using WA = WaveAttn<DT, D, B, NT>;
   constexpr int TC = WA::TC;
 
   __shared__ int32_t s_tab[kTabMax];
@@ -818,8 +819,12 @@ struct PartitionsF {
   static hipError_t call(const DecodeParams &a, hipStream_t st) {
     const int group = 8 * kXcdGroup;
     const int grid = ((a.items + group - 1) / group) * group;
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves>), dim3(grid),
-                       dim3(kNumWaves * 64), 0, st, a);
+    if (a.stream_kv)
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves, true>), dim3(grid),
+                         dim3(kNumWaves * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves, false>), dim3(grid),
+                         dim3(kNumWaves * 64), 0, st, a);
     return hipGetLastError();
   }
 };
