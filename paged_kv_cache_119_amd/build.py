@@ -3,7 +3,9 @@
     python -m paged_kv_cache_119_amd.build [--jobs N] [--verbose]
 
 Every ``csrc/*.hip`` file is compiled to an object under ``_build/`` and the
-objects are linked into ``paged_kv_cache_119_amd/libpagedkv.so``.
+objects are linked into ``paged_kv_cache_119_amd/libpagedkv.so``.  The
+streaming-read probe the benchmark reports for context (``probe/``, not part
+of the library) is built into ``paged_kv_cache_119_amd/libpkvprobe.so``.
 """
 
 from __future__ import annotations
@@ -22,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libpkvprobe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -64,7 +68,21 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The streaming-read probe (measurement context only)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def main(argv=None) -> int:

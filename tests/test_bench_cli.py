@@ -1,0 +1,23 @@
+"""bench.py's command line on a CPU-only machine: more than one GPU is
+refused with a message, before anything touches a GPU."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_help_lists_the_workload_options():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0
+    for opt in ("--config", "--op", "--kv", "--reuse-blocks", "--separate-append"):
+        assert opt in r.stdout
