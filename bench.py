@@ -315,28 +315,33 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
     import numpy as np
     import torch
 
-    from synth import make_pools, normal_16bit
+    from synth import make_fp8_pools, make_pools, normal_16bit
 
     Hkv, D, B, S = t.num_heads, t.head_dim, t.block_size, t.num_seqs
     G = args.group or config_query_heads(t) // Hkv
     Q = args.queries
     H = G * Hkv
     dsize = 2
+    fp8 = args.kv == "fp8"
+    ks = vs = 1.0 / 60
+    kvsize = 1 if fp8 else dsize
     tab = torch.from_numpy(t.block_tables).to(dev)
     lens = torch.from_numpy(t.context_lens).to(dev)
     reps = []
     for r in range(args.replicas):
         t.seed += 1000 * r
-        kp, vp = make_pools(t, dev)
+        kp, vp = make_fp8_pools(t, dev) if fp8 else make_pools(t, dev)
         t.seed -= 1000 * r
         shape = (S, H, D) if Q == 1 else (S, Q, H, D)
         q = normal_16bit(shape, t.dtype, dev, t.seed * 16 + 20 + r)
         reps.append((kp, vp, q, torch.empty_like(q)))
-    desc = pkv.pool_desc_of(reps[0][0], args.reuse_blocks)
+    desc = pkv.make_pool_desc(t.num_blocks, B, Hkv, D, t.dtype, args.reuse_blocks)
     dref = ctypes.byref(desc)
     stream = torch.cuda.current_stream(dev)
     sp = int(stream.cuda_stream)
-    if Q == 1:
+    if fp8:
+        wsb = pkv.fp8_multi_workspace_bytes(S, Q, H, t.max_blocks, reps[0][0], t.dtype)
+    elif Q == 1:
         wsb = pkv.decode_workspace_bytes(S, H, t.max_blocks, reps[0][0], 0)
     else:
         wsb = pkv.multi_workspace_bytes(S, Q, H, t.max_blocks, reps[0][0])
@@ -353,7 +358,14 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
         kp, vp, q, out = reps[i % len(reps)]
         if ev is not None:
             ev[0].record(stream)
-        if Q == 1:
+        if fp8:
+            check(lib.pkv_paged_attention_multi_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                    tab.data_ptr(), lens.data_ptr(), ctypes.c_float(D ** -0.5),
+                                                    ctypes.c_float(ks), ctypes.c_float(vs), S, Q, H, t.max_blocks,
+                                                    dref, ws.data_ptr(), wsb, sp), "paged_attention_multi_fp8")
+            if ev is not None:
+                ev[1].record(stream)
+        elif Q == 1:
             check(lib.pkv_decode_partitions(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), tab.data_ptr(),
                                             lens.data_ptr(), ctypes.c_float(D ** -0.5), S, H, t.max_blocks, dref, 0,
                                             ws.data_ptr(), wsb, sp), "decode_partitions")
@@ -384,7 +396,7 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     L = t.context_lens.astype(np.int64)
-    kv = int(L.sum()) * Hkv * D * 2 * dsize
+    kv = int(L.sum()) * Hkv * D * 2 * kvsize
     nbytes = kv + 2 * S * Q * H * D * dsize + int((-(-L // B)).sum()) * 4 + S * 4
     kern_mean_ms = float(np.mean(kern_ms))
     achieved = nbytes / (kern_mean_ms * 1e-3) / 1e9
@@ -393,13 +405,16 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
         "metric": "paged attention, several query rows per KV head: achieved HBM GB/s + KV tokens/s",
         "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype, "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": t.dtype + (" (K/V e4m3)" if fp8 else ""), "data": "synthetic",
         "config": {"workload": f"{args.config}: {S} seqs, {H} query heads over {Hkv} KV heads x {D}, {Q} query "
-                               f"token(s) per sequence, B={B}, context_len {describe_lengths(t)}",
+                               f"token(s) per sequence, B={B}, context_len {describe_lengths(t)}"
+                               + (", e4m3 pools (scales 1/60)" if fp8 else ""),
                    "global_batch": S, "kv_tokens": t.kv_tokens(), "query_rows_per_kv_head": G * Q,
                    "parallelism": "none (1 GPU)"},
         "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
-        "roofline": {"kernel": "decode_group_kernel" + (" + merge" if Q > 1 else ""), "bound": "hbm",
+        "roofline": {"kernel": "decode_group_kernel" + (" (e4m3 K/V) + merge" if fp8 else " + merge" if Q > 1 else ""),
+                     "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2)},

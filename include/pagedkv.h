@@ -396,7 +396,10 @@ pkv_status pkv_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, 
  * and out-of-pool contexts and the output rounding are those of
  * pkv_paged_attention_decode (balanced split, then the merge pass).
  *   out, q        [num_seqs][num_heads][head_dim] 16-bit (p->dtype)
- *   num_heads     == Hkv and head_dim 128, else PKV_ERR_UNSUPPORTED
+ *   num_heads     a multiple of Hkv, at most 16 query heads per KV head
+ *                 (grouped-query heads run on the matrix-core kernel, with
+ *                 the codes widened to the 16-bit type in registers);
+ *                 head_dim 128; else PKV_ERR_UNSUPPORTED
  *   k_scale, v_scale  as for pkv_reshape_and_cache_fp8
  *   workspace     >= pkv_fp8_decode_workspace_bytes(...) bytes, 256-byte aligned
  * pkv_fp8_decode_workspace_bytes returns 0 for invalid or unsupported
@@ -430,6 +433,22 @@ pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const
                                                  float scale, float k_scale, float v_scale, int32_t num_seqs,
                                                  int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
                                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_paged_attention_multi_fp8 -- pkv_paged_attention_multi over e4m3 pools
+ * (several query tokens per sequence, causal, grouped-query heads allowed),
+ * with the scales of pkv_paged_attention_decode_fp8.  Same layouts, rules and
+ * restrictions as pkv_paged_attention_multi; workspace >=
+ * pkv_fp8_multi_workspace_bytes(...) bytes (0 for invalid or unsupported
+ * arguments).
+ */
+size_t pkv_fp8_multi_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_pool *p);
+pkv_status pkv_paged_attention_multi_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                         const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                         float k_scale, float v_scale, int32_t num_seqs, int32_t num_queries,
+                                         int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

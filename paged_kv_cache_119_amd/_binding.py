@@ -41,6 +41,8 @@ EXPORTS = (
     "pkv_fp8_decode_workspace_bytes",
     "pkv_paged_attention_decode_fp8",
     "pkv_paged_attention_decode_append_fp8",
+    "pkv_fp8_multi_workspace_bytes",
+    "pkv_paged_attention_multi_fp8",
 )
 
 
@@ -105,6 +107,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_fp8_decode_workspace_bytes": (sz, [i32, i32, i32, pool]),
         "pkv_paged_attention_decode_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                                           ctypes.c_float, i32, i32, i32, pool, vp, sz, vp]),
+        "pkv_fp8_multi_workspace_bytes": (sz, [i32, i32, i32, i32, pool]),
+        "pkv_paged_attention_multi_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                                         ctypes.c_float, i32, i32, i32, i32, pool, vp, sz, vp]),
         "pkv_paged_attention_decode_append_fp8": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                                                  ctypes.c_float, ctypes.c_float, i32, i32, i32, pool,
                                                                  vp, sz, vp]),
@@ -463,6 +468,48 @@ def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, sc
                                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                             _stream_ptr(dev))
     _check(st, "pkv_paged_attention_decode_fp8")
+    return out
+
+
+def fp8_multi_workspace_bytes(num_seqs, num_queries, num_heads, max_blocks_per_seq, k_pool, dtype="f16") -> int:
+    N, H, B, D = (int(x) for x in k_pool.shape)
+    desc = make_pool_desc(N, B, H, D, dtype)
+    return int(load_library().pkv_fp8_multi_workspace_bytes(int(num_seqs), int(num_queries), int(num_heads),
+                                                            int(max_blocks_per_seq), ctypes.byref(desc)))
+
+
+def paged_attention_multi_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out=None,
+                              workspace=None, reuse_blocks=False):
+    """Several query tokens per sequence over e4m3 pools (see
+    paged_attention_multi): ``q`` [S, Q, H, D] 16-bit, returns ``out`` of the
+    same shape."""
+    torch = _torch()
+    lib = load_library()
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q), reuse_blocks)
+    dev = k_pool.device
+    _need(q, "q", ndim=4, device=dev)
+    S, Q, H, D = (int(x) for x in q.shape)
+    if D != desc.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {desc.head_dim}")
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("q, block_tables and context_lens disagree on the number of sequences")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, ndim=4, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    maxb = int(block_tables.shape[1])
+    if workspace is None:
+        need = fp8_multi_workspace_bytes(S, Q, H, maxb, k_pool, _dtype_name(q))
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.pkv_paged_attention_multi_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                           block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                                           float(k_scale), float(v_scale), S, Q, H, maxb, ctypes.byref(desc),
+                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                           _stream_ptr(dev))
+    _check(st, "pkv_paged_attention_multi_fp8")
     return out
 
 

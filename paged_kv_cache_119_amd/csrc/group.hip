@@ -24,9 +24,22 @@
 //  * O^T result for slice s: lane l holds dims 8(4(l/16) + i) + s of row l%16,
 //    so a lane ends with four runs of 8 consecutive dims of its row.
 // Each row's online softmax (max, sum) lives in the four lanes holding it.
+//
+// FP8 (e4m3) pools (F8): K and V codes are widened in registers to the query's
+// 16-bit type (every e4m3 value is exact in binary16 and bfloat16) and go
+// through the same products.  K: lane l loads bytes 32(l/16) .. +32 of token
+// l%16 and takes dims 32(l/16) + 8j .. +8 as k-slice j; the query fragment
+// uses the same dims (a dot product does not depend on how dims are assigned
+// to k-slots).  V: lane l loads bytes 8(l%16) .. +8 of tokens 4(l/16) + t.
+// The K scale is folded into the score scale, the V scale multiplies the V
+// sums when a piece is written.  The weighted V sum of e4m3 pools runs in
+// binary16 whatever the query type (V is exact in it, the weights round to
+// 11 bits as on the binary16 path): one product per slice.
 // The work split, the pipeline (table entries two chunks ahead, K/V/Q one
 // chunk ahead, arithmetic on the current chunk) and the partial results /
 // merge follow the balanced decode kernel; rows are (sequence, KV head).
+
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -38,7 +51,7 @@ namespace {
 
 constexpr int kGroupWaves = PKV_DECODE_WAVES;
 constexpr int GD = 128;  // head_dim of this path
-constexpr int GTC = 16;  // tokens per chunk
+constexpr int GTC = 16;  // tokens per MFMA tile (and per chunk of 16-bit pools)
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -63,6 +76,26 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)to16<DT>(a) | ((uint32_t)to16<DT>(b) << 16);
 }
 
+// Eight e4m3 codes (two dwords) -> eight values of the 16-bit type, exactly
+// (every e4m3 value is a binary16 and a bfloat16 value): gfx950's packed
+// conversions, two codes per instruction, with a unit scale.
+template <int DT>
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  if constexpr (DT == DT_F16) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+  } else {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+  }
+}
+
 // O^T += V^T * P^T for one 16-dim slice; p holds 4 weights as two packed
 // 16-bit pairs (f16: one product; bf16: the weights are split into a bf16
 // high part and a bf16 remainder, two products, so the weights keep 16 bits).
@@ -84,18 +117,31 @@ __device__ __forceinline__ f4_t mfma_pv(uint32_t v01, uint32_t v23, uint32_t p01
   }
 }
 
-template <int DT, int B, bool NT>
-struct GroupStream {
-  static constexpr int NE = GTC >= B ? GTC / B : 1;  // table entries per chunk
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-  struct Buf {
+template <int DT, int B, bool NT, bool F8>
+struct GroupStream {
+  // tokens per chunk: e4m3 chunks hold two 16-token tiles, so that a stage
+  // keeps as many bytes in flight as a 16-bit one
+  static constexpr int TC = F8 ? 2 * GTC : GTC;
+  static constexpr int NSUB = TC / GTC;
+  static constexpr int NE = TC >= B ? TC / B : 1;  // table entries per chunk
+
+  struct Buf16 {
     u32x4 k[4], v[4], q[4];
     bool bad;
   };
+  struct Buf8 {
+    u32x4 k[4];  // 32 codes of token r of each tile (k[2u], k[2u + 1]: tile u)
+    u32x2 v[8];  // 8 codes of each of tokens 4g .. 4g+3 of each tile (v[4u + t])
+    u32x4 q[4];
+    bool bad;
+  };
+  using Buf = typename std::conditional<F8, Buf8, Buf16>::type;
 
   // constants of the call
-  const uint16_t *kp;
-  const uint16_t *vp;
+  const char *kp;  // pools as bytes
+  const char *vp;
   const uint16_t *qp;
   const int32_t *tables;
   uint16_t *outp;
@@ -104,18 +150,18 @@ struct GroupStream {
   float *ws_o;
   int64_t blk_stride, num_blocks;
   int S, Hkv, H, maxb, nq, gq, M;
-  float scale_log2;
+  float scale_log2, v_scale;
   int lane, g, r;
   int64_t worker;
-  ChunkCursor<GTC> cur;  // the slice, chunk by chunk
+  ChunkCursor<TC> cur;  // the slice, chunk by chunk
   // running state of the current piece (row r of this lane)
   f4_t acc[8];
   float m, lp;
   bool bad;
 
   __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_, int lane_) {
-    kp = reinterpret_cast<const uint16_t *>(a.k_pool);
-    vp = reinterpret_cast<const uint16_t *>(a.v_pool);
+    kp = reinterpret_cast<const char *>(a.k_pool);
+    vp = reinterpret_cast<const char *>(a.v_pool);
     qp = reinterpret_cast<const uint16_t *>(a.q);
     tables = a.tables;
     outp = reinterpret_cast<uint16_t *>(a.out);
@@ -133,13 +179,14 @@ struct GroupStream {
     gq = a.H / a.Hkv;
     M = gq * nq;
     scale_log2 = a.scale_log2;
+    v_scale = a.v_scale;
     lane = lane_;
     g = lane >> 4;
     r = lane & 15;
   }
 
-  __device__ __forceinline__ static int first_block(int c) { return GTC >= B ? c * (GTC / B) : c / (B / GTC); }
-  __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * GTC) - 1) / B; }
+  __device__ __forceinline__ static int first_block(int c) { return TC >= B ? c * (TC / B) : c / (B / TC); }
+  __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * TC) - 1) / B; }
 
   // Stage 1: this lane's table entry of chunk d (clamped to the piece's last
   // block; tokens past it are masked).
@@ -151,14 +198,14 @@ struct GroupStream {
   // Base element offset of token t of chunk d (its block from the entries).
   __device__ __forceinline__ int64_t token_base(const Chunk &d, uint32_t e, int t, bool &bd) const {
     int blk, off;
-    if constexpr (GTC >= B) {
-      const int b0 = __builtin_amdgcn_readlane((int)e, 0);
-      const int b1 = __builtin_amdgcn_readlane((int)e, NE - 1);
-      blk = (t / B == 0) ? b0 : b1;  // NE <= 2 for the block sizes served (8, 16)
+    if constexpr (TC >= B) {
+      blk = __builtin_amdgcn_readlane((int)e, 0);
+#pragma unroll
+      for (int i = 1; i < NE; ++i) blk = (t / B == i) ? __builtin_amdgcn_readlane((int)e, i) : blk;
       off = t % B;
     } else {
       blk = __builtin_amdgcn_readlane((int)e, 0);
-      off = (d.c % (B / GTC)) * GTC + t;
+      off = (d.c % (B / TC)) * TC + t;
     }
     if (blk < 0 || (int64_t)blk >= num_blocks) {
       bd = true;
@@ -174,47 +221,57 @@ struct GroupStream {
   // traffic); they are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     bool bd = false;
-    const int last = d.L - 1 - d.c * GTC;  // token L - 1 relative to the chunk
-    const int64_t kb = token_base(d, e, min(r, last), bd) + 8 * g;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b.k[j] = ld_kv<NT>(kp + kb + 32 * j);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * r;
-      b.v[t] = ld_kv<NT>(vp + vb);
-    }
-    b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
+    const int last = d.L - 1 - d.c * TC;  // token L - 1 relative to the chunk
     // query row r of this KV head (rows >= M read row 0 and are zeroed)
     const int rr = r < M ? r : 0;
     const int qi = rr / gq, gi = rr - (rr / gq) * gq;
-    const int64_t qb = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD + 8 * g;
+    const int64_t qrow = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
+    if constexpr (F8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qb + 32 * j);
+      for (int u = 0; u < NSUB; ++u) {
+        const int64_t kb = token_base(d, e, min(GTC * u + r, last), bd) + 32 * g;
+        b.k[2 * u] = ld_kv<NT>(kp + kb);
+        b.k[2 * u + 1] = ld_kv<NT>(kp + kb + 16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t vb = token_base(d, e, min(GTC * u + 4 * g + t, last), bd) + 8 * r;
+          b.v[4 * u + t] = ld_kv8<NT>(vp + vb);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 32 * g + 8 * j);
+    } else {
+      const int64_t kb = token_base(d, e, min(r, last), bd) + 8 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.k[j] = ld_kv<NT>(kp + 2 * (kb + 32 * j));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * r;
+        b.v[t] = ld_kv<NT>(vp + 2 * vb);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
+    }
+    b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
   }
 
-  // Stage 3: scores, online softmax and the weighted V sum of chunk d.
-  __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
-    if (d.c == d.cb) {
-      m = kNegInf;
-      lp = 0.f;
-#pragma unroll
-      for (int s_ = 0; s_ < 8; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
-      bad = false;
-    }
-    bad = bad || b.bad;
+  // One 16-token tile starting at token t0: scores, online softmax and the
+  // weighted V sum.
+  __device__ __forceinline__ void tile(const Chunk &d, int t0, const u32x4 (&kk)[4], const u32x4 (&vv)[4],
+                                       const u32x4 (&q)[4]) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     f4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st = mfma_qk<DT>(b.k[j], r < M ? b.q[j] : zero, st);
+    for (int j = 0; j < 4; ++j) st = mfma_qk<DT>(kk[j], r < M ? q[j] : zero, st);
     // row r sees tokens [t_lo, min(t_hi, its causal limit))
-    const int t_lo = d.cb * GTC;
-    const int t_hi = min(d.L, d.ce * GTC);
+    const int t_lo = d.cb * TC;
+    const int t_hi = min(d.L, d.ce * TC);
     const int lim = r < M ? d.L - nq + 1 + r / gq : 0;
     const int t_row = min(t_hi, lim);
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = d.c * GTC + 4 * g + i;
+      const int tok = t0 + 4 * g + i;
       sc[i] = (tok >= t_lo && tok < t_row) ? st[i] * scale_log2 : kNegInf;
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -228,22 +285,23 @@ struct GroupStream {
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mref);  // -inf gives 0
     lp = lp * alpha + (p[0] + p[1]) + (p[2] + p[3]);
     m = mnew;
+    constexpr int PT = F8 ? DT_F16 : DT;  // type of the weighted V sum's operands
     uint32_t p01, p23, r01 = 0, r23 = 0;
-    if constexpr (DT == DT_F16) {
-      p01 = pack2<DT>(p[0], p[1]);
-      p23 = pack2<DT>(p[2], p[3]);
+    if constexpr (PT == DT_F16) {
+      p01 = pack2<PT>(p[0], p[1]);
+      p23 = pack2<PT>(p[2], p[3]);
     } else {
-      p01 = pack2<DT>(p[0], p[1]);
-      p23 = pack2<DT>(p[2], p[3]);
-      r01 = pack2<DT>(p[0] - lo16<DT>(p01), p[1] - hi16<DT>(p01));
-      r23 = pack2<DT>(p[2] - lo16<DT>(p23), p[3] - hi16<DT>(p23));
+      p01 = pack2<PT>(p[0], p[1]);
+      p23 = pack2<PT>(p[2], p[3]);
+      r01 = pack2<PT>(p[0] - lo16<PT>(p01), p[1] - hi16<PT>(p01));
+      r23 = pack2<PT>(p[2] - lo16<PT>(p23), p[3] - hi16<PT>(p23));
     }
     // V rows of tokens outside [t_lo, t_hi) are zeroed (unused slots may hold NaN)
     u32x4 v[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int tok = d.c * GTC + 4 * g + t;
-      v[t] = (tok >= t_lo && tok < t_hi) ? b.v[t] : zero;
+      const int tok = t0 + 4 * g + t;
+      v[t] = (tok >= t_lo && tok < t_hi) ? vv[t] : zero;
     }
 #pragma unroll
     for (int s_ = 0; s_ < 8; ++s_) {
@@ -252,7 +310,36 @@ struct GroupStream {
       const uint32_t sel = (s_ & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t v01 = __builtin_amdgcn_perm(v[1][s_ >> 1], v[0][s_ >> 1], sel);
       const uint32_t v23 = __builtin_amdgcn_perm(v[3][s_ >> 1], v[2][s_ >> 1], sel);
-      acc[s_] = mfma_pv<DT>(v01, v23, p01, p23, r01, r23, acc[s_]);
+      acc[s_] = mfma_pv<PT>(v01, v23, p01, p23, r01, r23, acc[s_]);
+    }
+  }
+
+  // Stage 3: scores, online softmax and the weighted V sum of chunk d.
+  __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
+    if (d.c == d.cb) {
+      m = kNegInf;
+      lp = 0.f;
+#pragma unroll
+      for (int s_ = 0; s_ < 8; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
+      bad = false;
+    }
+    bad = bad || b.bad;
+#pragma unroll
+    for (int u = 0; u < NSUB; ++u) {
+      u32x4 kk[4], vv[4];  // K and V fragments of tile u in the 16-bit type
+      if constexpr (F8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          kk[j] = widen8<DT>(b.k[2 * u + (j >> 1)][2 * (j & 1)], b.k[2 * u + (j >> 1)][2 * (j & 1) + 1]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vv[t] = widen8<DT_F16>(b.v[4 * u + t][0], b.v[4 * u + t][1]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kk[j] = b.k[j];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vv[t] = b.v[t];
+      }
+      tile(d, d.c * TC + GTC * u, kk, vv, b.q);
     }
     if (d.c == d.ce - 1) finish_piece(d);
   }
@@ -263,7 +350,11 @@ struct GroupStream {
     if (r >= M) return;
     const int qi = r / gq, gi = r - (r / gq) * gq;
     const float nanv = bad ? __builtin_nanf("") : 0.f;
-    if (d.cb == 0 && d.ce * GTC >= d.L) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int s_ = 0; s_ < 8; ++s_) acc[s_] *= v_scale;
+    }
+    if (d.cb == 0 && d.ce * TC >= d.L) {
       // the whole row: final output, four runs of 8 dims per lane
       uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
       const float inv = 1.f / lp;
@@ -329,9 +420,9 @@ struct GroupStream {
   }
 };
 
-template <int DT, int B, int NW, bool NT>
+template <int DT, int B, int NW, bool NT, bool F8>
 __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
-  using ST = GroupStream<DT, B, NT>;
+  using ST = GroupStream<DT, B, NT, F8>;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -339,7 +430,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) build_cost_prefix<GTC>(a, a.Hkv, cum, lens, lane, a.nq);
+  if (wave == 0) build_cost_prefix<ST::TC>(a, a.Hkv, cum, lens, lane, a.nq);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
@@ -366,7 +457,8 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
 // lanes x 32 dims): rows of empty or invalid contexts, and the LSE merge of
 // rows cut over several workers.  The pieces' (m, l) and o rows are fetched
 // four pieces per round of loads.
-template <int DT>
+// TC: the chunk length of the split pass that wrote the partials.
+template <int DT, int TC>
 __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
@@ -393,7 +485,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     }
     return;
   }
-  const int nch = (L + GTC - 1) / GTC;
+  const int nch = (L + TC - 1) / TC;
   const uint64_t seg = cum_s + (uint64_t)h * nch;
   const uint64_t end = seg + nch;
   const uint64_t slice = slice_of(total, a.G);
@@ -447,24 +539,31 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
 }
 
+template <int DT, int B, bool NT, bool F8>
+void go_group(const DecodeParams &a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, NT, F8>), dim3(a.G / kGroupWaves),
+                     dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
+}
+
 template <int DT, int B>
 hipError_t launch_group(const DecodeParams &a, hipStream_t st) {
-  if (a.stream_kv)
-    hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, true>), dim3(a.G / kGroupWaves),
-                       dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
-  else
-    hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, false>), dim3(a.G / kGroupWaves),
-                       dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
+  if (a.fp8) {
+    if (a.stream_kv) go_group<DT, B, true, true>(a, st);
+    else go_group<DT, B, false, true>(a, st);
+  } else {
+    if (a.stream_kv) go_group<DT, B, true, false>(a, st);
+    else go_group<DT, B, false, false>(a, st);
+  }
   return hipGetLastError();
 }
 
-template <int DT, bool NT>
+template <int DT, bool NT, bool F8>
 const void *group_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves, NT>);
-    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves, NT>);
-    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves, NT>);
-    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves, NT>);
+    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves, NT, F8>);
+    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves, NT, F8>);
+    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves, NT, F8>);
+    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves, NT, F8>);
     default: return nullptr;
   }
 }
@@ -475,9 +574,13 @@ size_t group_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *group_kernel(int dtype, int block_size, int nt) {
-  if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true>(block_size) : group_ptr<DT_BF16, true>(block_size);
-  return dtype == DT_F16 ? group_ptr<DT_F16, false>(block_size) : group_ptr<DT_BF16, false>(block_size);
+const void *group_kernel(int dtype, int block_size, int nt, int fp8) {
+  if (fp8) {
+    if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, true>(block_size) : group_ptr<DT_BF16, true, true>(block_size);
+    return dtype == DT_F16 ? group_ptr<DT_F16, false, true>(block_size) : group_ptr<DT_BF16, false, true>(block_size);
+  }
+  if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, false>(block_size) : group_ptr<DT_BF16, true, false>(block_size);
+  return dtype == DT_F16 ? group_ptr<DT_F16, false, false>(block_size) : group_ptr<DT_BF16, false, false>(block_size);
 }
 
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream) {
@@ -499,10 +602,16 @@ hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream) {
   if (a.S == 0) return hipSuccess;
   const int64_t groups = (int64_t)a.S * a.Hkv;  // one wavefront per (sequence, KV head)
   const int grid = (int)((groups + 3) / 4);
-  if (a.dtype == DT_F16)
-    hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+  if (a.fp8) {
+    if (a.dtype == DT_F16)
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, 2 * GTC>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16, 2 * GTC>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (a.dtype == DT_F16) {
+    hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, GTC>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16, GTC>), dim3(grid), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

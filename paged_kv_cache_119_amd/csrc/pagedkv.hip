@@ -84,18 +84,18 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
-  const size_t lds = align_up(fp8     ? pkv::fp8_lds_bytes(num_seqs)
-                              : group ? pkv::group_lds_bytes(num_seqs)
-                                      : pkv::balanced_lds_bytes(num_seqs),
+  const size_t lds = align_up(group ? pkv::group_lds_bytes(num_seqs)
+                              : fp8 ? pkv::fp8_lds_bytes(num_seqs)
+                                    : pkv::balanced_lds_bytes(num_seqs),
                               4096);
   // the smallest occupancy over the instances a call may launch (fused append
   // or not, streamed or cached K/V loads), so that the split and merge passes
   // agree on the worker count whatever the entry point and pool flags
   int nb = 1 << 30;
   for (int nt = 0; nt < 2; ++nt) {
-    const void *k = fp8     ? pkv::fp8_kernel(p->dtype, p->block_size, nt)
-                    : group ? pkv::group_kernel(p->dtype, p->block_size, nt)
-                            : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1, nt);
+    const void *k = group ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
+                    : fp8 ? pkv::fp8_kernel(p->dtype, p->block_size, nt)
+                          : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1, nt);
     if (!k) return 0;
     const int b = kernel_blocks_per_cu(dev, k, lds);
     if (b <= 0) return 0;
@@ -128,7 +128,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   const int unit = partition_unit(p);
   *lay = Layout{};
   const int32_t rows = (num_heads / p->num_kv_heads) * num_queries;  // query rows per KV head
-  if (fp8 && (rows != 1 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs))
+  if (fp8 && (p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs))
     return PKV_ERR_UNSUPPORTED;
   if (rows > 1) {
     // several query rows per KV head: the matrix-core kernel, balanced split only
@@ -262,7 +262,7 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
 hipError_t launch_split(const pkv::DecodeParams &a, hipStream_t stream) {
-  if (a.fp8) return pkv::launch_fp8_decode(a, stream);
+  if (a.fp8 && !a.group) return pkv::launch_fp8_decode(a, stream);
   return a.group ? pkv::launch_group_decode(a, stream) : pkv::launch_decode_partitions(a, stream);
 }
 
@@ -281,7 +281,8 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, a, 1, fp8);
   if (st != PKV_OK || num_seqs == 0) return st;
-  if (a->group) return PKV_ERR_UNSUPPORTED;  // one query row per KV head only
+  // the 16-bit step appends inside the split pass: one query row per KV head only
+  if (a->group && !fp8) return PKV_ERR_UNSUPPORTED;
   if (!k_new || !v_new) return PKV_ERR_NULL;
   const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
   if (new_token_stride == 0) new_token_stride = row;
@@ -573,6 +574,31 @@ pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const
   const pkv_status s0 = hip_status(pkv::launch_append_last_fp8(a, 1.0f / k_scale, 1.0f / v_scale, (hipStream_t)stream));
   if (s0 != PKV_OK) return s0;
   a.append = 0;
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+size_t pkv_fp8_multi_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                     int32_t max_blocks_per_seq, const pkv_pool *p) {
+  Layout lay;
+  if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, 0, num_queries, &lay, true) != PKV_OK) return 0;
+  return lay.bytes;
+}
+
+pkv_status pkv_paged_attention_multi_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                         const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                         float k_scale, float v_scale, int32_t num_seqs, int32_t num_queries,
+                                         int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PKV_ERR_SHAPE;
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale, num_seqs,
+                                    num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, true, &a,
+                                    num_queries, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

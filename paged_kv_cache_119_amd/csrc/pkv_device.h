@@ -115,6 +115,14 @@ __device__ __forceinline__ u32x4 ld_kv(const void *p) {
   else return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// 8 bytes of a K/V row (FP8 pools), the same load policy.
+template <bool NT>
+__device__ __forceinline__ uint32_t __attribute__((ext_vector_type(2))) ld_kv8(const void *p) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+  else return *reinterpret_cast<const u32x2_t *>(p);
+}
+
 // 2^x on the hardware unit (v_exp_f32); 2^0 is exactly 1 and 2^-inf is 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -185,7 +185,8 @@ def test_fp8_sizes_and_validation(lib):
     g = lib.pkv_paged_attention_decode_fp8
     assert g(nul, nul, nul, nul, nul, nul, 0.1, 1.0, 1.0, 0, 4, 8, ctypes.byref(d), nul, 0, nul) == 0
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 0.0, 1.0, 4, 4, 8, ctypes.byref(d), nul, 0, nul) == 2
-    assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 8, 8, ctypes.byref(d), nul, 0, nul) == 3
+    assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 6, 8, ctypes.byref(d), nul, 0, nul) == 3
+    assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4 * 17, 8, ctypes.byref(d), nul, 0, nul) == 3
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4, 8, ctypes.byref(_desc(D=64)), nul, 0,
              nul) == 3
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4, 8, ctypes.byref(d), nul, 0, nul) == 4
@@ -196,7 +197,8 @@ def test_fp8_sizes_and_validation(lib):
     sec = -(-units * 4 // 256) * 256
     cum = -(-(S + 1) * 8 // 256) * 256
     assert w(S, H, maxb, ctypes.byref(d)) == cum + 2 * sec + -(-units * 128 * 4 // 256) * 256
-    assert w(S, 8, maxb, ctypes.byref(d)) == 0                     # grouped heads: not served
+    # grouped heads: the matrix-core layout (16-token chunks, partials per query row)
+    assert w(S, 8, maxb, ctypes.byref(d)) == lib.pkv_multi_workspace_bytes(S, 1, 8, maxb, ctypes.byref(d))
 
 
 def test_product_path_never_imports_the_oracle():

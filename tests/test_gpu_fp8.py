@@ -286,7 +286,7 @@ def test_fp8_unsupported_shapes_are_rejected():
     c = _case([20, 30], 2, 16, seed=380)
     tab = torch.from_numpy(c["tables"]).to(DEV)
     lens = torch.from_numpy(c["lens"]).to(DEV)
-    q = normal_16bit((2, 4, D), "f16", DEV, 381)  # 4 query heads over 2 KV heads
+    q = normal_16bit((2, 34, D), "f16", DEV, 381)  # 17 query heads per KV head
     with pytest.raises(pkv.PagedKVError):
         pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, 0.1, 1.0, 1.0)
     q = normal_16bit((2, 2, D), "f16", DEV, 382)

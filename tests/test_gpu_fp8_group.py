@@ -1,0 +1,163 @@
+"""GPU: FP8 (e4m3) pools with several query rows per KV head (grouped-query
+heads, multi-token queries) on the matrix-core kernel, against the float64
+oracle."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_119_amd as pkv  # noqa: E402
+from oracle import paged_oracle as po  # noqa: E402
+from synth import FP8_NAN, normal_16bit, random_e4m3, to_bits  # noqa: E402
+
+from .gpu_util import DEV, assert_close, log  # noqa: E402
+
+D = 128
+
+
+def _codes(x):
+    return x.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def _case(lengths, Hkv, B, seed, slack=3, exp_lo=0, exp_hi=15):
+    rng = np.random.default_rng(seed)
+    nb = [-(-L // B) for L in lengths]
+    N = sum(nb) + slack
+    perm = rng.permutation(N)
+    maxb = max(max(nb), 1)
+    tables = np.full((len(lengths), maxb), -1, np.int32)
+    live = np.zeros((N, B), bool)
+    c = 0
+    for s, L in enumerate(lengths):
+        tables[s, :nb[s]] = perm[c:c + nb[s]]
+        for j in range(L):
+            live[perm[c + j // B], j % B] = True
+        c += nb[s]
+    kp = random_e4m3((N, Hkv, B, D), DEV, seed * 4 + 1, exp_lo, exp_hi)
+    vp = random_e4m3((N, Hkv, B, D), DEV, seed * 4 + 2, exp_lo, exp_hi)
+    dead = torch.from_numpy(~live).to(DEV)[:, None, :, None].expand(kp.shape)
+    for pool in (kp, vp):
+        pool.masked_fill_(dead, FP8_NAN)
+    return dict(kp=kp, vp=vp, tables=tables, lens=np.asarray(lengths, np.int32), B=B)
+
+
+def _run(c, q, scale, ks, vs, reuse=False):
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    if q.dim() == 3:
+        return pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, scale, ks, vs, reuse_blocks=reuse)
+    return pkv.paged_attention_multi_fp8(q, c["kp"], c["vp"], tab, lens, scale, ks, vs, reuse_blocks=reuse)
+
+
+def _oracle(c, q, scale, ks, vs, dtype):
+    qb = to_bits(q)
+    if qb.ndim == 3:
+        qb = qb[:, None]
+    ref = po.decode_rows_fp8(qb, _codes(c["kp"]), _codes(c["vp"]), c["tables"], c["lens"], scale, c["B"], dtype,
+                             ks, vs)
+    return ref[:, 0] if q.dim() == 3 else ref
+
+
+LENGTHS = [1, 15, 16, 17, 31, 33, 64, 100, 255, 256, 257, 511, 700, 1025, 40, 3]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+@pytest.mark.parametrize("G,Q", [(8, 1), (4, 1), (16, 1), (1, 4), (2, 4), (1, 16), (3, 2)])
+def test_fp8_rows_small_shapes(dtype, B, G, Q):
+    Hkv = 2
+    lengths = [max(L, Q) for L in LENGTHS]
+    c = _case(lengths, Hkv, B, seed=2000 + 10 * B + G + 100 * Q)
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 177 + G + Q)
+    ks, vs = 0.004, 0.006
+    out = _run(c, q, D ** -0.5, ks, vs)
+    torch.cuda.synchronize()
+    assert_close(to_bits(out), _oracle(c, q, D ** -0.5, ks, vs, dtype), dtype, f"fp8 rows G={G} Q={Q} {dtype} B={B}")
+
+
+def test_fp8_grouped_query_llama70b_shape_sampled():
+    """64 sequences, 64 query heads over 8 KV heads, bf16 queries, e4m3 pools,
+    B=16, lognormal lengths up to 2048; sampled sequences against the oracle."""
+    log("fp8 gqa llama-70b shape: 64 seqs, 64 q heads / 8 kv heads")
+    rng = np.random.default_rng(251)
+    lengths = [int(x) for x in np.clip(np.rint(np.exp(rng.normal(np.log(300), 1.0, 64))), 1, 2048)]
+    c = _case(lengths, 8, 16, seed=251, exp_lo=8, exp_hi=14)
+    q = normal_16bit((64, 64, D), "bf16", DEV, 252)
+    out = _run(c, q, D ** -0.5, 1 / 60, 1 / 60)
+    torch.cuda.synchronize()
+    pick = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), *[int(x) for x in rng.integers(0, 64, 6)]})
+    sub = dict(c)
+    sub["tables"] = c["tables"][pick]
+    sub["lens"] = c["lens"][pick]
+    ref = _oracle(sub, q[pick], D ** -0.5, 1 / 60, 1 / 60, "bf16")
+    assert_close(to_bits(out)[pick], ref, "bf16", f"fp8 gqa 64/8 ({len(pick)} sequences)")
+
+
+def test_fp8_rows_edge_cases_and_policy():
+    """L == 0 gives zeros; L < Q and an out-of-pool entry give NaN rows; the
+    other rows are unaffected; streamed and cached loads agree bit for bit."""
+    Q, Hkv, G = 4, 2, 2
+    lengths = [0, 2, 37, 80, 5]
+    c = _case([max(L, 1) for L in lengths], Hkv, 16, seed=261)
+    c["lens"] = np.asarray(lengths, np.int32)
+    c["tables"][3, 2] = 10 ** 6
+    q = normal_16bit((len(lengths), Q, Hkv * G, D), "f16", DEV, 262)
+    o1 = _run(c, q, D ** -0.5, 0.01, 0.02)
+    o2 = _run(c, q, D ** -0.5, 0.01, 0.02, reuse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    out = po.bits_to_f64(to_bits(o1), "f16")
+    assert np.all(out[0] == 0)
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
+    good = [2, 4]
+    sub = dict(c)
+    sub["tables"] = c["tables"][good]
+    sub["lens"] = c["lens"][good]
+    ref = _oracle(sub, q[good], D ** -0.5, 0.01, 0.02, "f16")
+    assert_close(to_bits(o1)[good], ref, "f16", "fp8 rows edge: valid sequences")
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 8)])
+def test_fp8_grouped_fused_append(dtype, B):
+    """The FP8 decode step with grouped-query heads: the codes equal the
+    oracle's append, the output equals the oracle's append-then-attend and the
+    separate append + decode bit for bit."""
+    lengths = [1, 31, 32, 33, 200, 77, 1025, 64]
+    Hkv, G = 2, 4
+    c = _case(lengths, Hkv, B, seed=271 + B)
+    S = len(lengths)
+    kn = normal_16bit((S, Hkv, D), dtype, DEV, 272)
+    vn = normal_16bit((S, Hkv, D), dtype, DEV, 273)
+    q = normal_16bit((S, Hkv * G, D), dtype, DEV, 274)
+    ks, vs = 0.02, 0.03
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    kw, vw = _codes(c["kp"]).copy(), _codes(c["vp"]).copy()
+    k1, v1 = c["kp"].clone(), c["vp"].clone()
+    out = pkv.paged_attention_decode_append_fp8(q, kn, vn, k1, v1, tab, lens, D ** -0.5, ks, vs)
+    slots = np.array([int(c["tables"][s, (L - 1) // B]) * B + (L - 1) % B for s, L in enumerate(lengths)], np.int64)
+    k2, v2 = c["kp"].clone(), c["vp"].clone()
+    pkv.reshape_and_cache_fp8(kn, vn, k2, v2, torch.from_numpy(slots).to(DEV), ks, vs)
+    out2 = pkv.paged_attention_decode_fp8(q, k2, v2, tab, lens, D ** -0.5, ks, vs)
+    torch.cuda.synchronize()
+    po.reshape_and_cache_fp8(to_bits(kn), to_bits(vn), kw, vw, slots, B, dtype, ks, vs)
+    assert np.array_equal(_codes(k1), kw) and np.array_equal(_codes(v1), vw)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    ref = po.decode_rows_fp8(to_bits(q)[:, None], kw, vw, c["tables"], c["lens"], D ** -0.5, B, dtype, ks, vs)[:, 0]
+    assert_close(to_bits(out), ref, dtype, f"fp8 gqa fused append {dtype} B={B}")
+
+
+def test_fp8_rows_unsupported_shapes_are_rejected():
+    c = _case([20, 30], 2, 16, seed=281)
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    q = normal_16bit((2, 34, D), "f16", DEV, 282)  # 17 query heads per KV head
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, 0.1, 1.0, 1.0)
+    q = normal_16bit((2, 2, 3, D), "f16", DEV, 283)  # 3 query heads over 2 KV heads
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_multi_fp8(q, c["kp"], c["vp"], tab, lens, 0.1, 1.0, 1.0)
