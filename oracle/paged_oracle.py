@@ -18,6 +18,8 @@ Pages cited (titles as printed on each page):
   gather (sections "KV Cache 如何按块分配", "“逐个 block 做 gather”具体执行什么",
   "vLLM 内核里的缓解写法").
 * [LP] "PagedAttention 与 vLLM 推理加速" (lpnh.cn), section 2.3.
+* [CB] the wiblog.cn article on vLLM paged attention and continuous batching,
+  section 局限与未解决的问题.
 
 Readings taken where the pages are silent or garbled (all listed in the design doc):
 
@@ -37,6 +39,11 @@ Readings taken where the pages are silent or garbled (all listed in the design doc):
 * A partition's partial result is (m, l, o~) with m the max score, l the sum of
   exp(z - m) and o~ the exp(z - m)-weighted V sum; partitions are merged by the
   log-sum-exp rule (the pages name the segment reduction but print no formula).
+* FP8 cache ([PA] 总结 item 6 names it, [CB] 局限与未解决的问题 leaves the
+  quantisation choices open; no page fixes a format): OCP e4m3 codes, one
+  float32 scale per pool, code = nearest e4m3 value of x * float32(1 / scale)
+  (the product rounded to float32; ties to the even code; saturating at 448;
+  NaN kept); a code c stands for e4m3(c) * scale.
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 against brute force, closed forms, library special cases or the pages' worked

@@ -39,6 +39,11 @@
 //    NaN in unused slots cannot leak.
 //  * The accumulation order depends only on logical positions, so results are
 //    bitwise independent of where blocks sit in the pool.
+//
+// Both ways read K/V with non-temporal loads (each row is read once per call)
+// unless the pool carries the reuse hint (blocks shared between sequences,
+// whose later readers can then hit the last-level cache).  The load policy
+// never changes a result bit.
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
