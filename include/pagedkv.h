@@ -229,9 +229,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *                 Llama-2-70B shape of the iaim.asia block-table article,
  *                 "末尾块的内部碎片").  With more than one query head per KV
  *                 head the matrix-core kernel runs: head_dim 128,
- *                 partition_size 0 and at most 16 query heads per KV head,
- *                 else PKV_ERR_UNSUPPORTED; the fused-append entry points
- *                 need num_heads == Hkv.
+ *                 partition_size 0, at most 16 query heads per KV head and
+ *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED; the 16-bit
+ *                 fused-append entry points need num_heads == Hkv.
  *   out           must be 16-byte aligned
  *   workspace     >= pkv_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                 may be NULL only when that size is 0
@@ -343,7 +343,7 @@ pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_
  *                 the pool; out 16-byte aligned
  *   num_heads     a multiple of Hkv (as above); (num_heads / Hkv) *
  *                 num_queries <= 16 query rows per KV head, head_dim 128,
- *                 else PKV_ERR_UNSUPPORTED
+ *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED
  *   workspace     >= pkv_multi_workspace_bytes(...) bytes, 256-byte aligned
  * Rows of a sequence with 0 < L < num_queries (or an invalid L) are NaN (the
  * queries must be part of the context); L == 0 gives zero rows.  Runs a split
@@ -399,7 +399,7 @@ pkv_status pkv_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, 
  *   num_heads     a multiple of Hkv, at most 16 query heads per KV head
  *                 (grouped-query heads run on the matrix-core kernel, with
  *                 the codes widened to the 16-bit type in registers);
- *                 head_dim 128; else PKV_ERR_UNSUPPORTED
+ *                 head_dim 128; num_seqs <= 4096; else PKV_ERR_UNSUPPORTED
  *   k_scale, v_scale  as for pkv_reshape_and_cache_fp8
  *   workspace     >= pkv_fp8_decode_workspace_bytes(...) bytes, 256-byte aligned
  * pkv_fp8_decode_workspace_bytes returns 0 for invalid or unsupported
