@@ -182,7 +182,8 @@ pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pair
  *    every compute unit busy.  The cut points depend on the context lengths
  *    and on the device (compute units and occupancy), so results are
  *    identical run to run on one device and build.  Batches of more than
- *    4096 sequences fall back to fixed partitions of 512.
+ *    4096 sequences fall back to fixed partitions (partition_size 0 then
+ *    means: one partition when max_blocks_per_seq * B <= 512, else 512).
  *
  * pkv_decode_partition_size() returns the P a call uses: P > 0 for fixed
  * partitions, 0 for the balanced split, -1 if the arguments are invalid.

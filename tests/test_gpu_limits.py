@@ -1,0 +1,121 @@
+"""GPU: the largest batches each path serves.  4096 sequences is the most the
+balanced split keeps its per-sequence cost prefix for (in LDS); one more
+sequence falls back to fixed partitions of 512 tokens on the 16-bit MHA
+path and is rejected on the matrix-core and FP8 paths."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_119_amd as pkv  # noqa: E402
+from oracle import paged_oracle as po  # noqa: E402
+from synth import FP8_NAN, normal_16bit, random_e4m3, to_bits  # noqa: E402
+
+from .gpu_util import DEV, assert_close, log  # noqa: E402
+
+D = 128
+B = 16
+
+
+def _tables(S, seed, max_len=64):
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(1, max_len + 1, S).astype(np.int32)
+    nb = -(-lengths // B)
+    N = int(nb.sum()) + 8
+    perm = rng.permutation(N)
+    maxb = int(nb.max())
+    tables = np.full((S, maxb), -1, np.int32)
+    c = 0
+    for s in range(S):
+        tables[s, :nb[s]] = perm[c:c + nb[s]]
+        c += nb[s]
+    return lengths, tables, N
+
+
+def _sample(S, seed):
+    rng = np.random.default_rng(seed)
+    return sorted({0, S - 1, *[int(x) for x in rng.integers(0, S, 40)]})
+
+
+# past the limit: fixed partitions of min(512, the table's context) tokens
+@pytest.mark.parametrize("S,expect_p", [(4096, 0), (4097, 64)])
+def test_mha_at_the_balanced_limit(S, expect_p):
+    log(f"mha limit: {S} sequences")
+    Hkv = 2
+    lens, tables, N = _tables(S, 400 + S)
+    kp = normal_16bit((N, Hkv, B, D), "f16", DEV, 401)
+    vp = normal_16bit((N, Hkv, B, D), "f16", DEV, 402)
+    q = normal_16bit((S, Hkv, D), "f16", DEV, 403)
+    tab = torch.from_numpy(tables).to(DEV)
+    ll = torch.from_numpy(lens).to(DEV)
+    assert pkv.decode_partition_size(S, Hkv, tables.shape[1], kp, 0) == expect_p
+    out = pkv.paged_attention_decode(q, kp, vp, tab, ll, D ** -0.5)
+    torch.cuda.synchronize()
+    ob = to_bits(out)
+    assert np.all(np.isfinite(po.bits_to_f64(ob, "f16")))
+    pick = _sample(S, 404)
+    ref = po.decode_rows(to_bits(q)[pick][:, None], to_bits(kp), to_bits(vp), tables[pick], lens[pick], D ** -0.5, B,
+                         "f16")[:, 0]
+    assert_close(ob[pick], ref, "f16", f"mha {S} sequences ({len(pick)} sampled)")
+
+
+def test_grouped_rows_at_the_limit():
+    S, Hkv, G = 4096, 2, 4
+    log(f"grouped rows limit: {S} sequences")
+    lens, tables, N = _tables(S, 410)
+    kp = normal_16bit((N, Hkv, B, D), "bf16", DEV, 411)
+    vp = normal_16bit((N, Hkv, B, D), "bf16", DEV, 412)
+    q = normal_16bit((S, Hkv * G, D), "bf16", DEV, 413)
+    tab = torch.from_numpy(tables).to(DEV)
+    ll = torch.from_numpy(lens).to(DEV)
+    out = pkv.paged_attention_decode(q, kp, vp, tab, ll, D ** -0.5)
+    torch.cuda.synchronize()
+    ob = to_bits(out)
+    assert np.all(np.isfinite(po.bits_to_f64(ob, "bf16")))
+    pick = _sample(S, 414)
+    ref = po.decode_rows(to_bits(q)[pick][:, None], to_bits(kp), to_bits(vp), tables[pick], lens[pick], D ** -0.5, B,
+                         "bf16")[:, 0]
+    assert_close(ob[pick], ref, "bf16", f"grouped rows {S} sequences ({len(pick)} sampled)")
+    # one more sequence: not served on this path
+    lens2, tables2, N2 = _tables(S + 1, 415)
+    kp2 = normal_16bit((N2, Hkv, B, D), "bf16", DEV, 416)
+    q2 = normal_16bit((S + 1, Hkv * G, D), "bf16", DEV, 417)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_decode(q2, kp2, kp2, torch.from_numpy(tables2).to(DEV), torch.from_numpy(lens2).to(DEV),
+                                   D ** -0.5)
+
+
+def test_fp8_at_the_limit():
+    S, Hkv = 4096, 2
+    log(f"fp8 limit: {S} sequences")
+    lens, tables, N = _tables(S, 420)
+    live = np.zeros((N, B), bool)
+    for s in range(S):
+        for j in range(int(lens[s])):
+            live[tables[s, j // B], j % B] = True
+    kp = random_e4m3((N, Hkv, B, D), DEV, 421, 0, 15)
+    vp = random_e4m3((N, Hkv, B, D), DEV, 422, 0, 15)
+    dead = torch.from_numpy(~live).to(DEV)[:, None, :, None].expand(kp.shape)
+    for pool in (kp, vp):
+        pool.masked_fill_(dead, FP8_NAN)
+    q = normal_16bit((S, Hkv, D), "f16", DEV, 423)
+    tab = torch.from_numpy(tables).to(DEV)
+    ll = torch.from_numpy(lens).to(DEV)
+    out = pkv.paged_attention_decode_fp8(q, kp, vp, tab, ll, D ** -0.5, 0.004, 0.006)
+    torch.cuda.synchronize()
+    ob = to_bits(out)
+    assert np.all(np.isfinite(po.bits_to_f64(ob, "f16")))
+    pick = _sample(S, 424)
+    kc = kp.cpu().numpy()
+    vc = vp.cpu().numpy()
+    ref = po.decode_rows_fp8(to_bits(q)[pick][:, None], kc, vc, tables[pick], lens[pick], D ** -0.5, B, "f16",
+                             0.004, 0.006)[:, 0]
+    assert_close(ob[pick], ref, "f16", f"fp8 {S} sequences ({len(pick)} sampled)")
+    with pytest.raises(pkv.PagedKVError):
+        q2 = normal_16bit((S + 1, Hkv, D), "f16", DEV, 425)
+        t2 = torch.from_numpy(np.concatenate([tables, tables[:1]])).to(DEV)
+        l2 = torch.from_numpy(np.concatenate([lens, lens[:1]])).to(DEV)
+        pkv.paged_attention_decode_fp8(q2, kp, vp, t2, l2, D ** -0.5, 0.004, 0.006)
