@@ -21,7 +21,7 @@ Pages cited (titles as printed on each page):
 * [CB] the wiblog.cn article on vLLM paged attention and continuous batching,
   section 局限与未解决的问题.
 
-Readings taken where the pages are silent or garbled (all listed in the design doc):
+Readings taken where the pages are silent or garbled:
 
 * The softmax denominator of the blockwise equation in [PA] 原理详解（二） is
   printed as the exp of a block's summed score; it is read as the ordinary
