@@ -231,8 +231,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  *                 "末尾块的内部碎片").  With more than one query head per KV
  *                 head the matrix-core kernel runs: head_dim 128,
  *                 partition_size 0, at most 16 query heads per KV head and
- *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED; the 16-bit
- *                 fused-append entry points need num_heads == Hkv.
+ *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED.  The
+ *                 fused-append entry points then run the append as its own
+ *                 launch (slots from the table) before the split pass.
  *   out           must be 16-byte aligned
  *   workspace     >= pkv_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                 may be NULL only when that size is 0
@@ -260,11 +261,12 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
  * in: equivalent to appending row s of k_new / v_new as token L_s - 1 of
  * every sequence with 1 <= L_s <= max_blocks_per_seq * B (pkv_slot_mapping
  * with pos = L_s - 1, then pkv_reshape_and_cache), followed by
- * pkv_paged_attention_decode -- in two launches instead of four.  The pool
- * slot of token L_s - 1 receives the new row bit for bit, and attention uses
- * the new row for that token ("PagedAttention 完全拆解", 原理详解（一）, Figure 6
- * walk-through: the new token's K/V goes into its block, then attention runs
- * over the blocks).
+ * pkv_paged_attention_decode -- in two launches instead of four (with more
+ * than one query head per KV head: three, the append as its own launch with
+ * slots from the table).  The pool slot of token L_s - 1 receives the new row
+ * bit for bit, and attention uses the new row for that token ("PagedAttention
+ * 完全拆解", 原理详解（一）, Figure 6 walk-through: the new token's K/V goes into
+ * its block, then attention runs over the blocks).
  *
  *   k_new, v_new  [num_seqs][Hkv][D], consecutive sequences new_token_stride
  *                 ELEMENTS apart (0 means Hkv * D); rows 16-byte aligned

@@ -10,6 +10,10 @@
 // Slot translation (iaim.asia block-table article, "KV Cache 如何按块分配",
 // BLOCK_SIZE=16 table): slot = block_tables[s][pos / B] * B + pos % B.
 //
+// The decode step's append from the block table: row s of the new-token K/V
+// becomes token L - 1 of sequence s, its slot found through the table (no
+// slot list); used where the append is not fused into the split pass.
+//
 // Block copy ("PagedAttention 完全拆解", 内存共享 and Figure 8: a sequence about
 // to write into a block it shares first gets a private copy of it): a batch
 // of (src, dst) pairs is copied in one launch.  A pool block holds all heads
@@ -86,7 +90,38 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *__restrict__
   *reinterpret_cast<u32x4 *>(vp + d_o) = vv;
 }
 
+// One thread per 16-byte piece of a (sequence, head) row, K and V; invalid
+// contexts and table entries outside the pool write nothing.
+__global__ __launch_bounds__(256) void append_last_kernel(DecodeParams a) {
+  const int vpr = a.D / 8;
+  const int64_t per_seq = (int64_t)a.Hkv * vpr;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.S * per_seq) return;
+  const int s = (int)(idx / per_seq);
+  const int r = (int)(idx - (int64_t)s * per_seq);
+  const int h = r / vpr;
+  const int piece = r - h * vpr;
+  const int L = a.lens[s];
+  if (L <= 0 || L > a.maxb * a.B) return;
+  const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
+  const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * a.D + piece * 8;
+  const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * a.D + piece * 8;
+  const u32x4 kv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
+  const u32x4 vv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
+  *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(const_cast<void *>(a.k_pool)) + dst) = kv;
+  *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(const_cast<void *>(a.v_pool)) + dst) = vv;
+}
+
 }  // namespace
+
+hipError_t launch_append_last(const DecodeParams &a, hipStream_t stream) {
+  const int64_t threads = (int64_t)a.S * a.Hkv * (a.D / 8);
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  hipLaunchKernelGGL(append_last_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
                               int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,

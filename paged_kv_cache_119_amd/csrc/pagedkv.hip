@@ -261,6 +261,16 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
+// Grouped rows take the append as its own launch (slots from the table)
+// before the matrix-core split pass; one row per KV head fuses it into the
+// split pass.
+pkv_status append_if_separate(pkv::DecodeParams *a, hipStream_t stream) {
+  if (!a->append || !a->group) return PKV_OK;
+  const pkv_status st = hip_status(pkv::launch_append_last(*a, stream));
+  a->append = 0;
+  return st;
+}
+
 hipError_t launch_split(const pkv::DecodeParams &a, hipStream_t stream) {
   if (a.fp8 && !a.group) return pkv::launch_fp8_decode(a, stream);
   return a.group ? pkv::launch_group_decode(a, stream) : pkv::launch_decode_partitions(a, stream);
@@ -281,8 +291,7 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, a, 1, fp8);
   if (st != PKV_OK || num_seqs == 0) return st;
-  // the 16-bit step appends inside the split pass: one query row per KV head only
-  if (a->group && !fp8) return PKV_ERR_UNSUPPORTED;
+
   if (!k_new || !v_new) return PKV_ERR_NULL;
   const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
   if (new_token_stride == 0) new_token_stride = row;
@@ -447,6 +456,8 @@ pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const voi
                                     max_blocks_per_seq, p, partition_size, workspace,
                                     workspace_bytes, &a);
   if (st != PKV_OK) return st;
+  const pkv_status s0 = append_if_separate(&a, (hipStream_t)stream);
+  if (s0 != PKV_OK) return s0;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));
@@ -465,6 +476,8 @@ pkv_status pkv_decode_partitions_append(void *out, const void *q, const void *k_
                                     max_blocks_per_seq, p, partition_size, workspace,
                                     workspace_bytes, &a);
   if (st != PKV_OK) return st;
+  const pkv_status s0 = append_if_separate(&a, (hipStream_t)stream);
+  if (s0 != PKV_OK) return s0;
   return hip_status(launch_split(a, (hipStream_t)stream));
 }
 

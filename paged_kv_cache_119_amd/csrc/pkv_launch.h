@@ -103,6 +103,10 @@ hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, c
                                     int32_t T, int32_t Hkv, int32_t B, int32_t D,
                                     int64_t num_blocks, hipStream_t stream);
 
+// The decode step's append of 16-bit rows, slots from the block table (the
+// append fields of `a`).
+hipError_t launch_append_last(const DecodeParams &a, hipStream_t stream);
+
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
                               int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
                               hipStream_t stream);

@@ -144,6 +144,39 @@ def test_rows_placement_and_run_to_run_bitwise():
     assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype,B,G", [("bf16", 16, 8), ("f16", 8, 4), ("f16", 64, 2)])
+def test_grouped_decode_step_with_append(dtype, B, G):
+    """One decode step with grouped-query heads and the append: the pool slots
+    receive the new rows bit for bit, and the output equals the oracle's
+    append-then-attend and the separate append + decode bit for bit."""
+    lengths = [1, 31, 32, 33, 200, 77, 1025, 64, 0]
+    Hkv = 2
+    c = _case([max(L, 1) for L in lengths], Hkv, B, dtype, seed=1300 + B + G)
+    c["lens"] = np.asarray(lengths, np.int32)
+    S = len(lengths)
+    kn = normal_16bit((S, Hkv, D), dtype, DEV, 1301)
+    vn = normal_16bit((S, Hkv, D), dtype, DEV, 1302)
+    q = normal_16bit((S, Hkv * G, D), dtype, DEV, 1303)
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    k1, v1 = c["kp"].clone(), c["vp"].clone()
+    out = pkv.paged_attention_decode_append(q, kn, vn, k1, v1, tab, lens, D ** -0.5)
+    slots = np.array([int(c["tables"][s, (L - 1) // B]) * B + (L - 1) % B if L > 0 else -1
+                      for s, L in enumerate(lengths)], np.int64)
+    k2, v2 = c["kp"].clone(), c["vp"].clone()
+    pkv.reshape_and_cache(kn, vn, k2, v2, torch.from_numpy(slots).to(DEV))
+    out2 = pkv.paged_attention_decode(q, k2, v2, tab, lens, D ** -0.5)
+    torch.cuda.synchronize()
+    kw, vw = to_bits(c["kp"]).copy(), to_bits(c["vp"]).copy()
+    po.reshape_and_cache(to_bits(kn), to_bits(vn), kw, vw, slots, B)
+    assert np.array_equal(to_bits(k1), kw) and np.array_equal(to_bits(v1), vw)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    sub = dict(c)
+    sub["kp"], sub["vp"] = k1, v1
+    ref = _oracle(sub, q, D ** -0.5, dtype)
+    assert_close(to_bits(out), ref, dtype, f"grouped step with append {dtype} B={B} G={G}")
+
+
 def test_rows_unsupported_shapes_are_rejected():
     c = _case([20, 30], 2, 16, "f16", seed=81)
     tab = torch.from_numpy(c["tables"]).to(DEV)
@@ -154,9 +187,6 @@ def test_rows_unsupported_shapes_are_rejected():
     q = normal_16bit((2, 4, D), "f16", DEV, 83)
     with pytest.raises(pkv.PagedKVError):  # fixed partitions are not served for grouped rows
         pkv.paged_attention_decode(q, c["kp"], c["vp"], tab, lens, 0.1, partition_size=64)
-    kn = normal_16bit((2, 2, D), "f16", DEV, 84)
-    with pytest.raises(pkv.PagedKVError):  # the fused append needs one row per KV head
-        pkv.paged_attention_decode_append(q, kn, kn, c["kp"], c["vp"], tab, lens, 0.1)
     q = normal_16bit((2, 2, 3, D), "f16", DEV, 85)
     with pytest.raises(pkv.PagedKVError):  # 3 query heads over 2 KV heads
         pkv.paged_attention_multi(q, c["kp"], c["vp"], tab, lens, 0.1)
