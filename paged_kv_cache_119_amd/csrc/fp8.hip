@@ -14,9 +14,11 @@
 //  * Decode (the attention equation of the same page, 背景): the balanced
 //    split and pipelined chunk stream of the 16-bit kernel, with 32-token
 //    chunks: 8 lanes hold a token row (16 codes each), a load instruction
-//    reads 8 whole rows (1 KiB), codes are widened with v_cvt_pk_f32_fp8 and
-//    multiplied in float32.  The K scale is folded into the score scale and
-//    the V scale applied to the weighted V sum.
+//    reads 8 whole rows (1 KiB).  Codes are widened in pairs by gfx950's
+//    packed conversions, exactly: K to the query's 16-bit type, so q.k runs
+//    on v_dot2c with exact products as in the 16-bit kernel; V to binary16,
+//    accumulated in float32 by mixed-precision FMAs.  The K scale is folded
+//    into the score scale and the V scale applied to the weighted V sum.
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -33,16 +35,17 @@ constexpr int FTPI = 64 / FLPT;       // token rows per load instruction
 constexpr int FNL = 4;                // loads per tensor per chunk
 constexpr int FTC = FNL * FTPI;       // tokens per chunk
 
-typedef float f2_t __attribute__((ext_vector_type(2)));
-
-// Four codes of a dword -> four floats.
-__device__ __forceinline__ void widen4(uint32_t w, float *f) {
-  const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  f[0] = lo[0];
-  f[1] = lo[1];
-  f[2] = hi[0];
-  f[3] = hi[1];
+// Two e4m3 codes (bytes 0, 1 or, hi, bytes 2, 3 of w) -> a packed pair of the
+// 16-bit type, exactly (gfx950's packed conversion at unit scale).
+template <int DT>
+__device__ __forceinline__ uint32_t pair16(uint32_t w, bool hi) {
+  if constexpr (DT == DT_F16) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  } else {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
 }
 
 // float -> e4m3 code: saturate to +-448 (NaN passes), round to nearest even.
@@ -150,7 +153,7 @@ struct Fp8Stream {
   int lane, lane_off, row, qoff;
   int64_t worker;
   ChunkCursor<FTC> cur;
-  float qf[16];
+  u32x4 qa, qb;  // this lane's 16 query elements as packed pairs
   float m, l, acc[16];
   bool bad;
 
@@ -218,12 +221,8 @@ struct Fp8Stream {
 
   __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
     if (d.c == d.cb) {
-      const uint32_t w[8] = {b.q0.x, b.q0.y, b.q0.z, b.q0.w, b.q1.x, b.q1.y, b.q1.z, b.q1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        qf[2 * j] = lo16<DT>(w[j]);
-        qf[2 * j + 1] = hi16<DT>(w[j]);
-      }
+      qa = b.q0;
+      qb = b.q1;
       m = kNegInf;
       l = 0.f;
 #pragma unroll
@@ -239,15 +238,13 @@ struct Fp8Stream {
       const int tok = d.c * FTC + i * FTPI + row;
       const bool valid = tok >= t_lo && tok < t_hi;
       const uint32_t w[4] = {b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w};
+      const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
       float dot = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float f[4];
-        widen4(w[j], f);
-        dot = fmaf(qf[4 * j], f[0], dot);
-        dot = fmaf(qf[4 * j + 1], f[1], dot);
-        dot = fmaf(qf[4 * j + 2], f[2], dot);
-        dot = fmaf(qf[4 * j + 3], f[3], dot);
+        // four codes -> two pairs of the query's type (exact), two dot2 steps
+        dot = dot2<DT>(qw[2 * j], pair16<DT>(w[j], false), dot);
+        dot = dot2<DT>(qw[2 * j + 1], pair16<DT>(w[j], true), dot);
       }
       const float dd = group_sum<FLPT>(dot) * scale_log2;
       z[i] = valid ? dd : kNegInf;
@@ -275,10 +272,12 @@ struct Fp8Stream {
       const uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float f[4];
-        widen4(w[j], f);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(pz[i], f[e], acc[4 * j + e]);
+        // four codes -> two binary16 pairs (exact), mixed-precision FMAs
+        const uint32_t h0 = pair16<DT_F16>(w[j], false), h1 = pair16<DT_F16>(w[j], true);
+        acc[4 * j] = fmaf(pz[i], lo16<DT_F16>(h0), acc[4 * j]);
+        acc[4 * j + 1] = fmaf(pz[i], hi16<DT_F16>(h0), acc[4 * j + 1]);
+        acc[4 * j + 2] = fmaf(pz[i], lo16<DT_F16>(h1), acc[4 * j + 2]);
+        acc[4 * j + 3] = fmaf(pz[i], hi16<DT_F16>(h1), acc[4 * j + 3]);
       }
     }
     m = mnew;
