@@ -111,6 +111,7 @@ struct Layout {
   bool group;  // several query rows per KV head (matrix-core kernel)
   int32_t P, MP;
   int64_t units;
+  int64_t workers;  // balanced split: most workers the batch can use (slices of >= kMinWorkerChunks)
   size_t off_m, off_l, off_o, off_cum, bytes;
 };
 
@@ -142,6 +143,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
     const int64_t workers = (most + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
     const int64_t units = (workers + (int64_t)num_seqs * p->num_kv_heads) * rows;
     lay->units = units;
+    lay->workers = workers;
     const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
     const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
     lay->off_cum = 0;
@@ -164,6 +166,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
     const int64_t workers = (most + pkv::kMinWorkerChunks - 1) / pkv::kMinWorkerChunks;
     const int64_t units = workers + (int64_t)num_seqs * num_heads;
     lay->units = units;
+    lay->workers = workers;
     const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
     const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
     lay->off_cum = 0;
@@ -237,6 +240,12 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   if (lay.balanced) {
     a->G = balanced_waves(p, num_seqs, lay.group, fp8);
     if (a->G == 0) return PKV_ERR_HIP;
+    // a small batch cannot use every resident wavefront: launch whole
+    // workgroups for the most workers it can use (the split and merge passes
+    // compute the same count from the same arguments)
+    const int nw = pkv::decode_waves();
+    const int64_t useful = (lay.workers + nw - 1) / nw * nw;
+    if (useful < a->G) a->G = (int32_t)useful;
   }
   a->nq = num_queries;
   a->group = lay.group ? 1 : 0;
