@@ -638,46 +638,6 @@ struct Stream {
       }
     }
   }
-
-  // The stream: stage 1 of chunk n + 2, stage 2 of chunk n + 1, stage 3 of
-  // chunk n.  The loop body handles two chunks (one per buffer) and has one
-  // back edge, so the wait before each consume leaves the younger chunk's
-  // loads in flight.  The priority falls from 3 to 0 as the wavefront passes
-  // quarters of its slice (th1..th3 chunks).
-  __device__ __forceinline__ void run(int th1, int th2, int th3) {
-    Chunk d0 = cur.produce();
-    if (!d0.valid) return;
-    int done = 0;
-    Buf ba, bb;
-    uint32_t ea = load_entries(d0);
-    Chunk d1 = cur.produce();
-    uint32_t eb = load_entries(d1);
-    load_kv(d0, ea, ba);
-    for (;;) {
-      const Chunk d2 = cur.produce();
-      ea = load_entries(d2);
-      load_kv(d1, eb, bb);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(d0, ba);
-      ++done;
-      if (done == th1) __builtin_amdgcn_s_setprio(2);
-      if (done == th2) __builtin_amdgcn_s_setprio(1);
-      if (done == th3) __builtin_amdgcn_s_setprio(0);
-      if (!d1.valid) break;
-      const Chunk d3 = cur.produce();
-      eb = load_entries(d3);
-      load_kv(d2, ea, ba);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(d1, bb);
-      ++done;
-      if (done == th1) __builtin_amdgcn_s_setprio(2);
-      if (done == th2) __builtin_amdgcn_s_setprio(1);
-      if (done == th3) __builtin_amdgcn_s_setprio(0);
-      if (!d2.valid) break;
-      d0 = d2;
-      d1 = d3;
-    }
-  }
 };
 
 template <int DT, int D, int B, int NW, bool APP, bool NT>
@@ -710,10 +670,8 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
   st.init(a, cum, lens, lane);
   st.worker = w;
   st.cur.enter(lo, hi);
-  const int n = (int)(hi - lo);
-  const int th1 = n / 4, th2 = n / 2, th3 = (3 * n) / 4;
   __builtin_amdgcn_s_setprio(3);
-  st.run(th1, th2, th3);
+  run_stream(st, (int)(hi - lo));
   __builtin_amdgcn_s_setprio(0);
 }
 

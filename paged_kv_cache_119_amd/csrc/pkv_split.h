@@ -180,4 +180,51 @@ struct ChunkCursor {
   }
 };
 
+// Runs a wavefront's stream of n chunks (n >= 1) through the three stages
+// of ST: load_entries (the chunk's table entries), load_kv (its K/V rows)
+// and consume (fold it into the running softmax).  Stage 1 of chunk i + 2,
+// stage 2 of chunk i + 1 and stage 3 of chunk i overlap.  The loop body
+// handles two chunks, one per buffer, runs a counted number of times and has
+// its only exit at the bottom; the prologue issues its loads in the loop's
+// order.  Every path into the loop top therefore carries the same
+// outstanding loads, so the compiler's wait before each consume leaves the
+// younger chunk's loads in flight.  An odd last chunk is consumed after the
+// loop; past the end of the slice the cursor repeats its last chunk, whose
+// loads stay in bounds and are never consumed.  The priority falls from 3 to
+// 0 as the wavefront passes quarters of its slice, so wavefronts that share
+// a SIMD progress together instead of in order of age.
+template <class ST>
+__device__ __forceinline__ void run_stream(ST &st, int n) {
+  const int th1 = n / 4, th2 = n / 2, th3 = (3 * n) / 4;
+  typename ST::Buf ba, bb;
+  Chunk d0 = st.cur.produce();
+  uint32_t ea = st.load_entries(d0);
+  Chunk d1 = st.cur.produce();
+  uint32_t eb = st.load_entries(d1);
+  __builtin_amdgcn_sched_barrier(0);
+  st.load_kv(d0, ea, ba);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int done = 0; done + 2 <= n; done += 2) {
+    const Chunk d2 = st.cur.produce();
+    ea = st.load_entries(d2);
+    st.load_kv(d1, eb, bb);
+    __builtin_amdgcn_sched_barrier(0);
+    st.consume(d0, ba);
+    if (done + 1 == th1) __builtin_amdgcn_s_setprio(2);
+    if (done + 1 == th2) __builtin_amdgcn_s_setprio(1);
+    if (done + 1 == th3) __builtin_amdgcn_s_setprio(0);
+    const Chunk d3 = st.cur.produce();
+    eb = st.load_entries(d3);
+    st.load_kv(d2, ea, ba);
+    __builtin_amdgcn_sched_barrier(0);
+    st.consume(d1, bb);
+    if (done + 2 == th1) __builtin_amdgcn_s_setprio(2);
+    if (done + 2 == th2) __builtin_amdgcn_s_setprio(1);
+    if (done + 2 == th3) __builtin_amdgcn_s_setprio(0);
+    d0 = d2;
+    d1 = d3;
+  }
+  if (n & 1) st.consume(d0, ba);
+}
+
 }  // namespace pkv
