@@ -16,8 +16,10 @@ finds the previous step's KV in the 256 MiB MALL or the L2s.
 
 Prints ONE JSON line.  `value` is algorithmic bytes per step / time per step
 (GB/s); `roofline` prices the partition kernel alone (algorithmic decode bytes
-per launch / its mean launch time, HIP events on its stream); `cpu_baseline`
-times the float64 CPU oracle on a bounded sample of the same batch.
+per launch / its mean launch time, from a pair of HIP events around each launch
+on its stream, created without the system-scope fence so that recording them
+adds no cache writeback between launches); `cpu_baseline` times the float64 CPU
+oracle on a bounded sample of the same batch.
 """
 
 from __future__ import annotations
@@ -174,7 +176,7 @@ def main(argv=None) -> int:
         step(i)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(KernelEvent(), KernelEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -277,18 +279,68 @@ def copy_calibration(torch, dev) -> None:
     del src, dst
 
 
+def probe_lib():
+    """The measurement helpers built beside the library (read probe, timing
+    events); built here if missing."""
+    global _PROBE
+    if _PROBE is None:
+        from paged_kv_cache_119_amd.build import PROBE_LIB, build_probe
+        if not os.path.exists(PROBE_LIB):
+            build_probe()
+        lib = ctypes.CDLL(PROBE_LIB)
+        vp = ctypes.c_void_p
+        lib.pkvprobe_stream_read.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int, vp]
+        lib.pkvprobe_event_create.argtypes = [ctypes.POINTER(vp)]
+        lib.pkvprobe_event_record.argtypes = [vp, vp]
+        lib.pkvprobe_event_elapsed.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.pkvprobe_event_destroy.argtypes = [vp]
+        _PROBE = lib
+    return _PROBE
+
+
+_PROBE = None
+
+
+class KernelEvent:
+    """A HIP timing event for per-launch durations, created with
+    hipEventDisableSystemFence: recording it adds no system-scope cache
+    writeback and invalidation between the launches it brackets.  Same
+    record / elapsed_time use as torch.cuda.Event; read after a device
+    synchronisation."""
+
+    def __init__(self):
+        self._lib = probe_lib()
+        self.h = ctypes.c_void_p()
+        st = self._lib.pkvprobe_event_create(ctypes.byref(self.h))
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: HIP error {st}")
+
+    def record(self, stream=None):
+        import torch
+        s = torch.cuda.current_stream() if stream is None else stream
+        st = self._lib.pkvprobe_event_record(self.h, ctypes.c_void_p(int(s.cuda_stream)))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord: HIP error {st}")
+
+    def elapsed_time(self, end) -> float:
+        ms = ctypes.c_float()
+        st = self._lib.pkvprobe_event_elapsed(ctypes.byref(ms), self.h, end.h)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime: HIP error {st}")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "h", None) and self._lib is not None:
+            self._lib.pkvprobe_event_destroy(self.h)
+
+
 def read_ceiling(torch, dev, nbytes: int) -> dict:
     """Context for the roofline: a plain streaming read of the same number of
     bytes from one contiguous buffer (the probe built beside the library),
     cached and non-temporal loads, 32,768 workgroups; the median of 20
     HIP-event-timed launches, the faster of the two load kinds."""
     import numpy as np
-    from paged_kv_cache_119_amd.build import PROBE_LIB, build_probe
-    if not os.path.exists(PROBE_LIB):
-        build_probe()
-    lib = ctypes.CDLL(PROBE_LIB)
-    lib.pkvprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                         ctypes.c_int, ctypes.c_void_p]
+    lib = probe_lib()
     n = max(16, nbytes // 16 * 16)
     bufs = [torch.zeros(n, dtype=torch.uint8, device=dev) for _ in range(2)]
     out = torch.zeros(1024, dtype=torch.int32, device=dev)
@@ -297,7 +349,7 @@ def read_ceiling(torch, dev, nbytes: int) -> dict:
     for nt in (0, 1):
         ts = []
         for i in range(23):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = KernelEvent(), KernelEvent()
             e0.record()
             st = lib.pkvprobe_stream_read(bufs[i % 2].data_ptr(), n, out.data_ptr(), 32768, nt, sp)
             e1.record()
@@ -390,7 +442,7 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(KernelEvent(), KernelEvent()) for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
@@ -505,7 +557,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(KernelEvent(), KernelEvent()) for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
@@ -630,7 +682,7 @@ def bench_copy_blocks(args, t, pkv, lib, dev) -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(KernelEvent(), KernelEvent()) for _ in range(args.steps)]
     for i in range(args.steps):
         evs[i][0].record(stream)
         step(args.warmup + i)

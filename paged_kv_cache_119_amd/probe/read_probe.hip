@@ -1,6 +1,6 @@
 // Measurement context for the roofline (not part of libpagedkv): a plain
 // streaming read of a contiguous buffer, the practical read ceiling the
-// decode kernels are compared with.  Grid-stride over 16-byte pieces, four
+// decode kernels are compared with, and timing events for the benchmark.  Grid-stride over 16-byte pieces, four
 // loads in flight per iteration; the XOR of what was read is written only if
 // it equals an arbitrary constant, so the loads cannot be removed.
 
@@ -45,4 +45,24 @@ extern "C" int pkvprobe_stream_read(const void *p, int64_t bytes, void *out, int
     hipLaunchKernelGGL((stream_read_kernel<false>), dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const u32x4 *>(p), bytes / 16, reinterpret_cast<uint32_t *>(out));
   return (int)hipGetLastError();
+}
+
+// Timing events for per-launch durations: created with
+// hipEventDisableSystemFence, so recording one does not add a system-scope
+// cache writeback and invalidation between the launches it brackets (HIP
+// documents the flag for events used only to measure time).  Elapsed times
+// are read after a device synchronisation.  Each returns the HIP error.
+extern "C" int pkvprobe_event_create(void **ev) {
+  if (!ev) return (int)hipErrorInvalidValue;
+  return (int)hipEventCreateWithFlags(reinterpret_cast<hipEvent_t *>(ev), hipEventDisableSystemFence);
+}
+extern "C" int pkvprobe_event_record(void *ev, void *stream) {
+  return (int)hipEventRecord(reinterpret_cast<hipEvent_t>(ev), reinterpret_cast<hipStream_t>(stream));
+}
+extern "C" int pkvprobe_event_elapsed(float *ms, void *start, void *stop) {
+  if (!ms) return (int)hipErrorInvalidValue;
+  return (int)hipEventElapsedTime(ms, reinterpret_cast<hipEvent_t>(start), reinterpret_cast<hipEvent_t>(stop));
+}
+extern "C" int pkvprobe_event_destroy(void *ev) {
+  return (int)hipEventDestroy(reinterpret_cast<hipEvent_t>(ev));
 }
