@@ -263,6 +263,7 @@ def main(argv=None) -> int:
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
+        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, P, 1, False, not args.separate_append),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -481,6 +482,7 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2)},
         "cpu_baseline": None,
         "read_ceiling": ceiling,
+        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, Q, args.kv == "fp8"),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -609,6 +611,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
+        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True),
     }
     print(json.dumps(line), flush=True)
     return 0

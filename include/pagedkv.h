@@ -209,6 +209,39 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
                                   const pkv_pool *p, int32_t partition_size);
 
 /*
+ * pkv_decode_launch_info -- what the split pass of a decode call with these
+ * arguments launches, read from the library's own code objects (no kernel
+ * runs, nothing is allocated).  num_queries, fp8 and append select the path
+ * as the corresponding entry points do: num_queries > 1 or grouped heads the
+ * matrix-core kernel, fp8 != 0 the e4m3 kernels, append != 0 the 16-bit
+ * balanced kernel with the fused append.  On the current device it fills:
+ *   workgroups, waves_per_workgroup  the split pass's grid;
+ *   waves_per_simd      wavefronts of that kernel that fit on a SIMD
+ *                       (hipOccupancyMaxActiveBlocksPerMultiprocessor); the
+ *                       balanced split sizes its grid for the smallest value
+ *                       among the kernels a call may use (with or without
+ *                       the fused append, streamed or cached loads), so the
+ *                       grid can hold fewer;
+ *   compute_units       of the device;
+ *   registers           per lane (hipFuncGetAttributes numRegs);
+ *   lds_static_bytes, lds_dynamic_bytes  per workgroup;
+ *   scratch_bytes       per lane (register spills; 0 for every kernel here);
+ *   balanced, partition_size  the split the call uses.
+ * Returns PKV_ERR_NULL for a NULL info, the argument errors of the decode
+ * calls, PKV_ERR_HIP if the device cannot be queried.  Used for the
+ * occupancy and resource figures of the benchmark.
+ */
+typedef struct {
+  int32_t workgroups, waves_per_workgroup, waves_per_simd, compute_units;
+  int32_t registers, lds_static_bytes, lds_dynamic_bytes, scratch_bytes;
+  int32_t balanced, partition_size;
+} pkv_launch_info;
+
+pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                  const pkv_pool *p, int32_t partition_size, int32_t num_queries,
+                                  int32_t fp8, int32_t append, pkv_launch_info *info);
+
+/*
  * pkv_paged_attention_decode -- one query token per sequence over paged K/V.
  *
  * For every sequence s and head h, with L = context_lens[s]:

@@ -29,6 +29,7 @@ EXPORTS = (
     "pkv_copy_blocks",
     "pkv_decode_partition_size",
     "pkv_decode_workspace_bytes",
+    "pkv_decode_launch_info",
     "pkv_paged_attention_decode",
     "pkv_paged_attention_decode_append",
     "pkv_decode_partitions_append",
@@ -60,6 +61,13 @@ class PoolDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
+class LaunchInfo(ctypes.Structure):
+    """pkv_launch_info: the split pass's grid, occupancy and resources."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "workgroups", "waves_per_workgroup", "waves_per_simd", "compute_units", "registers",
+        "lds_static_bytes", "lds_dynamic_bytes", "scratch_bytes", "balanced", "partition_size")]
+
+
 POOL_REUSE = 1  # pkv_pool.flags: blocks read by several sequences in one call
 
 
@@ -88,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_reshape_and_cache": (ctypes.c_int, [vp, vp, vp, vp, i64, i64, vp, i32, pool, vp]),
         "pkv_copy_blocks": (ctypes.c_int, [vp, vp, vp, i32, pool, vp]),
         "pkv_decode_partition_size": (i32, [i32, i32, i32, pool, i32]),
+        "pkv_decode_launch_info": (ctypes.c_int, [i32, i32, i32, pool, i32, i32, i32, i32, P(LaunchInfo)]),
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, pool, i32]),
         "pkv_paged_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
                                                       i32, pool, i32, vp, sz, vp]),
@@ -279,6 +288,20 @@ def decode_partition_size(num_seqs, num_heads, max_blocks_per_seq, k_pool, parti
     desc = pool_desc_of(k_pool)
     return int(load_library().pkv_decode_partition_size(int(num_seqs), int(num_heads), int(max_blocks_per_seq),
                                                         ctypes.byref(desc), int(partition_size)))
+
+
+def decode_launch_info(num_seqs, num_heads, max_blocks_per_seq, desc, partition_size=0, num_queries=1,
+                       fp8=False, append=False) -> dict:
+    """The split pass a decode call with these arguments launches on the
+    current device: grid, resident waves per SIMD, registers, LDS and scratch
+    from the library's own code objects (pkv_decode_launch_info).  `desc` is
+    the pool's PoolDesc (make_pool_desc / pool_desc_of)."""
+    info = LaunchInfo()
+    st = load_library().pkv_decode_launch_info(int(num_seqs), int(num_heads), int(max_blocks_per_seq),
+                                               ctypes.byref(desc), int(partition_size), int(num_queries),
+                                               1 if fp8 else 0, 1 if append else 0, ctypes.byref(info))
+    _check(st, "pkv_decode_launch_info")
+    return {name: int(getattr(info, name)) for name, _ in LaunchInfo._fields_}
 
 
 def decode_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, partition_size=0) -> int:

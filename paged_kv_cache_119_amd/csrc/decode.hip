@@ -780,8 +780,7 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
 template <int DT, int D, int B>
 struct PartitionsF {
   static hipError_t call(const DecodeParams &a, hipStream_t st) {
-    const int group = 8 * kXcdGroup;
-    const int grid = ((a.items + group - 1) / group) * group;
+    const int grid = (int)partition_grid(a.items);
     if (a.stream_kv)
       hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves, true>), dim3(grid),
                          dim3(kNumWaves * 64), 0, st, a);
@@ -789,6 +788,14 @@ struct PartitionsF {
       hipLaunchKernelGGL((decode_partition_kernel<DT, D, B, kNumWaves, false>), dim3(grid),
                          dim3(kNumWaves * 64), 0, st, a);
     return hipGetLastError();
+  }
+};
+
+template <int DT, int D, int B>
+struct PartitionsPtrF {
+  static const void *call(int nt) {
+    return nt ? reinterpret_cast<const void *>(&decode_partition_kernel<DT, D, B, kNumWaves, true>)
+              : reinterpret_cast<const void *>(&decode_partition_kernel<DT, D, B, kNumWaves, false>);
   }
 };
 
@@ -854,6 +861,15 @@ int decode_chunk_tokens(int head_dim) {
 
 size_t balanced_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
+}
+
+const void *partition_kernel(int dtype, int head_dim, int block_size, int nt) {
+  return dispatch<PartitionsPtrF, const void *>(dtype, head_dim, block_size, nullptr, nt);
+}
+
+int64_t partition_grid(int64_t items) {
+  const int64_t group = 8 * kXcdGroup;
+  return (items + group - 1) / group * group;
 }
 
 const void *balanced_kernel(int dtype, int head_dim, int block_size, int append, int nt) {

@@ -195,6 +195,19 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   return PKV_OK;
 }
 
+// Workers (wavefronts) the balanced split launches for these arguments, 0 if
+// the device cannot be queried.  A small batch cannot use every resident
+// wavefront: whole workgroups for the most workers it can use (the split and
+// merge passes compute the same count from the same arguments).
+int32_t balanced_workers(const pkv_pool *p, int32_t num_seqs, const Layout &lay, bool fp8) {
+  int32_t G = balanced_waves(p, num_seqs, lay.group, fp8);
+  if (G == 0) return 0;
+  const int nw = pkv::decode_waves();
+  const int64_t useful = (lay.workers + nw - 1) / nw * nw;
+  if (useful < G) G = (int32_t)useful;
+  return G;
+}
+
 pkv_status fill_params(void *out, const void *q, const void *k_pool, const void *v_pool,
                        const int32_t *block_tables, const int32_t *context_lens, float scale,
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
@@ -238,14 +251,8 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
     a->ws_cum = lay.balanced ? (int64_t *)(ws + lay.off_cum) : nullptr;
   }
   if (lay.balanced) {
-    a->G = balanced_waves(p, num_seqs, lay.group, fp8);
+    a->G = balanced_workers(p, num_seqs, lay, fp8);
     if (a->G == 0) return PKV_ERR_HIP;
-    // a small batch cannot use every resident wavefront: launch whole
-    // workgroups for the most workers it can use (the split and merge passes
-    // compute the same count from the same arguments)
-    const int nw = pkv::decode_waves();
-    const int64_t useful = (lay.workers + nw - 1) / nw * nw;
-    if (useful < a->G) a->G = (int32_t)useful;
   }
   a->nq = num_queries;
   a->group = lay.group ? 1 : 0;
@@ -422,6 +429,61 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
   if (decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, 1, &lay) != PKV_OK)
     return 0;
   return lay.bytes;
+}
+
+pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                  const pkv_pool *p, int32_t partition_size, int32_t num_queries, int32_t fp8,
+                                  int32_t append, pkv_launch_info *info) {
+  if (!info) return PKV_ERR_NULL;
+  *info = pkv_launch_info{};
+  if (num_seqs < 1) return PKV_ERR_SHAPE;
+  Layout lay;
+  const pkv_status st =
+      decode_layout(num_seqs, num_heads, max_blocks_per_seq, p, partition_size, num_queries, &lay, fp8 != 0);
+  if (st != PKV_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  const int cus = device_cus(dev);
+  if (cus <= 0) return PKV_ERR_HIP;
+  const int nw = pkv::decode_waves();
+  const int nt = (p->flags & PKV_POOL_REUSE) ? 0 : 1;
+  const void *k = nullptr;
+  size_t lds = 0;
+  int64_t wgs = 0;
+  if (lay.balanced) {
+    if (lay.group) {
+      k = pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0);
+      lds = pkv::group_lds_bytes(num_seqs);
+    } else if (fp8) {
+      k = pkv::fp8_kernel(p->dtype, p->block_size, nt);
+      lds = pkv::fp8_lds_bytes(num_seqs);
+    } else {
+      k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, append ? 1 : 0, nt);
+      lds = pkv::balanced_lds_bytes(num_seqs);
+    }
+    const int32_t G = balanced_workers(p, num_seqs, lay, fp8 != 0);
+    if (G == 0) return PKV_ERR_HIP;
+    wgs = G / nw;
+  } else {
+    k = pkv::partition_kernel(p->dtype, p->head_dim, p->block_size, nt);
+    wgs = pkv::partition_grid(lay.units);
+  }
+  if (!k) return PKV_ERR_UNSUPPORTED;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, k) != hipSuccess) return PKV_ERR_HIP;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, nw * 64, lds) != hipSuccess) return PKV_ERR_HIP;
+  info->workgroups = wgs > INT32_MAX ? INT32_MAX : (int32_t)wgs;
+  info->waves_per_workgroup = nw;
+  info->waves_per_simd = blocks * nw / 4;  // four SIMDs per compute unit
+  info->compute_units = cus;
+  info->registers = attr.numRegs;
+  info->lds_static_bytes = (int32_t)attr.sharedSizeBytes;
+  info->lds_dynamic_bytes = (int32_t)lds;
+  info->scratch_bytes = (int32_t)attr.localSizeBytes;
+  info->balanced = lay.balanced ? 1 : 0;
+  info->partition_size = lay.balanced ? 0 : lay.P;
+  return PKV_OK;
 }
 
 pkv_status pkv_decode_partitions(void *out, const void *q, const void *k_pool, const void *v_pool,

@@ -77,6 +77,10 @@ size_t balanced_lds_bytes(int num_seqs);
 // The balanced kernel instance for (dtype, D, B, append, non-temporal K/V
 // loads), for occupancy queries.
 const void *balanced_kernel(int dtype, int head_dim, int block_size, int append, int nt);
+// The fixed-partition kernel instance and the number of workgroups it is
+// launched with for `items` (sequence, head, partition) items.
+const void *partition_kernel(int dtype, int head_dim, int block_size, int nt);
+int64_t partition_grid(int64_t items);
 
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
 // Several query rows per KV head (grouped-query heads, multi-token queries).

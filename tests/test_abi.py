@@ -210,3 +210,15 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert not re.search(r"(import\s+oracle|from\s+oracle|oracle\.)", text), fn
                 assert "paged_oracle" not in text, fn
+
+def test_launch_info_validation(lib):
+    """pkv_decode_launch_info rejects a NULL result and bad shapes before it
+    touches the device."""
+    d = _desc(D=128)
+    info = bd.LaunchInfo()
+    f = lib.pkv_decode_launch_info
+    assert f(8, 4, 16, ctypes.byref(d), 0, 1, 0, 0, None) == 1                   # PKV_ERR_NULL
+    assert f(0, 4, 16, ctypes.byref(d), 0, 1, 0, 0, ctypes.byref(info)) == 2     # no sequences
+    assert f(8, 4, 16, None, 0, 1, 0, 0, ctypes.byref(info)) == 1                # no pool
+    assert f(8, 4, 16, ctypes.byref(_desc(D=96)), 0, 1, 0, 0, ctypes.byref(info)) == 3
+    assert f(8, 4, 16, ctypes.byref(d), 0, 17 * 4, 0, 0, ctypes.byref(info)) == 3  # > 16 rows per KV head
