@@ -611,7 +611,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
-        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True),
+        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True, not args.separate_append),
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -213,8 +213,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t m
  * arguments launches, read from the library's own code objects (no kernel
  * runs, nothing is allocated).  num_queries, fp8 and append select the path
  * as the corresponding entry points do: num_queries > 1 or grouped heads the
- * matrix-core kernel, fp8 != 0 the e4m3 kernels, append != 0 the 16-bit
- * balanced kernel with the fused append.  On the current device it fills:
+ * matrix-core kernel, fp8 != 0 the e4m3 kernels, append != 0 the kernels
+ * of the decode step with the fused append (16-bit, and e4m3 with one row
+ * per KV head).  On the current device it fills:
  *   workgroups, waves_per_workgroup  the split pass's grid;
  *   waves_per_simd      wavefronts of that kernel that fit on a SIMD
  *                       (hipOccupancyMaxActiveBlocksPerMultiprocessor); the
@@ -455,13 +456,18 @@ pkv_status pkv_paged_attention_decode_fp8(void *out, const void *q, const void *
  * (0 < L <= max_blocks_per_seq * B), row s of k_new / v_new ([S][Hkv][D],
  * 16-bit, token stride new_token_stride elements, 0 = Hkv * D, a multiple of
  * 8; 16-byte aligned) is quantised exactly as pkv_reshape_and_cache_fp8 does
- * and written to the slot of token L - 1; then the attention of
- * pkv_paged_attention_decode_fp8 runs, reading that token from the pool like
- * the others (append first, then attend: "PagedAttention 完全拆解",
- * 原理详解（一）, Figure 6 walk-through).  A needed table entry outside the
- * pool writes nothing and gives a NaN row.  Same restrictions, scales and
- * workspace as pkv_paged_attention_decode_fp8.  Three launches: the append
- * (slots from the table, no slot list), the split pass and the merge pass.
+ * and written to the slot of token L - 1; the attention of
+ * pkv_paged_attention_decode_fp8 runs over the context with that token's
+ * codes (append first, then attend: "PagedAttention 完全拆解", 原理详解（一）,
+ * Figure 6 walk-through).  A needed table entry outside the pool writes
+ * nothing and gives a NaN row.  Same restrictions, scales and workspace as
+ * pkv_paged_attention_decode_fp8.  One row per KV head: two launches, the
+ * split pass (which quantises each new token itself and uses those codes in
+ * place of the pool's) and the merge pass (which also writes the codes to
+ * the pool).  Grouped heads: three, a separate append (slots from the table,
+ * no slot list) before the two passes.  The output and the pool bytes are
+ * the same either way, and bit for bit those of pkv_reshape_and_cache_fp8
+ * followed by pkv_paged_attention_decode_fp8.
  */
 pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const void *k_new, const void *v_new,
                                                  int64_t new_token_stride, void *k_pool, void *v_pool,

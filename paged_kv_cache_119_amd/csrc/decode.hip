@@ -690,6 +690,25 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   const int s = (int)(g / a.H);
   const int h = (int)(g - (int64_t)s * a.H);
   const int L = a.lens[s];
+  if constexpr (D == 128 && TC == 32) {
+    // FP8 decode step with the append: the split pass attended over token
+    // L - 1's codes quantised from k_new / v_new; write them to its pool
+    // slot now (8 lanes x 16 codes per row; nothing for an invalid context or
+    // an entry outside the pool)
+    if (a.fp8 && a.append && L >= 1 && L <= a.maxb * a.B && lane < 8) {
+      const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
+      if (blk >= 0 && (int64_t)blk < a.num_blocks) {
+        const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * D + lane * 16;
+        const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * D + lane * 16;
+        const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + dst) =
+            quant16<DT>(ks[0], ks[1], a.k_inv);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + dst) =
+            quant16<DT>(vs[0], vs[1], a.v_inv);
+      }
+    }
+  }
   const uint64_t cum_s = (uint64_t)a.ws_cum[s];
   const uint64_t total = (uint64_t)a.ws_cum[a.S];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;

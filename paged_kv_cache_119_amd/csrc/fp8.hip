@@ -6,11 +6,14 @@
 //    1, with a quantising store): code = e4m3(x * (1 / scale)), the product
 //    rounded in float32, saturated to +-448, then rounded to the nearest e4m3
 //    value, ties to even (v_cvt_pk_fp8_f32); NaN stays NaN.
-//  * Append of each sequence's new token: the same quantising write, with
-//    the slot of token L - 1 taken from the block table (the decode step's
-//    append, one launch, no slot list).  Kept out of the decode kernel:
-//    stores into the pool from inside the long stream kernel measured far
-//    slower than this separate launch on large pools.
+//  * Append of each sequence's new token (the decode step): the same
+//    quantisation, the slot of token L - 1 taken from the block table.  With
+//    one row per KV head the split pass quantises the new token itself and
+//    uses those codes in place of the pool's, and the merge launch writes
+//    them to the pool afterwards: no launch of its own, and no stores from
+//    inside the long stream kernel (they measured far slower than a separate
+//    launch on large pools).  Grouped rows use a separate launch with no slot
+//    list before the split pass.
 //  * Decode (the attention equation of the same page, 背景): the balanced
 //    split and pipelined chunk stream of the 16-bit kernel, with 32-token
 //    chunks: 8 lanes hold a token row (16 codes each), a load instruction
@@ -19,6 +22,8 @@
 //    on v_dot2c with exact products as in the 16-bit kernel; V to binary16,
 //    accumulated in float32 by mixed-precision FMAs.  The K scale is folded
 //    into the score scale and the V scale applied to the weighted V sum.
+
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -48,35 +53,15 @@ __device__ __forceinline__ uint32_t pair16(uint32_t w, bool hi) {
   }
 }
 
-// float -> e4m3 code: saturate to +-448 (NaN passes), round to nearest even.
-__device__ __forceinline__ float sat448(float y) { return (y != y) ? y : fminf(fmaxf(y, -448.f), 448.f); }
-
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
-  return (uint32_t)w;
-}
-
 // 16 elements of a K row and of a V row (16-bit, 32 bytes each) -> 16 codes
 // each, written at element offset dst of the pools.
 template <int DT>
 __device__ __forceinline__ void quantise_piece(uint8_t *kp, uint8_t *vp, const uint16_t *ksrc, const uint16_t *vsrc,
                                                int64_t dst, float k_inv, float v_inv) {
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const uint16_t *src = which == 0 ? ksrc : vsrc;
-    const float inv = which == 0 ? k_inv : v_inv;
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(src);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(src + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = quant4(lo16<DT>(w[2 * j]) * inv, hi16<DT>(w[2 * j]) * inv, lo16<DT>(w[2 * j + 1]) * inv,
-                    hi16<DT>(w[2 * j + 1]) * inv);
-    const u32x4 ov = {o[0], o[1], o[2], o[3]};
-    *reinterpret_cast<u32x4 *>((which == 0 ? kp : vp) + dst) = ov;
-  }
+  const u32x4 *ks = reinterpret_cast<const u32x4 *>(ksrc);
+  const u32x4 *vs = reinterpret_cast<const u32x4 *>(vsrc);
+  *reinterpret_cast<u32x4 *>(kp + dst) = quant16<DT>(ks[0], ks[1], k_inv);
+  *reinterpret_cast<u32x4 *>(vp + dst) = quant16<DT>(vs[0], vs[1], v_inv);
 }
 
 // One thread per 16 elements of a (token, head) row, slots from a list.
@@ -128,16 +113,30 @@ __global__ __launch_bounds__(256) void append_last_fp8_kernel(DecodeParams a, fl
                      reinterpret_cast<const uint16_t *>(a.v_new) + src, dst, k_inv, v_inv);
 }
 
-template <int DT, int B, bool NT>
+// APP: the decode step's append -- token L - 1 of every row is taken from
+// k_new / v_new, quantised here exactly as the append quantises it, in place
+// of the pool's codes (the merge launch writes the codes to the pool after
+// this pass has run).
+template <int DT, int B, bool NT, bool APP>
 struct Fp8Stream {
   static constexpr int NE = FTC >= B ? FTC / B : 1;  // table entries per chunk
   static_assert(B % FTPI == 0, "a load must not straddle two blocks");
 
-  struct Buf {
+  struct BufP {
     u32x4 k[FNL], v[FNL];
     u32x4 q0, q1;
     bool bad;
   };
+  struct BufA {
+    u32x4 k[FNL], v[FNL];
+    u32x4 q0, q1;
+    // chunk of token L - 1 only: the new-token rows spread over the wave,
+    // lane l < 32 holding K elements 4l .. 4l+3, lane 32 + l V elements
+    // 4l .. 4l+3 (8 bytes a lane)
+    uint32_t nw0, nw1;
+    bool bad;
+  };
+  using Buf = typename std::conditional<APP, BufA, BufP>::type;
 
   const uint8_t *kp;
   const uint8_t *vp;
@@ -150,6 +149,10 @@ struct Fp8Stream {
   int64_t blk_stride, num_blocks;
   int H, maxb;
   float scale_log2, v_scale;
+  const uint16_t *knp;  // APP: new-token rows and quantisation factors
+  const uint16_t *vnp;
+  int64_t new_stride;
+  float k_inv, v_inv;
   int lane, lane_off, row, qoff;
   int64_t worker;
   ChunkCursor<FTC> cur;
@@ -172,6 +175,11 @@ struct Fp8Stream {
     maxb = a.maxb;
     scale_log2 = a.scale_log2;
     v_scale = a.v_scale;
+    knp = reinterpret_cast<const uint16_t *>(a.k_new);
+    vnp = reinterpret_cast<const uint16_t *>(a.v_new);
+    new_stride = a.new_stride;
+    k_inv = a.k_inv;
+    v_inv = a.v_inv;
     lane = lane_;
     lane_off = lane * 16;
     row = lane / FLPT;
@@ -181,6 +189,9 @@ struct Fp8Stream {
 
   __device__ __forceinline__ static int first_block(int c) { return FTC >= B ? c * (FTC / B) : c / (B / FTC); }
   __device__ __forceinline__ static int last_block(const Chunk &d) { return (min(d.L, d.ce * FTC) - 1) / B; }
+  __device__ __forceinline__ static bool is_app_chunk(const Chunk &d) {
+    return d.c == d.ce - 1 && d.ce * FTC >= d.L;  // the chunk of token L - 1
+  }
 
   __device__ __forceinline__ uint32_t load_entries(const Chunk &d) const {
     const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
@@ -217,6 +228,15 @@ struct Fp8Stream {
     const uint16_t *q = qp + ((int64_t)d.s * H + d.h) * FD + qoff;
     b.q0 = *reinterpret_cast<const u32x4 *>(q);
     b.q1 = *reinterpret_cast<const u32x4 *>(q + 8);
+    if constexpr (APP) {
+      // only the chunk of token L - 1 (once per row) loads the new rows
+      if (is_app_chunk(d)) {
+        const int64_t src = (int64_t)d.s * new_stride + (int64_t)d.h * FD + 4 * (lane & 31);
+        const uint64_t w = *reinterpret_cast<const uint64_t *>((lane < 32 ? knp : vnp) + src);
+        b.nw0 = (uint32_t)w;
+        b.nw1 = (uint32_t)(w >> 32);
+      }
+    }
   }
 
   __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
@@ -230,6 +250,32 @@ struct Fp8Stream {
       bad = false;
     }
     bad = bad || b.bad;
+    if constexpr (APP) {
+      if (is_app_chunk(d)) {
+        // each lane quantises its 4 elements (the same quant4 steps as the
+        // append's); the lanes of token L - 1's row gather their 16 codes
+        // of K (from lanes 4(l%8) .. +3) and of V (32 + the same)
+        const float inv = lane < 32 ? k_inv : v_inv;
+        const int qd = (int)quant4(lo16<DT>(b.nw0) * inv, hi16<DT>(b.nw0) * inv, lo16<DT>(b.nw1) * inv,
+                                   hi16<DT>(b.nw1) * inv);
+        const int sl = (lane & 7) * 4;
+        u32x4 kc, vc;
+        kc.x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * sl, qd);
+        kc.y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 1), qd);
+        kc.z = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 2), qd);
+        kc.w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 3), qd);
+        vc.x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (32 + sl), qd);
+        vc.y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (33 + sl), qd);
+        vc.z = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (34 + sl), qd);
+        vc.w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (35 + sl), qd);
+#pragma unroll
+        for (int i = 0; i < FNL; ++i) {
+          const bool sub = (d.c * FTC + i * FTPI + row) == d.L - 1;
+          b.k[i] = sub ? kc : b.k[i];
+          b.v[i] = sub ? vc : b.v[i];
+        }
+      }
+    }
     const int t_lo = d.cb * FTC;
     const int t_hi = min(d.L, d.ce * FTC);
     float z[FNL];
@@ -326,9 +372,9 @@ struct Fp8Stream {
   }
 };
 
-template <int DT, int B, int NW, bool NT>
+template <int DT, int B, int NW, bool NT, bool APP>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
-  using ST = Fp8Stream<DT, B, NT>;
+  using ST = Fp8Stream<DT, B, NT, APP>;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -356,25 +402,31 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int DT, bool NT>
+template <int DT, bool NT, bool APP>
 const void *fp8_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT>);
-    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT>);
-    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT>);
-    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT>);
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT, APP>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT, APP>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT, APP>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT, APP>);
     default: return nullptr;
   }
 }
 
+template <int DT, int B, bool APP>
+void launch_fp8_app(const DecodeParams &a, hipStream_t st) {
+  if (a.stream_kv)
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true, APP>), dim3(a.G / kFp8Waves),
+                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
+  else
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false, APP>), dim3(a.G / kFp8Waves),
+                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
+}
+
 template <int DT, int B>
 hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
-  if (a.stream_kv)
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true>), dim3(a.G / kFp8Waves), dim3(kFp8Waves * 64),
-                       fp8_lds_bytes(a.S), st, a);
-  else
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false>), dim3(a.G / kFp8Waves),
-                       dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
+  if (a.append) launch_fp8_app<DT, B, true>(a, st);
+  else launch_fp8_app<DT, B, false>(a, st);
   return hipGetLastError();
 }
 
@@ -386,9 +438,13 @@ size_t fp8_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *fp8_kernel(int dtype, int block_size, int nt) {
-  if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true>(block_size) : fp8_ptr<DT_BF16, true>(block_size);
-  return dtype == DT_F16 ? fp8_ptr<DT_F16, false>(block_size) : fp8_ptr<DT_BF16, false>(block_size);
+const void *fp8_kernel(int dtype, int block_size, int nt, int append) {
+  if (append) {
+    if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true, true>(block_size) : fp8_ptr<DT_BF16, true, true>(block_size);
+    return dtype == DT_F16 ? fp8_ptr<DT_F16, false, true>(block_size) : fp8_ptr<DT_BF16, false, true>(block_size);
+  }
+  if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true, false>(block_size) : fp8_ptr<DT_BF16, true, false>(block_size);
+  return dtype == DT_F16 ? fp8_ptr<DT_F16, false, false>(block_size) : fp8_ptr<DT_BF16, false, false>(block_size);
 }
 
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {

@@ -93,13 +93,15 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
   // agree on the worker count whatever the entry point and pool flags
   int nb = 1 << 30;
   for (int nt = 0; nt < 2; ++nt) {
-    const void *k = group ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
-                    : fp8 ? pkv::fp8_kernel(p->dtype, p->block_size, nt)
-                          : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, 1, nt);
-    if (!k) return 0;
-    const int b = kernel_blocks_per_cu(dev, k, lds);
-    if (b <= 0) return 0;
-    nb = b < nb ? b : nb;
+    for (int app = 0; app < 2; ++app) {
+      const void *k = group ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
+                      : fp8 ? pkv::fp8_kernel(p->dtype, p->block_size, nt, app)
+                            : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
+      if (!k) return 0;
+      const int b = kernel_blocks_per_cu(dev, k, lds);
+      if (b <= 0) return 0;
+      nb = b < nb ? b : nb;
+    }
   }
   long long g = (long long)cus * nb * pkv::decode_waves();
   if (g > pkv::kMaxWorkers) g = pkv::kMaxWorkers / pkv::decode_waves() * pkv::decode_waves();
@@ -455,7 +457,7 @@ pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t m
       k = pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0);
       lds = pkv::group_lds_bytes(num_seqs);
     } else if (fp8) {
-      k = pkv::fp8_kernel(p->dtype, p->block_size, nt);
+      k = pkv::fp8_kernel(p->dtype, p->block_size, nt, append ? 1 : 0);
       lds = pkv::fp8_lds_bytes(num_seqs);
     } else {
       k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, append ? 1 : 0, nt);
@@ -654,10 +656,16 @@ pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const
   if (st != PKV_OK || num_seqs == 0) return st;
   a.scale_log2 = scale * k_scale * 1.4426950408889634f;
   a.v_scale = v_scale;
-  // the append as its own launch (slots from the table), then the decode passes
-  const pkv_status s0 = hip_status(pkv::launch_append_last_fp8(a, 1.0f / k_scale, 1.0f / v_scale, (hipStream_t)stream));
-  if (s0 != PKV_OK) return s0;
-  a.append = 0;
+  a.k_inv = 1.0f / k_scale;
+  a.v_inv = 1.0f / v_scale;
+  if (a.group) {
+    // grouped rows: the append as its own launch (slots from the table)
+    const pkv_status s0 = hip_status(pkv::launch_append_last_fp8(a, a.k_inv, a.v_inv, (hipStream_t)stream));
+    if (s0 != PKV_OK) return s0;
+    a.append = 0;
+  }
+  // one row per KV head: the split pass quantises each row's new token in
+  // place of its pool slot, and the merge launch writes the codes to the pool
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

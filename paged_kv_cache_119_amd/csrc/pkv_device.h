@@ -137,4 +137,28 @@ __device__ __forceinline__ int xcd_remap(int i) {
   return (j / G) * (8 * G) + x * G + (j % G);
 }
 
+// FP8 (OCP e4m3) quantisation, shared by the append and the decode step:
+// code = the e4m3 value nearest to float32(x * inv), ties to even, with the
+// product saturated to +-448 first (the conversion itself does not
+// saturate); NaN stays NaN.
+__device__ __forceinline__ float sat448(float y) { return (y != y) ? y : fminf(fmaxf(y, -448.f), 448.f); }
+
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+// 16 consecutive 16-bit elements (two 16-byte pieces) -> their 16 codes.
+template <int DT>
+__device__ __forceinline__ u32x4 quant16(const u32x4 &a, const u32x4 &b, float inv) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = quant4(lo16<DT>(w[2 * j]) * inv, hi16<DT>(w[2 * j]) * inv, lo16<DT>(w[2 * j + 1]) * inv,
+                  hi16<DT>(w[2 * j + 1]) * inv);
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 }  // namespace pkv

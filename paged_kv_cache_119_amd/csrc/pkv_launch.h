@@ -64,6 +64,9 @@ struct DecodeParams {
   // multiplied by v_scale.
   int32_t fp8;
   float v_scale;
+  // FP8 decode step with the append (fp8 and append != 0): 1 / k_scale and
+  // 1 / v_scale, the factors the new rows are quantised with
+  float k_inv, v_inv;
   // 1: K/V loads of the stream kernels are non-temporal (blocks read once
   // per call); 0: ordinary cached loads (blocks shared between sequences).
   int32_t stream_kv;
@@ -92,7 +95,7 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
 // FP8 (e4m3) pools, head_dim 128, one query row per KV head.
 int fp8_chunk_tokens();
 size_t fp8_lds_bytes(int num_seqs);
-const void *fp8_kernel(int dtype, int block_size, int nt);
+const void *fp8_kernel(int dtype, int block_size, int nt, int append);
 // The decode step's append into e4m3 pools: token L - 1 of every sequence
 // from k_new / v_new (a.append fields), slots from the block table.
 hipError_t launch_append_last_fp8(const DecodeParams &a, float k_inv, float v_inv, hipStream_t stream);
