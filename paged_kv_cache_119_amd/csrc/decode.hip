@@ -403,7 +403,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // table entries of chunk n + 2, K/V rows of chunk n + 1, arithmetic on chunk
 // n -- so piece and row boundaries cost no exposed memory latency.  Every
 // step issues the same loads (after the last chunk they repeat it and hit
-// the cache), so the compiler's waits stay exact.  A wavefront lowers its
+// the cache), so the compiler's waits stay exact; the one exception, the new
+// rows of the fused append, are loaded only with the chunk of token L - 1 and
+// at worst make the wait before the next consume a little stricter.  A
+// wavefront lowers its
 // priority as it progresses through its slice, so wavefronts that share a
 // SIMD finish together instead of in order of age.
 
@@ -515,11 +518,14 @@ struct Stream {
     // issues the same loads.
     b.q = *reinterpret_cast<const u32x4 *>(qp + ((int64_t)d.s * H + d.h) * D + qoff);
     if constexpr (APP) {
-      const int64_t ne = (int64_t)d.s * new_stride + (int64_t)d.h * D + qoff;
-      b.kn = *reinterpret_cast<const u32x4 *>(knp + ne);
-      b.vn = *reinterpret_cast<const u32x4 *>(vnp + ne);
-      const int ei = TC >= B ? min(NE - 1, max(0, (d.L - 1) / B - first_block(d.c))) : 0;
-      b.app_blk = __builtin_amdgcn_readlane((int)e, ei);
+      // only the chunk of token L - 1 (once per row) loads the new rows
+      if (is_app_chunk(d)) {
+        const int64_t ne = (int64_t)d.s * new_stride + (int64_t)d.h * D + qoff;
+        b.kn = *reinterpret_cast<const u32x4 *>(knp + ne);
+        b.vn = *reinterpret_cast<const u32x4 *>(vnp + ne);
+        const int ei = TC >= B ? min(NE - 1, max(0, (d.L - 1) / B - first_block(d.c))) : 0;
+        b.app_blk = __builtin_amdgcn_readlane((int)e, ei);
+      }
     }
   }
 
