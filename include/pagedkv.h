@@ -161,7 +161,9 @@ pkv_status pkv_reshape_and_cache(void *k_pool, void *v_pool, const void *k, cons
  *   block_pairs  int64 [num_pairs][2] (src, dst), device memory, 8-byte aligned
  * Pairs with src or dst outside [0, N) are skipped.  The copies run
  * concurrently: a dst must appear once, and no dst may be the src of another
- * pair in the same call.  num_pairs == 0 is a no-op.
+ * pair in the same call.  num_pairs == 0 is a no-op.  PKV_ERR_SHAPE when
+ * num_pairs * ceil(Hkv * B * D / 8192) exceeds 2^31 - 1 (the launch's
+ * workgroups: 16 KiB of each pool per workgroup).
  */
 pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pairs, int32_t num_pairs,
                            const pkv_pool *p, void *stream);

@@ -17,8 +17,8 @@
 // Block copy ("PagedAttention 完全拆解", 内存共享 and Figure 8: a sequence about
 // to write into a block it shares first gets a private copy of it): a batch
 // of (src, dst) pairs is copied in one launch.  A pool block holds all heads
-// ([Hkv][B][D]), so each copy is one contiguous run per pool; each thread
-// moves one 16-byte piece of K and the same piece of V.
+// ([Hkv][B][D]), so each copy is one contiguous run per pool, cut into runs of
+// 16 KiB per workgroup.
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -70,24 +70,45 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(int64_t *__restrict__
   slots[t] = out;
 }
 
+// Workgroup w copies run w % per_pair of pair w / per_pair: kCopyUnroll
+// 16-byte pieces per thread and tensor, all loads issued before the stores.
+// Source and destination are touched once, so both go around the caches.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *__restrict__ kp,
                                                           uint16_t *__restrict__ vp,
                                                           const int64_t *__restrict__ pairs,
                                                           int64_t pieces,  // 16-byte pieces per block
-                                                          int64_t total, int64_t num_blocks) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int64_t i = idx / pieces;
-  const int64_t piece = idx - i * pieces;
-  const int64_t src = pairs[2 * i];
-  const int64_t dst = pairs[2 * i + 1];
+                                                          uint32_t per_pair, int64_t num_blocks) {
+  const uint32_t i = blockIdx.x / per_pair;
+  const uint32_t run = blockIdx.x - i * per_pair;
+  const int64_t src = pairs[2 * (int64_t)i];
+  const int64_t dst = pairs[2 * (int64_t)i + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const int64_t so = (src * pieces + piece) * 8;
-  const int64_t d_o = (dst * pieces + piece) * 8;
-  const u32x4 kv = *reinterpret_cast<const u32x4 *>(kp + so);
-  const u32x4 vv = *reinterpret_cast<const u32x4 *>(vp + so);
-  *reinterpret_cast<u32x4 *>(kp + d_o) = kv;
-  *reinterpret_cast<u32x4 *>(vp + d_o) = vv;
+  const int64_t first = (int64_t)run * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  const uint16_t *ks = kp + (src * pieces + first) * 8, *vs = vp + (src * pieces + first) * 8;
+  uint16_t *kd = kp + (dst * pieces + first) * 8, *vd = vp + (dst * pieces + first) * 8;
+  constexpr int kStep = kCopyThreads * 8;  // elements between a thread's pieces
+  if ((int64_t)(run + 1) * (kCopyThreads * kCopyUnroll) <= pieces) {
+    // a whole run: every load in flight before the first store
+    u32x4 kv[kCopyUnroll], vv[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ks + u * kStep));
+      vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vs + u * kStep));
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4 *>(kd + u * kStep));
+      __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4 *>(vd + u * kStep));
+    }
+  } else {
+    // the block's last, partial run
+    for (int u = 0; u < kCopyUnroll && first + u * kCopyThreads < pieces; ++u) {
+      const u32x4 kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ks + u * kStep));
+      const u32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vs + u * kStep));
+      __builtin_nontemporal_store(kv, reinterpret_cast<u32x4 *>(kd + u * kStep));
+      __builtin_nontemporal_store(vv, reinterpret_cast<u32x4 *>(vd + u * kStep));
+    }
+  }
 }
 
 // One thread per 16-byte piece of a (sequence, head) row, K and V; invalid
@@ -123,16 +144,22 @@ hipError_t launch_append_last(const DecodeParams &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int64_t copy_blocks_workgroups(int64_t num_pairs, int32_t Hkv, int32_t B, int32_t D) {
+  const int64_t pieces = (int64_t)Hkv * B * D / 8;
+  return num_pairs * ((pieces + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll));
+}
+
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
                               int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
                               hipStream_t stream) {
   const int64_t pieces = (int64_t)Hkv * B * D / 8;
-  const int64_t total = (int64_t)n * pieces;
-  if (total == 0) return hipSuccess;
-  const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+  const int64_t grid = copy_blocks_workgroups(n, Hkv, B, D);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const uint32_t per_pair = (uint32_t)(grid / n);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, stream,
                      reinterpret_cast<uint16_t *>(k_pool), reinterpret_cast<uint16_t *>(v_pool), pairs,
-                     pieces, total, num_blocks);
+                     pieces, per_pair, num_blocks);
   return hipGetLastError();
 }
 

@@ -410,7 +410,7 @@ pkv_status pkv_copy_blocks(void *k_pool, void *v_pool, const int64_t *block_pair
   if (num_pairs == 0) return PKV_OK;
   if (!k_pool || !v_pool || !block_pairs) return PKV_ERR_NULL;
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_pairs, 8)) return PKV_ERR_SHAPE;
-  if ((int64_t)num_pairs * p->num_kv_heads * p->block_size * (p->head_dim / 8) > ((int64_t)1 << 40))
+  if (pkv::copy_blocks_workgroups(num_pairs, p->num_kv_heads, p->block_size, p->head_dim) > 0x7FFFFFFF)
     return PKV_ERR_SHAPE;
   return hip_status(pkv::launch_copy_blocks(k_pool, v_pool, block_pairs, num_pairs, p->num_kv_heads,
                                             p->block_size, p->head_dim, p->num_blocks,

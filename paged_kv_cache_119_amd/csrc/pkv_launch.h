@@ -114,6 +114,12 @@ hipError_t launch_reshape_and_cache(void *k_pool, void *v_pool, const void *k, c
 // append fields of `a`).
 hipError_t launch_append_last(const DecodeParams &a, hipStream_t stream);
 
+// Block copy: each workgroup of kCopyThreads threads copies kCopyUnroll
+// 16-byte pieces per thread of one block of each pool; the launch has
+// copy_blocks_workgroups(...) workgroups (at most 2^31 - 1 are launched).
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+int64_t copy_blocks_workgroups(int64_t num_pairs, int32_t Hkv, int32_t B, int32_t D);
 hipError_t launch_copy_blocks(void *k_pool, void *v_pool, const int64_t *pairs, int32_t n,
                               int32_t Hkv, int32_t B, int32_t D, int64_t num_blocks,
                               hipStream_t stream);
