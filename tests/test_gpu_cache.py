@@ -194,6 +194,28 @@ def test_copy_blocks_exact_skips_invalid_pairs_and_empty_calls():
         pkv.copy_blocks(kp, vp, _pairs_tensor(pairs).to(torch.int32))
 
 
+@pytest.mark.parametrize("H,B,D,dtype", [(3, 8, 64, "bf16"), (5, 16, 128, "f16"), (7, 32, 64, "bf16"),
+                                         (12, 64, 64, "f16")])
+def test_copy_blocks_whole_runs_and_partial_runs(H, B, D, dtype):
+    """Blocks of 192, 1280, 1792 and 6144 16-byte pieces: a workgroup copies
+    1024 pieces of a block, so these cover a partial run alone, whole runs
+    followed by a partial one, and whole runs only; bit-exact against the
+    oracle's copy, invalid pairs skipped."""
+    log(f"copy_blocks: runs and partial runs H={H} B={B} D={D} {dtype}")
+    rng = np.random.default_rng(34 + H)
+    N = 96
+    kp = normal_16bit((N, H, B, D), dtype, DEV, 321 + H)
+    vp = normal_16bit((N, H, B, D), dtype, DEV, 331 + H)
+    kb, vb = to_bits(kp), to_bits(vp)
+    perm = rng.permutation(N)
+    pairs = [(int(perm[i]), int(perm[40 + i])) for i in range(37)]
+    pairs += [(int(perm[90]), -3), (N, int(perm[91]))]
+    pkv.copy_blocks(kp, vp, _pairs_tensor(pairs))
+    po.copy_blocks(kb, vb, pairs)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(kp), kb) and np.array_equal(to_bits(vp), vb)
+
+
 def test_copy_blocks_full_size_llama13b():
     """4096 copies in the 3.3 GB bf16 pools: every destination equals its
     source, every other block is unchanged."""
