@@ -691,30 +691,40 @@ template <int DT, int D, int TC>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
   constexpr int V = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)a.S * a.H;
+  if constexpr (D == 128 && TC == 32) {
+    // FP8 decode step with the append: the split pass attended over token
+    // L - 1's codes quantised from k_new / v_new; the workgroups past the
+    // merge's own write them to the pool slot (8 lanes x 16 codes per row, 8
+    // rows per wavefront; nothing for an invalid context or an entry outside
+    // the pool), beside the merge instead of ahead of it in its wavefronts.
+    const int64_t merge_blocks = (rows + 3) / 4;
+    if ((int64_t)blockIdx.x >= merge_blocks) {
+      const int64_t row = (((int64_t)blockIdx.x - merge_blocks) * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+      const int p = lane & 7;
+      if (!a.fp8 || !a.append || row >= rows) return;
+      const int s = (int)(row / a.H);
+      const int h = (int)(row - (int64_t)s * a.H);
+      const int L = a.lens[s];
+      if (L < 1 || L > a.maxb * a.B) return;
+      const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
+      if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
+      const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * D + p * 16;
+      const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * D + p * 16;
+      const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
+      const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + dst) =
+          quant16<DT>(ks[0], ks[1], a.k_inv);
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + dst) =
+          quant16<DT>(vs[0], vs[1], a.v_inv);
+      return;
+    }
+  }
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= (int64_t)a.S * a.H) return;
+  if (g >= rows) return;
   const int s = (int)(g / a.H);
   const int h = (int)(g - (int64_t)s * a.H);
   const int L = a.lens[s];
-  if constexpr (D == 128 && TC == 32) {
-    // FP8 decode step with the append: the split pass attended over token
-    // L - 1's codes quantised from k_new / v_new; write them to its pool
-    // slot now (8 lanes x 16 codes per row; nothing for an invalid context or
-    // an entry outside the pool)
-    if (a.fp8 && a.append && L >= 1 && L <= a.maxb * a.B && lane < 8) {
-      const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
-      if (blk >= 0 && (int64_t)blk < a.num_blocks) {
-        const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * D + lane * 16;
-        const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * D + lane * 16;
-        const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
-        const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + dst) =
-            quant16<DT>(ks[0], ks[1], a.k_inv);
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + dst) =
-            quant16<DT>(vs[0], vs[1], a.v_inv);
-      }
-    }
-  }
   const uint64_t cum_s = (uint64_t)a.ws_cum[s];
   const uint64_t total = (uint64_t)a.ws_cum[a.S];
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + g * D;
@@ -920,10 +930,12 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC>), dim3(grid), dim3(256), 0, stream, a)
     if (a.fp8) {
       if (a.D != 128 || fp8_chunk_tokens() != 32) return hipErrorInvalidValue;
+      // with the append: one more workgroup per 32 rows writes the new codes
+      const int fgrid = grid + (a.append ? (int)((segs + 31) / 32) : 0);
       if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32>), dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32>), dim3(fgrid), dim3(256), 0, stream, a);
       else
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32>), dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32>), dim3(fgrid), dim3(256), 0, stream, a);
     } else if (a.dtype == DT_F16) {
       if (a.D == 64) PKV_BMERGE(DT_F16, 64);
       else PKV_BMERGE(DT_F16, 128);
