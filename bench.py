@@ -50,6 +50,9 @@ def parse(argv=None):
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--one-call", action="store_true",
+                    help="time the whole decode step as one pkv_paged_attention_decode_append call (split + "
+                         "merge, the merge launch writing the new rows) instead of the split pass alone")
     ap.add_argument("--separate-append", action="store_true",
                     help="append with pkv_slot_mapping + pkv_reshape_and_cache, then decode")
     ap.add_argument("--duplicate-shared", action="store_true",
@@ -76,6 +79,9 @@ def main(argv=None) -> int:
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this path has no multi-GPU step (heads and sequences shard with "
               "no exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.one_call and (args.separate_append or args.op != "decode" or args.kv != "16bit"):
+        print("--one-call times the 16-bit decode step with the append fused", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -159,6 +165,13 @@ def main(argv=None) -> int:
 
     def step(i, ev=None):
         a_slot, a_app, a_dec, a_fused, a_mrg = calls[i % len(calls)]
+        if args.one_call:
+            if ev is not None:
+                ev[0].record(stream)
+            check(lib.pkv_paged_attention_decode_append(*a_fused), "paged_attention_decode_append")
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if args.separate_append:
             check(lib.pkv_slot_mapping(*a_slot), "slot_mapping")
             check(lib.pkv_reshape_and_cache(*a_app), "reshape_and_cache")
@@ -209,6 +222,8 @@ def main(argv=None) -> int:
         step_bytes = dec["total"] + app_write
         kern_bytes = step_bytes
         kern_name = ("decode_balanced_kernel" if P == 0 else "decode_partition_kernel") + " (append fused)"
+        if args.one_call:
+            kern_name += " + merge, one call"
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     kern_mean_ms = float(np.mean(kern_ms))
     achieved = kern_bytes / (kern_mean_ms * 1e-3) / 1e9
@@ -218,7 +233,8 @@ def main(argv=None) -> int:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash() and tr.get("config") == args.config and \
-                tr.get("partition_size") == P and tr.get("separate_append", False) == args.separate_append:
+                tr.get("partition_size") == P and tr.get("separate_append", False) == args.separate_append \
+                and not args.one_call:
             traffic = tr.get("hbm_bytes_per_launch")
 
     if args.copy_calibration:

@@ -302,7 +302,9 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
  * slots from the table).  The pool slot of token L_s - 1 receives the new row
  * bit for bit, and attention uses the new row for that token ("PagedAttention
  * 完全拆解", 原理详解（一）, Figure 6 walk-through: the new token's K/V goes into
- * its block, then attention runs over the blocks).
+ * its block, then attention runs over the blocks).  With the balanced split
+ * and one query head per KV head the split pass takes the new row from
+ * k_new / v_new and the merge launch writes it to the pool.
  *
  *   k_new, v_new  [num_seqs][Hkv][D], consecutive sequences new_token_stride
  *                 ELEMENTS apart (0 means Hkv * D); rows 16-byte aligned

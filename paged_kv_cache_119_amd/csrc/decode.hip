@@ -445,9 +445,11 @@ struct Stream {
   u32x4 qv;
   float m, l, acc[8];
   bool bad;
+  bool store_new;  // fused append: write the new rows here (else the merge launch does)
 
   __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_,
                                        int lane_) {
+    store_new = a.append_in_merge == 0;
     kp = reinterpret_cast<const uint16_t *>(a.k_pool);
     vp = reinterpret_cast<const uint16_t *>(a.v_pool);
     qp = reinterpret_cast<const uint16_t *>(a.q);
@@ -596,7 +598,7 @@ struct Stream {
       const int blk = b.app_blk;
       if (blk < 0 || (int64_t)blk >= num_blocks) {
         bad = true;
-      } else if (row == (d.L - 1) % TPI) {
+      } else if (store_new && row == (d.L - 1) % TPI) {
         const int64_t base = (int64_t)blk * blk_stride + (int64_t)d.h * B * D + ((d.L - 1) % B) * D + qoff;
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(kp) + base) = b.kn;
         *reinterpret_cast<u32x4 *>(const_cast<uint16_t *>(vp) + base) = b.vn;
@@ -692,33 +694,43 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   constexpr int V = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
   const int64_t rows = (int64_t)a.S * a.H;
-  if constexpr (D == 128 && TC == 32) {
-    // FP8 decode step with the append: the split pass attended over token
-    // L - 1's codes quantised from k_new / v_new; the workgroups past the
-    // merge's own write them to the pool slot (8 lanes x 16 codes per row, 8
-    // rows per wavefront; nothing for an invalid context or an entry outside
-    // the pool), beside the merge instead of ahead of it in its wavefronts.
-    const int64_t merge_blocks = (rows + 3) / 4;
-    if ((int64_t)blockIdx.x >= merge_blocks) {
-      const int64_t row = (((int64_t)blockIdx.x - merge_blocks) * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
-      const int p = lane & 7;
-      if (!a.fp8 || !a.append || row >= rows) return;
-      const int s = (int)(row / a.H);
-      const int h = (int)(row - (int64_t)s * a.H);
-      const int L = a.lens[s];
-      if (L < 1 || L > a.maxb * a.B) return;
-      const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
-      if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
-      const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * D + p * 16;
+  // Decode step with the append (FP8 pools, or a 16-bit balanced split that
+  // left the pool writes to this launch): the split pass attended over token
+  // L - 1's row taken from k_new / v_new (FP8: quantised); the workgroups past
+  // the merge's own write it to its pool slot, beside the merge instead of
+  // ahead of it in its wavefronts.  16 bytes per lane: a row takes D / 8 lanes
+  // (16-bit) or 8 lanes (FP8 codes, from 16-bit rows of 128); nothing for an
+  // invalid context or an entry outside the pool.
+  const int64_t merge_blocks = (rows + 3) / 4;
+  if ((int64_t)blockIdx.x >= merge_blocks) {
+    constexpr bool F8 = D == 128 && TC == 32;  // the FP8 instance
+    constexpr int LPR = F8 ? 8 : D / 8;        // lanes per row
+    const int64_t row = (((int64_t)blockIdx.x - merge_blocks) * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
+    const int p = lane % LPR;
+    if (!a.append || row >= rows) return;
+    const int s = (int)(row / a.H);
+    const int h = (int)(row - (int64_t)s * a.H);
+    const int L = a.lens[s];
+    if (L < 1 || L > a.maxb * a.B) return;
+    const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
+    if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
+    const int64_t slot = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * D;
+    if constexpr (F8) {
       const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * D + p * 16;
       const u32x4 *ks = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
       const u32x4 *vs = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + dst) =
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)) + slot + p * 16) =
           quant16<DT>(ks[0], ks[1], a.k_inv);
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + dst) =
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)) + slot + p * 16) =
           quant16<DT>(vs[0], vs[1], a.v_inv);
-      return;
+    } else {
+      const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * D + p * 8;
+      const u32x4 kv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.k_new) + src);
+      const u32x4 vv = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.v_new) + src);
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(const_cast<void *>(a.k_pool)) + slot + p * 8) = kv;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(const_cast<void *>(a.v_pool)) + slot + p * 8) = vv;
     }
+    return;
   }
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= rows) return;
@@ -926,8 +938,12 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
   if (a.balanced) {
     const int64_t segs = (int64_t)a.S * a.H;
     const int grid = (int)((segs + 3) / 4);
+    // a 16-bit split that left the pool writes to this launch: one more
+    // workgroup per 4 * 64 / (D / 8) rows writes them
+    const int rows_per_wg = 4 * 64 / (a.D / 8);
+    const int hgrid = grid + (a.append && a.append_in_merge ? (int)((segs + rows_per_wg - 1) / rows_per_wg) : 0);
 #define PKV_BMERGE(DT, DD) \
-  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC>), dim3(grid), dim3(256), 0, stream, a)
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC>), dim3(hgrid), dim3(256), 0, stream, a)
     if (a.fp8) {
       if (a.D != 128 || fp8_chunk_tokens() != 32) return hipErrorInvalidValue;
       // with the append: one more workgroup per 32 rows writes the new codes

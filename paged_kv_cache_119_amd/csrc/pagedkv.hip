@@ -531,6 +531,9 @@ pkv_status pkv_paged_attention_decode_append(void *out, const void *q, const voi
   if (st != PKV_OK) return st;
   const pkv_status s0 = append_if_separate(&a, (hipStream_t)stream);
   if (s0 != PKV_OK) return s0;
+  // balanced split, one row per KV head: the split pass substitutes the new
+  // rows and the merge launch writes them to the pool
+  if (a.append && a.balanced && !a.group) a.append_in_merge = 1;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

@@ -51,6 +51,9 @@ struct DecodeParams {
   // head) is taken from k_new / v_new ([S][Hkv][D], token stride new_stride
   // elements) and also written to its pool slot.
   int32_t append;
+  // Balanced 16-bit split with the append: the split pass only substitutes
+  // the new rows, and extra workgroups of the merge launch write them.
+  int32_t append_in_merge;
   const void *k_new;
   const void *v_new;
   int64_t new_stride;
