@@ -403,3 +403,36 @@ def test_fused_append_equals_separate_calls_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(kp.view(torch.int16), kp2.view(torch.int16))
     assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_one_call_step_equals_split_then_merge_bitwise(D):
+    """The one-call step (the merge launch writes the new rows) and the split
+    pass with its own writes followed by the merge give the same pools and
+    outputs bit for bit, empty and out-of-pool rows included."""
+    log(f"one-call step vs split + merge D={D}")
+    lengths = [1, 2, 15, 16, 17, 33, 64, 65, 127, 200, 511, 513, 0, 700, 1025, 40, 3]
+    t = build_tables(params=dict(name="small", index=41, num_heads=5, head_dim=D, dtype="bf16",
+                                 block_size=16, num_seqs=len(lengths), lengths=("fixed", lengths),
+                                 pool=("slack", 1.3), tables="permute", max_len=1100))
+    bt = t.block_tables.copy()
+    bt[15, (40 - 1) // 16] = t.num_blocks + 3  # token L - 1 of row 15 outside the pool
+    tab = torch.from_numpy(bt).to(DEV)
+    lens = torch.from_numpy(t.context_lens.astype(np.int32)).to(DEV)
+    kp, vp = make_pools(t, DEV)
+    kp2, vp2 = kp.clone(), vp.clone()
+    q = make_query(t, DEV)
+    from synth import normal_16bit
+    knew = normal_16bit((t.num_seqs, t.num_heads, D), t.dtype, DEV, 511)
+    vnew = normal_16bit((t.num_seqs, t.num_heads, D), t.dtype, DEV, 512)
+    one = pkv.paged_attention_decode_append(q, knew, vnew, kp, vp, tab, lens, t.scale)
+    ws = pkv.alloc_workspace(t.num_seqs, t.num_heads, t.max_blocks, kp2, 0)
+    two = torch.full_like(q, 0.0)
+    pkv.decode_partitions_append(q, knew, vnew, kp2, vp2, tab, lens, t.scale, two, ws)
+    pkv.decode_merge(two, lens, t.max_blocks, kp2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kp.view(torch.int16), kp2.view(torch.int16))
+    assert torch.equal(vp.view(torch.int16), vp2.view(torch.int16))
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    o = one.float().cpu().numpy()
+    assert np.all(o[12] == 0) and np.all(np.isnan(o[15]))
