@@ -5,6 +5,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -15,11 +17,19 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU" in r.stderr
 
 
+def test_one_call_is_refused_outside_the_fused_16bit_step():
+    for extra in (["--separate-append"], ["--kv", "fp8"], ["--op", "rows"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--one-call", *extra],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, extra
+        assert "--one-call" in r.stderr
+
+
 def test_help_lists_the_workload_options():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for opt in ("--config", "--op", "--kv", "--reuse-blocks", "--separate-append"):
+    for opt in ("--config", "--op", "--kv", "--reuse-blocks", "--separate-append", "--one-call"):
         assert opt in r.stdout
 
 
