@@ -688,8 +688,9 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
 // length and the chunk prefix; then every piece's (m, l) (lane j: piece j)
 // together with the o rows of the first four pieces.  Pieces are combined in
 // worker order.
-// TC is the chunk length of the split pass that wrote the partials.
-template <int DT, int D, int TC>
+// TC is the chunk length of the split pass that wrote the partials; F8: the
+// pools hold e4m3 codes (the appended rows are quantised when written).
+template <int DT, int D, int TC, bool F8>
 __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams a) {
   constexpr int V = D / 64;  // dims per lane
   const int lane = threadIdx.x & 63;
@@ -703,7 +704,6 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   // invalid context or an entry outside the pool.
   const int64_t merge_blocks = (rows + 3) / 4;
   if ((int64_t)blockIdx.x >= merge_blocks) {
-    constexpr bool F8 = D == 128 && TC == 32;  // the FP8 instance
     constexpr int LPR = F8 ? 8 : D / 8;        // lanes per row
     const int64_t row = (((int64_t)blockIdx.x - merge_blocks) * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
     const int p = lane % LPR;
@@ -943,15 +943,15 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
     const int rows_per_wg = 4 * 64 / (a.D / 8);
     const int hgrid = grid + (a.append && a.append_in_merge ? (int)((segs + rows_per_wg - 1) / rows_per_wg) : 0);
 #define PKV_BMERGE(DT, DD) \
-  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC>), dim3(hgrid), dim3(256), 0, stream, a)
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC, false>), dim3(hgrid), dim3(256), 0, stream, a)
     if (a.fp8) {
       if (a.D != 128 || fp8_chunk_tokens() != 32) return hipErrorInvalidValue;
       // with the append: one more workgroup per 32 rows writes the new codes
       const int fgrid = grid + (a.append ? (int)((segs + 31) / 32) : 0);
       if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32>), dim3(fgrid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32, true>), dim3(fgrid), dim3(256), 0, stream, a);
       else
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32>), dim3(fgrid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32, true>), dim3(fgrid), dim3(256), 0, stream, a);
     } else if (a.dtype == DT_F16) {
       if (a.D == 64) PKV_BMERGE(DT_F16, 64);
       else PKV_BMERGE(DT_F16, 128);
