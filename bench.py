@@ -49,7 +49,8 @@ def parse(argv=None):
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="seconds of oracle work per host core (the one-thread leg takes half)")
     ap.add_argument("--one-call", action="store_true",
                     help="time the whole decode step as one pkv_paged_attention_decode_append call (split + "
                          "merge, the merge launch writing the new rows) instead of the split pass alone")
@@ -602,7 +603,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
     achieved = kern_bytes / (kern_mean_ms * 1e-3) / 1e9
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_fp8(t, reps[0], ks, vs, args.cpu_budget_s)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(t, reps[0], args.cpu_budget_s, "fp8", ks, vs)
     ceiling = read_ceiling(torch, dev, kern_bytes)
     line = {
         "metric": "paged decode attention over an FP8 (e4m3) KV cache: achieved HBM GB/s + KV tokens/s",
@@ -631,37 +632,6 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
-
-
-def cpu_baseline_fp8(t, rep, ks, vs, budget_s: float):
-    """The oracle's e4m3 attention on host copies of one replica, one thread,
-    sequence by sequence until the time budget is used."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    from oracle import paged_oracle as po
-    from paged_kv_cache_119_amd import accounting as acc
-    from synth import to_bits
-
-    kp, vp, q, _, _, _ = rep
-    kc, vc = kp.cpu().numpy(), vp.cpu().numpy()
-    qb = to_bits(q)
-    done = []
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 <= budget_s:
-            s = len(done) % t.num_seqs
-            po.decode_rows_fp8(qb[s:s + 1, None], kc, vc, t.block_tables[s:s + 1], t.context_lens[s:s + 1],
-                               t.scale, t.block_size, t.dtype, ks, vs)
-            done.append(s)
-        dt = time.perf_counter() - t0
-    lens = t.context_lens[np.asarray(done)]
-    by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size, kv_dtype_bytes=1)["total"]
-    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} sequence decodes over e4m3 pools ({len(done) / t.num_seqs:.1f} passes over the "
-                      f"{t.num_seqs}-sequence batch, all {t.num_heads} heads), {int(lens.sum())} KV tokens, "
-                      f"{dt:.1f} s, numpy float64, 1 thread",
-            "kv_tokens_per_s": round(float(lens.sum()) / dt, 1)}
 
 
 def config_query_heads(t) -> int:
@@ -760,41 +730,125 @@ def describe_lengths(t) -> str:
     return f"min {int(L.min())} median {int(__import__('numpy').median(L))} max {int(L.max())}"
 
 
-def cpu_baseline(t, rep, budget_s: float):
-    """Float64 oracle on host copies of one replica, one BLAS thread, sequence
-    by sequence, passing over the batch again until the time budget is used
-    (a whole batch takes well under a second at the OPT-13B shape)."""
+def _oracle_pass(kind, files, meta, seqs, t_start, budget_s):
+    """One oracle timing leg (runs in a worker process, or in the parent for
+    the one-thread figure): wait until wall time t_start, then decode the
+    given sequences (all heads, in turn, again and again) until budget_s has
+    passed.  One BLAS thread.  Returns (sequences done, wall-clock start and
+    end of the timed window)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import paged_oracle as po
+
+    kb, vb, qb, tabs, lens = (np.load(f, mmap_mode="r") for f in files)
+    tabs, lens = np.asarray(tabs), np.asarray(lens)
+    done = []
+    with threadpool_limits(limits=1):
+        while time.time() < t_start:
+            time.sleep(0.001)
+        w0 = time.time()
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 <= budget_s:
+            s = seqs[i % len(seqs)]
+            i += 1
+            if kind == "fp8":
+                po.decode_rows_fp8(np.asarray(qb[s:s + 1])[:, None], kb, vb, tabs[s:s + 1], lens[s:s + 1],
+                                   meta["scale"], meta["block_size"], meta["dtype"], meta["k_scale"],
+                                   meta["v_scale"])
+            else:
+                for h in range(meta["num_heads"]):
+                    po.decode_one(qb, kb, vb, tabs, lens, meta["scale"], meta["block_size"], meta["dtype"], s, h)
+            done.append(s)
+        dt = time.perf_counter() - t0
+    return done, w0, w0 + dt
+
+
+def _oracle_worker(a):
+    return _oracle_pass(*a)
+
+
+def host_cores() -> tuple:
+    """(cores the oracle uses, cores this process may run on): the affinity
+    set, capped at the host-core share a one-GPU job gets (OMP_NUM_THREADS,
+    else 16)."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS") or 16)
+    except ValueError:
+        share = 16
+    return max(1, min(aff, share)), aff
+
+
+def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, vs: float = 1.0):
+    """The float64 oracle timed on the host's cores, on host copies of one
+    replica: N worker processes (N from host_cores(), one BLAS thread each)
+    take the batch's sequences round-robin and decode them, all heads,
+    passing over their share again until the budget is used; all workers
+    start at one wall-clock time and the rate is taken over the span from the
+    first start to the last end.  A one-thread leg in this process (budget / 2) is
+    reported beside it.  GB/s of the same algorithmic bytes, and KV tokens/s."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
+
     from paged_kv_cache_119_amd import accounting as acc
     from synth import to_bits
 
     kp, vp, q, _, _, _ = rep
-    kb, vb, qb = to_bits(kp), to_bits(vp), to_bits(q)
-    done = []
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            for s in range(t.num_seqs):
-                for h in range(t.num_heads):
-                    po.decode_one(qb, kb, vb, t.block_tables, t.context_lens, t.scale, t.block_size, t.dtype,
-                                  s, h)
-                done.append(s)
-                if time.perf_counter() - t0 > budget_s:
-                    break
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
-    lens = t.context_lens[np.asarray(done)]
-    by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size)["total"]
-    passes = len(done) / t.num_seqs
-    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(done)} sequence decodes ({passes:.1f} passes over the {t.num_seqs}-sequence batch, "
-                      f"all {t.num_heads} heads), {int(lens.sum())} KV tokens, {dt:.1f} s, numpy float64, "
-                      f"1 thread",
-            "kv_tokens_per_s": round(float(lens.sum()) / dt, 1)}
+    if kind == "fp8":
+        kb, vb = kp.cpu().numpy(), vp.cpu().numpy()
+    else:
+        kb, vb = to_bits(kp), to_bits(vp)
+    qb = to_bits(q)
+    meta = {"scale": t.scale, "block_size": t.block_size, "dtype": t.dtype, "num_heads": t.num_heads,
+            "k_scale": ks, "v_scale": vs}
+    kv_bytes = 1 if kind == "fp8" else None
+    tmp = tempfile.mkdtemp(prefix="pkv_oracle_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        files = []
+        for name, arr in (("k", kb), ("v", vb), ("q", qb), ("tab", t.block_tables), ("lens", t.context_lens)):
+            f = os.path.join(tmp, name + ".npy")
+            np.save(f, np.ascontiguousarray(arr))
+            files.append(f)
+        del kb, vb
+
+        def rate(done, dt):
+            lens = t.context_lens[np.asarray(done, dtype=np.int64)]
+            by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size, kv_dtype_bytes=kv_bytes)["total"]
+            return by, int(lens.sum())
+
+        # one thread, in this process
+        done1, a1, b1 = _oracle_pass(kind, files, meta, list(range(t.num_seqs)), 0.0, budget_s / 2)
+        dt1 = b1 - a1
+        by1, tok1 = rate(done1, dt1)
+
+        # N worker processes (started fresh, not forked from this GPU process)
+        n, aff = host_cores()
+        ctx = mp.get_context("spawn")
+        t_start = time.time() + 8.0  # time for the workers to start and import
+        jobs = [(kind, files, meta, list(range(w, t.num_seqs, n)) or [w % t.num_seqs], t_start, budget_s)
+                for w in range(n)]
+        with ctx.Pool(n) as pool:
+            res = pool.map(_oracle_worker, jobs)
+        done = [s for d, _, _ in res for s in d]
+        dt = max(b for _, _, b in res) - min(a for _, a, _ in res)  # span of all windows
+        by, tok = rate(done, dt)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    what = "sequence decodes over e4m3 pools" if kind == "fp8" else "sequence decodes"
+    return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"{len(done)} {what} ({len(done) / t.num_seqs:.1f} passes over the {t.num_seqs}-sequence "
+                      f"batch, all {t.num_heads} heads), {tok} KV tokens, {dt:.1f} s, numpy float64, {n} worker "
+                      f"processes x 1 BLAS thread ({aff} cores in the affinity set); the sequences dealt "
+                      f"round-robin to the workers",
+            "kv_tokens_per_s": round(tok / dt, 1),
+            "one_thread": {"value": round(by1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "kv_tokens_per_s": round(tok1 / dt1, 1),
+                           "sample": f"{len(done1)} {what}, {tok1} KV tokens, {dt1:.1f} s"}}
 
 
 if __name__ == "__main__":
