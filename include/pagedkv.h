@@ -66,7 +66,9 @@ typedef enum {
   PKV_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent    */
   PKV_ERR_UNSUPPORTED = 3, /* head_dim, block_size, dtype, GQA ratio or partition */
   PKV_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required             */
-  PKV_ERR_HIP = 5          /* the HIP runtime rejected a launch                   */
+  PKV_ERR_HIP = 5,         /* the HIP runtime rejected a launch                   */
+  PKV_ERR_SCRATCH = 6      /* pkv_paged_attention_decode_noalloc: the call needs
+                              more than the library's static scratch holds        */
 } pkv_status;
 
 typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
@@ -291,6 +293,46 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                       int32_t num_heads, int32_t max_blocks_per_seq,
                                       const pkv_pool *p, int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode with no
+ * workspace argument and no allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  The caller still owns q, the pools, the tables,
+ * context_lens and out.
+ *
+ * It computes exactly what pkv_paged_attention_decode computes with
+ * partition_size 0 (the balanced split), with the same kernels and the same
+ * split, so its output is bit for bit that call's on the same device.  The
+ * partial results and the chunk prefix go to a static device array of
+ * 16 MiB (256-byte aligned) inside the library instead of a workspace.  Each
+ * GPU the library runs on holds its own copy of that array until the process
+ * ends; its device address is taken on the first call on each device (with
+ * that device current).  The array needs no clearing: every call writes what
+ * it later reads.
+ *
+ * Need: (S + 1) * 8 bytes of chunk prefix, then (m, l, o) of float32, i.e.
+ * (D + 2) * 4 bytes, for each of (min(G, workers) + S * Hkv) * (H / Hkv)
+ * partial rows, each section rounded up to 256 bytes (G = worker wavefronts
+ * launched: compute units x resident workgroups x 4).  A call that needs more
+ * than 16 MiB returns PKV_ERR_SCRATCH and enqueues nothing.  On MI355X
+ * (G = 3072 at one query row per KV head) that admits, at D = 128, about
+ * 29,000 (sequence, head) rows: the 64 x 40 and 256 x 40 batches fit.
+ *
+ * Calls on one GPU share that GPU's array: two calls whose kernels may
+ * overlap on the same device (different streams, or different host threads
+ * without ordering) race and give wrong results.  Calls on one stream are
+ * ordered and safe.  partition_size is always 0; more than 4096 sequences
+ * (which need fixed partitions) return PKV_ERR_UNSUPPORTED.  Other
+ * arguments, layouts, restrictions and device-side rules as in
+ * pkv_paged_attention_decode.  Calls no hipMalloc, hipFree or other
+ * allocating routine.
+ */
+pkv_status pkv_paged_attention_decode_noalloc(void *out, const void *q, const void *k_pool,
+                                              const void *v_pool, const int32_t *block_tables,
+                                              const int32_t *context_lens, float scale, int32_t num_seqs,
+                                              int32_t num_heads, int32_t max_blocks_per_seq,
+                                              const pkv_pool *p, void *stream);
 
 /*
  * pkv_paged_attention_decode_append -- one decode step with the append fused

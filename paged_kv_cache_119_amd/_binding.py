@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 
 PKV_OK = 0
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
-                4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP"}
+                4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_SCRATCH"}
 DTYPE_CODES = {"f16": 0, "bf16": 1}
 
 # every symbol include/pagedkv.h declares
@@ -31,6 +31,7 @@ EXPORTS = (
     "pkv_decode_workspace_bytes",
     "pkv_decode_launch_info",
     "pkv_paged_attention_decode",
+    "pkv_paged_attention_decode_noalloc",
     "pkv_paged_attention_decode_append",
     "pkv_decode_partitions_append",
     "pkv_decode_partitions",
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_decode_workspace_bytes": (sz, [i32, i32, i32, pool, i32]),
         "pkv_paged_attention_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
                                                       i32, pool, i32, vp, sz, vp]),
+        "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
+                                                              i32, pool, vp]),
         "pkv_paged_attention_decode_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                                              i32, i32, i32, pool, i32, vp, sz, vp]),
         "pkv_decode_partitions_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
@@ -360,6 +363,23 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
                                         maxb, ctypes.byref(desc), int(partition_size), ws_ptr, ws_bytes,
                                         _stream_ptr(k_pool.device))
     _check(st, "pkv_paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out,
+                                   reuse_blocks=False):
+    """pkv_paged_attention_decode_noalloc: the decode of paged_attention_decode
+    (balanced split) with its partial results in the library's static device
+    scratch; nothing is allocated, so ``out`` must be passed.  Calls that may
+    overlap on one GPU race on that scratch."""
+    lib = load_library()
+    if out is None:
+        raise ValueError("out must be given: this call allocates nothing")
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
+    st = lib.pkv_paged_attention_decode_noalloc(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                                block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H,
+                                                maxb, ctypes.byref(desc), _stream_ptr(k_pool.device))
+    _check(st, "pkv_paged_attention_decode_noalloc")
     return out
 
 

@@ -37,6 +37,16 @@ int partition_unit(const pkv_pool *p) {
 
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
+// ---- static scratch of the no-allocation decode call
+//
+// Partial results and the chunk prefix of pkv_paged_attention_decode_noalloc
+// live in this array instead of a caller workspace.  Every device the library
+// runs on holds its own copy until the process ends.  In host code the name is
+// only a stand-in: kernels get the device address that hipGetSymbolAddress
+// returns, taken once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // ---- device properties, cached per device (CU count, balanced-kernel occupancy)
 
 struct OccEntry {
@@ -48,6 +58,7 @@ struct OccEntry {
 
 std::mutex g_cache_mu;
 int g_cus[64];            // 0 = not queried yet
+void *g_scratch[64];      // device address of `scratch` per device; NULL = not taken yet
 OccEntry g_occ[256];
 int g_occ_n = 0;
 
@@ -60,6 +71,19 @@ int device_cus(int dev) {
     g_cus[dev] = n;
   }
   return g_cus[dev];
+}
+
+// Device address of `scratch` on device `dev` (the current device), taken on
+// the first call for that device; NULL if the runtime refuses.
+void *scratch_on(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
 }
 
 int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
@@ -197,6 +221,25 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   return PKV_OK;
 }
 
+// The balanced split's workspace sized for the G workers actually launched
+// rather than for the most the batch could use: the chunk prefix, then (m, l,
+// o) for each (worker, KV row) pair that can hold a partial, times the query
+// rows per KV head.  A worker w < min(G, lay.workers) writes slot
+// (w + s * Hkv + h) * rows + r at most, so this holds every partial.
+void compact_layout(Layout *lay, int32_t G, int32_t num_seqs, int32_t num_kv_heads, int32_t rows,
+                    int32_t head_dim) {
+  const int64_t active = G < lay->workers ? (int64_t)G : lay->workers;
+  const int64_t units = (active + (int64_t)num_seqs * num_kv_heads) * rows;
+  const size_t cum = align_up((size_t)(num_seqs + 1) * sizeof(int64_t), kAlign);
+  const size_t sec = align_up((size_t)units * sizeof(float), kAlign);
+  lay->units = units;
+  lay->off_cum = 0;
+  lay->off_m = cum;
+  lay->off_l = cum + sec;
+  lay->off_o = cum + 2 * sec;
+  lay->bytes = cum + 2 * sec + align_up((size_t)units * head_dim * sizeof(float), kAlign);
+}
+
 // Workers (wavefronts) the balanced split launches for these arguments, 0 if
 // the device cannot be queried.  A small batch cannot use every resident
 // wavefront: whole workgroups for the most workers it can use (the split and
@@ -215,7 +258,7 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
                        int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
                        int32_t partition_size, const void *workspace, size_t workspace_bytes,
                        bool need_inputs, pkv::DecodeParams *a, int32_t num_queries = 1,
-                       bool fp8 = false) {
+                       bool fp8 = false, bool no_alloc = false) {
   if (num_seqs == 0) {  // nothing to do; still validate the static arguments
     Layout lay;
     const pkv_status st = decode_layout(0, num_heads, max_blocks, p, partition_size, num_queries, &lay, fp8);
@@ -234,6 +277,21 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
   Layout lay;
   const pkv_status st = decode_layout(num_seqs, num_heads, max_blocks, p, partition_size, num_queries, &lay, fp8);
   if (st != PKV_OK) return st;
+  int32_t G = 0;
+  if (no_alloc) {
+    // the static scratch of this device in place of a workspace
+    if (!lay.balanced) return PKV_ERR_UNSUPPORTED;
+    G = balanced_workers(p, num_seqs, lay, fp8);
+    if (G == 0) return PKV_ERR_HIP;
+    compact_layout(&lay, G, num_seqs, p->num_kv_heads, (num_heads / p->num_kv_heads) * num_queries,
+                   p->head_dim);
+    if (lay.bytes > kScratchBytes) return PKV_ERR_SCRATCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+    workspace = scratch_on(dev);
+    if (!workspace) return PKV_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (lay.bytes > 0) {
     if (!workspace || workspace_bytes < lay.bytes || !aligned(workspace, kAlign))
       return PKV_ERR_WORKSPACE;
@@ -252,10 +310,11 @@ pkv_status fill_params(void *out, const void *q, const void *k_pool, const void 
     a->ws_o = (float *)(ws + lay.off_o);
     a->ws_cum = lay.balanced ? (int64_t *)(ws + lay.off_cum) : nullptr;
   }
-  if (lay.balanced) {
-    a->G = balanced_workers(p, num_seqs, lay, fp8);
-    if (a->G == 0) return PKV_ERR_HIP;
+  if (lay.balanced && G == 0) {
+    G = balanced_workers(p, num_seqs, lay, fp8);
+    if (G == 0) return PKV_ERR_HIP;
   }
+  a->G = G;
   a->nq = num_queries;
   a->group = lay.group ? 1 : 0;
   a->fp8 = fp8 ? 1 : 0;
@@ -339,6 +398,7 @@ const char *pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype, head ratio or partition size";
     case PKV_ERR_WORKSPACE: return "workspace is NULL, too small or not 256-byte aligned";
     case PKV_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case PKV_ERR_SCRATCH: return "the call needs more than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -568,6 +628,21 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                     num_seqs, num_heads, max_blocks_per_seq, p, partition_size,
                                     workspace, workspace_bytes, true, &a);
   if (st != PKV_OK) return st;
+  const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
+  if (s1 != PKV_OK) return s1;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(void *out, const void *q, const void *k_pool,
+                                              const void *v_pool, const int32_t *block_tables,
+                                              const int32_t *context_lens, float scale, int32_t num_seqs,
+                                              int32_t num_heads, int32_t max_blocks_per_seq,
+                                              const pkv_pool *p, void *stream) {
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                                    num_seqs, num_heads, max_blocks_per_seq, p, 0, nullptr, 0, true, &a, 1,
+                                    false, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));

@@ -47,8 +47,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert pkv.version() == 2
-    for code in range(6):
+    for code in range(7):
         assert len(pkv.status_string(code)) > 0
+    assert "scratch" in pkv.status_string(6)
     assert pkv.status_string(99) == "unknown status"
 
 
