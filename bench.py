@@ -61,6 +61,9 @@ def parse(argv=None):
     ap.add_argument("--op", choices=("decode", "copy_blocks", "rows"), default="decode",
                     help="decode (the hot path, default), the batched block copy of copy-on-write, or "
                          "several query rows per KV head (grouped-query heads, multi-token queries)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="shared workload: decode with pkv_paged_attention_decode_shared (each prompt's prefix read "
+                         "once for its siblings) instead of the plain decode")
     ap.add_argument("--reuse-blocks", action="store_true",
                     help="pass the pool's reuse hint (cached K/V loads) for batches that share blocks")
     ap.add_argument("--kv", choices=("16bit", "fp8"), default="16bit",
@@ -111,6 +114,8 @@ def main(argv=None) -> int:
         return bench_rows(args, t, pkv, lib, dev)
     if args.kv == "fp8":
         return bench_fp8(args, t, pkv, lib, dev)
+    if args.shared_prefix:
+        return bench_shared(args, t, pkv, lib, dev)
     dup = None
     if args.duplicate_shared:
         dup_tab, copies, n_total = duplicate_shared(t)
@@ -629,6 +634,100 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
         "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True, not args.separate_append),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_shared(args, t, pkv, lib, dev) -> int:
+    """Groups of siblings sharing a prompt prefix, decoded with
+    pkv_paged_attention_decode_shared: one step is one call (prefix pass and
+    its merge, suffix pass and its merge).  `value` counts the batch's bytes
+    by the plain decode formula (every sequence's whole context), so it
+    compares with the plain decode of the same batch; `unique` counts the
+    bytes the call must move (each prefix once per group), and the roofline
+    prices the call on those."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_119_amd import accounting as acc
+    from synth import make_pools, make_query
+
+    if "siblings" not in t.extra:
+        print("--shared-prefix needs a workload of sibling groups (--config shared)", file=sys.stderr)
+        return 2
+    S, H, D, B = t.num_seqs, t.num_heads, t.head_dim, t.block_size
+    k = t.extra["siblings"]
+    P = t.extra["prefix_blocks"] * B
+    tab = torch.from_numpy(t.block_tables).to(dev)
+    lens = torch.from_numpy(t.context_lens).to(dev)
+    pl_np = np.full(S // k, P, np.int32)
+    pl = torch.from_numpy(pl_np).to(dev)
+    reps = []
+    for r in range(args.replicas):
+        t.seed += 1000 * r
+        kp, vp = make_pools(t, dev)
+        q = make_query(t, dev)
+        t.seed -= 1000 * r
+        reps.append((kp, vp, q, torch.empty_like(q)))
+    desc = pkv.pool_desc_of(reps[0][0], args.reuse_blocks)
+    dref = ctypes.byref(desc)
+    wsb = pkv.shared_prefix_workspace_bytes(S, H, t.max_blocks, reps[0][0], k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = int(stream.cuda_stream)
+
+    def step(i, ev=None):
+        kp, vp, q, out = reps[i % len(reps)]
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.pkv_paged_attention_decode_shared(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                   tab.data_ptr(), lens.data_ptr(), ctypes.c_float(t.scale), S, H,
+                                                   t.max_blocks, dref, k, pl.data_ptr(), ws.data_ptr(), wsb, sp)
+        if st != 0:
+            raise RuntimeError(f"paged_attention_decode_shared: {pkv.status_string(st)}")
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(KernelEvent(), KernelEvent()) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    by = acc.shared_prefix_bytes(t.context_lens, pl_np, k, H, D, 2, B)
+    call_mean = float(np.mean(call_ms))
+    achieved = by["total"] / (call_mean * 1e-3) / 1e9
+    assert torch.isfinite(reps[0][3].float()).all().item(), "non-finite output"
+    line = {
+        "metric": METRIC,
+        "value": round(by["logical"] / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": t.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.config}: {S // k} prompts x {k} siblings ({S} seqs) x {H} heads x {D}, "
+                               f"B={B}, {P}-token shared prefix, context_len {describe_lengths(t)}, decode with "
+                               f"each prefix read once per group (pkv_paged_attention_decode_shared)",
+                   "global_batch": S, "kv_tokens": t.kv_tokens(), "group_size": k, "prefix_tokens": P,
+                   "replicas": args.replicas, "parallelism": "none (1 GPU)"},
+        "value_counts": "logical bytes (every sequence's whole context, the plain decode formula)",
+        "logical_bytes": by["logical"], "unique_bytes": by["total"],
+        "unique_gbs": round(by["total"] / (ms_per_step * 1e-3) / 1e9, 2),
+        "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "shared-prefix call: prefix pass (decode_group_kernel) + merge, suffix pass "
+                               "(decode_balanced_kernel) + merge", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": by["total"],
+                     "mean_launch_us": round(call_mean * 1e3, 2)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -295,6 +295,54 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * pkv_paged_attention_decode_shared -- decode for batches whose sequences
+ * come in groups that share a prompt prefix (parallel samples of one prompt,
+ * the beams of one request, a common system prompt: "PagedAttention 完全拆解",
+ * 内存共享：并行采样、Beam Search 与共享前缀 and 共享前缀与系统提示词, where the
+ * prefix blocks are referenced by every sequence of the group).
+ *
+ * Computes exactly what pkv_paged_attention_decode computes (every
+ * sequence's attention over all its L tokens), but reads each group's prefix
+ * once for all its sequences instead of once per sequence.  The sum over a
+ * context splits into a prefix part and a suffix part merged by the
+ * log-sum-exp rule (the blockwise form of 原理详解（二）; the segment
+ * reduction of the iaim.asia block-table article, "vLLM 内核里的缓解写法"):
+ *   1. prefix pass (matrix-core kernel): per group and head, the prefix K/V
+ *      rows are streamed once and scored against the group_size query rows of
+ *      its sequences (a real contraction: group_size rows per K/V row); each
+ *      row's softmax state (max, sum, unnormalised V sum) goes to the
+ *      workspace;
+ *   2. suffix pass: each sequence's tokens prefix_len .. L - 1, starting from
+ *      its prefix state, then the merge of rows the split cut.
+ * Four launches on `stream`.
+ *
+ *   group_size    sequences per group (2 .. 16): sequences g * group_size ..
+ *                 (g + 1) * group_size - 1 form group g; num_seqs must be a
+ *                 multiple of it (else PKV_ERR_SHAPE)
+ *   prefix_lens   int32 [num_seqs / group_size], device: the leading tokens
+ *                 every sequence of group g shares.  Tokens 0 .. prefix_lens[g] - 1
+ *                 must hold the same K and V in every sequence of the group
+ *                 (shared blocks, or copies with the same contents); the
+ *                 prefix pass reads them through the group's first sequence's
+ *                 table row.  0 means no shared prefix.
+ *   workspace     >= pkv_shared_prefix_workspace_bytes(...) bytes, 256-byte
+ *                 aligned; needs no initialisation.
+ * Other arguments, layouts and device-side rules as in
+ * pkv_paged_attention_decode; a sequence shorter than its group's prefix
+ * gets a NaN row.  Restrictions (else PKV_ERR_UNSUPPORTED): head_dim 128,
+ * num_heads == num_kv_heads, num_seqs <= 4096.  The result depends only on
+ * the prefix contents: shared blocks and per-sequence copies give the same
+ * bits.  Differs from pkv_paged_attention_decode only by rounding.
+ */
+size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         const pkv_pool *p, int32_t group_size);
+pkv_status pkv_paged_attention_decode_shared(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                             const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                             int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                             const pkv_pool *p, int32_t group_size, const int32_t *prefix_lens,
+                                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pkv_paged_attention_decode_noalloc -- pkv_paged_attention_decode with no
  * workspace argument and no allocation, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, hosts

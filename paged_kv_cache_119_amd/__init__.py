@@ -12,7 +12,8 @@ from ._binding import (EXPORTS, LIB_PATH, POOL_REUSE, PagedKVError, PoolDesc, al
                        decode_workspace_bytes, fp8_decode_workspace_bytes, fp8_multi_workspace_bytes, fp8_pool_bytes,
                        load_library,
                        make_pool_desc, multi_workspace_bytes, paged_attention_decode, paged_attention_decode_append,
-                       paged_attention_decode_noalloc,
+                       paged_attention_decode_noalloc, paged_attention_decode_shared,
+                       shared_prefix_workspace_bytes,
                        paged_attention_decode_append_fp8, paged_attention_decode_fp8, paged_attention_multi,
                        paged_attention_multi_fp8,
                        pool_bytes, pool_desc_of, pool_index, reshape_and_cache, reshape_and_cache_fp8, slot_mapping,

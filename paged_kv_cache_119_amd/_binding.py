@@ -32,6 +32,8 @@ EXPORTS = (
     "pkv_decode_launch_info",
     "pkv_paged_attention_decode",
     "pkv_paged_attention_decode_noalloc",
+    "pkv_shared_prefix_workspace_bytes",
+    "pkv_paged_attention_decode_shared",
     "pkv_paged_attention_decode_append",
     "pkv_decode_partitions_append",
     "pkv_decode_partitions",
@@ -103,6 +105,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                       i32, pool, i32, vp, sz, vp]),
         "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32,
                                                               i32, pool, vp]),
+        "pkv_shared_prefix_workspace_bytes": (sz, [i32, i32, i32, pool, i32]),
+        "pkv_paged_attention_decode_shared": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i32,
+                                                             pool, i32, vp, vp, sz, vp]),
         "pkv_paged_attention_decode_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                                              i32, i32, i32, pool, i32, vp, sz, vp]),
         "pkv_decode_partitions_append": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
@@ -380,6 +385,37 @@ def paged_attention_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens
                                                 block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H,
                                                 maxb, ctypes.byref(desc), _stream_ptr(k_pool.device))
     _check(st, "pkv_paged_attention_decode_noalloc")
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_heads, max_blocks_per_seq, k_pool, group_size) -> int:
+    desc = pool_desc_of(k_pool)
+    return int(load_library().pkv_shared_prefix_workspace_bytes(int(num_seqs), int(num_heads),
+                                                                int(max_blocks_per_seq), ctypes.byref(desc),
+                                                                int(group_size)))
+
+
+def paged_attention_decode_shared(q, k_pool, v_pool, block_tables, context_lens, scale, group_size, prefix_lens,
+                                  out=None, workspace=None, reuse_blocks=False):
+    """Decode over groups of ``group_size`` consecutive sequences whose first
+    ``prefix_lens[g]`` tokens (int32 [S / group_size], device) hold the same
+    K/V: each group's prefix is read once for all its sequences
+    (pkv_paged_attention_decode_shared)."""
+    torch = _torch()
+    lib = load_library()
+    desc, S, H, maxb, out = _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_blocks)
+    _need(prefix_lens, "prefix_lens", dtype=torch.int32, ndim=1, device=k_pool.device)
+    if group_size < 1 or S % group_size != 0 or prefix_lens.shape[0] != S // group_size:
+        raise ValueError("prefix_lens must hold one length per group of group_size sequences")
+    need = shared_prefix_workspace_bytes(S, H, maxb, k_pool, group_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k_pool.device)
+    st = lib.pkv_paged_attention_decode_shared(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                               block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H,
+                                               maxb, ctypes.byref(desc), int(group_size), prefix_lens.data_ptr(),
+                                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                               _stream_ptr(k_pool.device))
+    _check(st, "pkv_paged_attention_decode_shared")
     return out
 
 

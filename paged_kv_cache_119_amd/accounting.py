@@ -87,3 +87,32 @@ def slot_mapping_bytes(num_tokens: int) -> int:
     """Slot translation: read (sequence, position) and one table entry, write
     one int64 slot per token."""
     return int(num_tokens) * (4 + 4 + TABLE_ENTRY_BYTES + SLOT_BYTES)
+
+
+def shared_prefix_bytes(context_lens, prefix_lens, group_size: int, num_heads: int, head_dim: int,
+                        dtype_bytes: int, block_size: int) -> dict:
+    """Algorithmic bytes of a decode over groups of ``group_size`` sequences
+    that share their first ``prefix_lens[g]`` tokens, when each group's
+    prefix is read once: the prefix K/V once per group, every sequence's own
+    tokens, q, out, the table entries read (the first sequence's prefix
+    entries once per group, every sequence's own), the lengths and the
+    prefix lengths.  ``logical`` is the same batch counted by the plain
+    decode formula (every sequence's whole context)."""
+    L = np.maximum(np.asarray(context_lens, dtype=np.int64), 0)
+    P = np.asarray(prefix_lens, dtype=np.int64)
+    S = int(L.shape[0])
+    own = np.maximum(L - np.repeat(P, group_size), 0)
+    row = num_heads * head_dim * 2 * dtype_bytes
+    kv = int(P.sum()) * row + int(own.sum()) * row
+    q = S * num_heads * head_dim * dtype_bytes
+    # the prefix pass reads a group's prefix entries once; a sequence's own
+    # tokens need the entries from the block holding token prefix_len on
+    pre_entries = int(sum(num_blocks_for(x, block_size) for x in P))
+    own_entries = int(sum(num_blocks_for(l, block_size) - p // block_size
+                          for l, p in zip(L, np.repeat(P, group_size)) if l > p))
+    table = (pre_entries + own_entries) * TABLE_ENTRY_BYTES
+    small = S * CONTEXT_LEN_BYTES + int(P.shape[0]) * CONTEXT_LEN_BYTES
+    total = kv + 2 * q + table + small
+    logical = decode_bytes(L, num_heads, head_dim, dtype_bytes, block_size)["total"]
+    return {"kv": kv, "q": q, "out": q, "table": table, "total": total, "logical": logical,
+            "kv_tokens": int(L.sum()), "unique_kv_tokens": int(P.sum() + own.sum())}

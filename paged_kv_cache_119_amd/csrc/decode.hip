@@ -45,6 +45,8 @@
 // whose later readers can then hit the last-level cache).  The load policy
 // never changes a result bit.
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_launch.h"
 #include "pkv_split.h"
@@ -410,18 +412,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
 // priority as it progresses through its slice, so wavefronts that share a
 // SIMD finish together instead of in order of age.
 
-template <int DT, int D, int B, bool APP, bool NT>
+// PFX: the suffix pass of the shared-prefix decode -- a row covers tokens
+// t0 .. L - 1 and, when t0 > 0, starts from the softmax state the prefix pass
+// left for it (lane group 0 takes it; the other groups start empty).
+template <int DT, int D, int B, bool APP, bool NT, bool PFX = false>
 struct Stream {
   using G = Geo<D>;
   static constexpr int LPT = G::LPT, TPI = G::TPI, NL = G::NL, TC = G::TC;
   static constexpr int NE = TC >= B ? TC / B : 1;  // table entries per chunk
   static_assert(B % TPI == 0, "a load must not straddle two blocks");
 
+  struct PfxState {
+    float m, l;
+    u32x4 o0, o1;  // 8 float32 sums as bits
+  };
+  struct NoState {};
   struct Buf {
     u32x4 k[NL], v[NL];
     u32x4 q, kn, vn;
     int app_blk;
     bool bad;
+    typename std::conditional<PFX, PfxState, NoState>::type ps;
   };
 
   // constants of the call
@@ -440,7 +451,10 @@ struct Stream {
   float scale_log2;
   int lane, lane_off, row, qoff;
   int64_t worker;
-  ChunkCursor<TC> cur;  // the slice, chunk by chunk
+  ChunkCursor<TC, PFX> cur;  // the slice, chunk by chunk
+  const float *pfx_m;
+  const float *pfx_l;
+  const float *pfx_o;
   // running state of the current piece
   u32x4 qv;
   float m, l, acc[8];
@@ -448,8 +462,11 @@ struct Stream {
   bool store_new;  // fused append: write the new rows here (else the merge launch does)
 
   __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_,
-                                       int lane_) {
+                                       int lane_, const int32_t *starts_ = nullptr) {
     store_new = a.append_in_merge == 0;
+    pfx_m = a.pfx_m;
+    pfx_l = a.pfx_l;
+    pfx_o = a.pfx_o;
     kp = reinterpret_cast<const uint16_t *>(a.k_pool);
     vp = reinterpret_cast<const uint16_t *>(a.v_pool);
     qp = reinterpret_cast<const uint16_t *>(a.q);
@@ -460,7 +477,7 @@ struct Stream {
     ws_m = a.ws_m;
     ws_l = a.ws_l;
     ws_o = a.ws_o;
-    cur.init(cum_, lens_, a.S, a.H, lane_);
+    cur.init(cum_, lens_, a.S, a.H, lane_, starts_, a.maxb, a.B);
     blk_stride = (int64_t)a.Hkv * B * D;
     num_blocks = a.num_blocks;
     new_stride = a.new_stride;
@@ -519,6 +536,17 @@ struct Stream {
     // Issued for every chunk (an L2 hit after the first), so every chunk
     // issues the same loads.
     b.q = *reinterpret_cast<const u32x4 *>(qp + ((int64_t)d.s * H + d.h) * D + qoff);
+    if constexpr (PFX) {
+      // the prefix state of the row, with the row's first chunk
+      if (d.c == d.c0 && d.t0 > 0) {
+        const int64_t g = (int64_t)d.s * H + d.h;
+        b.ps.m = pfx_m[g];
+        b.ps.l = pfx_l[g];
+        const u32x4 *po = reinterpret_cast<const u32x4 *>(pfx_o + g * D + qoff);
+        b.ps.o0 = po[0];
+        b.ps.o1 = po[1];
+      }
+    }
     if constexpr (APP) {
       // only the chunk of token L - 1 (once per row) loads the new rows
       if (is_app_chunk(d)) {
@@ -541,6 +569,17 @@ struct Stream {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.f;
       bad = false;
+      if constexpr (PFX) {
+        bad = d.t0 > d.L;  // the group's prefix is longer than this sequence
+        if (d.c == d.c0 && d.t0 > 0 && row == 0) {
+          m = b.ps.m;
+          l = b.ps.l;
+          const uint32_t w[8] = {b.ps.o0.x, b.ps.o0.y, b.ps.o0.z, b.ps.o0.w,
+                                 b.ps.o1.x, b.ps.o1.y, b.ps.o1.z, b.ps.o1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] = __uint_as_float(w[j]);
+        }
+      }
     }
     bad = bad || b.bad;
     const bool app = APP && is_app_chunk(d);
@@ -552,7 +591,7 @@ struct Stream {
         b.v[i] = sub ? b.vn : b.v[i];
       }
     }
-    const int t_lo = d.cb * TC;
+    const int t_lo = PFX ? max(d.cb * TC, d.t0) : d.cb * TC;
     const int t_hi = min(d.L, d.ce * TC);
     float z[NL];
 #pragma unroll
@@ -623,7 +662,7 @@ struct Stream {
     const int64_t g = (int64_t)d.s * H + d.h;
     if (lane < LPT) {
       const float nanv = bad ? __builtin_nanf("") : 0.f;
-      if (d.cb == 0 && d.ce * TC >= d.L) {
+      if (d.cb == d.c0 && d.ce * TC >= d.L) {
         // the whole row: final output
         uint32_t packed[4];
 #pragma unroll
@@ -648,19 +687,20 @@ struct Stream {
   }
 };
 
-template <int DT, int D, int B, int NW, bool APP, bool NT>
+template <int DT, int D, int B, int NW, bool APP, bool NT, bool PFX = false>
 __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a) {
-  using ST = Stream<DT, D, B, APP, NT>;
+  using ST = Stream<DT, D, B, APP, NT, PFX>;
   constexpr int TC = ST::TC;
 
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
+  int32_t *starts = lens + a.S;                               // [S] (PFX)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) build_cost_prefix<TC>(a, a.H, cum, lens, lane);
+  if (wave == 0) build_cost_prefix<TC, PFX>(a, a.H, cum, lens, lane, 1, starts);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
@@ -675,7 +715,7 @@ __global__ __launch_bounds__(NW * 64) void decode_balanced_kernel(DecodeParams a
   if (lo >= hi) return;
 
   ST st;
-  st.init(a, cum, lens, lane);
+  st.init(a, cum, lens, lane, starts);
   st.worker = w;
   st.cur.enter(lo, hi);
   __builtin_amdgcn_s_setprio(3);
@@ -745,7 +785,11 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
     for (int d = lane; d < D; d += 64) out_row[d] = v;
     return;
   }
-  const int nch = (L + TC - 1) / TC;
+  int nch = (L + TC - 1) / TC;
+  if (a.pfx_pass == 2) {  // suffix pass of a shared prefix: the row's suffix
+    int c0;
+    suffix_span<TC>(L, a.pfx_lens[s / a.pfx_group], a.maxb, a.B, c0, nch);
+  }
   const uint64_t seg = cum_s + (uint64_t)h * nch;
   const uint64_t end = seg + nch;  // the row's chunks are [seg, end)
   const uint64_t slice = slice_of(total, a.G);
@@ -866,6 +910,27 @@ struct BalancedF {
 };
 
 template <int DT, int D, int B>
+struct SuffixF {
+  static hipError_t call(const DecodeParams &a, hipStream_t st) {
+    if (a.stream_kv)
+      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, false, true, true>), dim3(a.G / kNumWaves),
+                         dim3(kNumWaves * 64), suffix_lds_bytes(a.S), st, a);
+    else
+      hipLaunchKernelGGL((decode_balanced_kernel<DT, D, B, kNumWaves, false, false, true>), dim3(a.G / kNumWaves),
+                         dim3(kNumWaves * 64), suffix_lds_bytes(a.S), st, a);
+    return hipGetLastError();
+  }
+};
+
+template <int DT, int D, int B>
+struct SuffixPtrF {
+  static const void *call(int nt) {
+    return nt ? reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false, true, true>)
+              : reinterpret_cast<const void *>(&decode_balanced_kernel<DT, D, B, kNumWaves, false, false, true>);
+  }
+};
+
+template <int DT, int D, int B>
 struct BalancedPtrF {
   static const void *call(int append, int nt) {
     if (append)
@@ -898,7 +963,37 @@ R dispatch(int dtype, int D, int B, R fail, Args... args) {
   return fail;
 }
 
+// F<DT, 128, B>::call(args...) for the runtime (dtype, B): head_dim 128 only.
+template <template <int, int, int> class F, typename R, typename... Args>
+R dispatch128(int dtype, int B, R fail, Args... args) {
+#define PKV_B(DT)                                  \
+  switch (B) {                                     \
+    case 8: return F<DT, 128, 8>::call(args...);   \
+    case 16: return F<DT, 128, 16>::call(args...); \
+    case 32: return F<DT, 128, 32>::call(args...); \
+    case 64: return F<DT, 128, 64>::call(args...); \
+    default: return fail;                          \
+  }
+  if (dtype == DT_F16) { PKV_B(DT_F16) }
+  PKV_B(DT_BF16)
+#undef PKV_B
+}
+
 }  // namespace
+
+const void *suffix_kernel(int dtype, int block_size, int nt) {
+  return dispatch128<SuffixPtrF, const void *>(dtype, block_size, nullptr, nt);
+}
+
+size_t suffix_lds_bytes(int num_seqs) {
+  return (size_t)(num_seqs + 1) * sizeof(int64_t) + 2 * (size_t)num_seqs * sizeof(int32_t);
+}
+
+hipError_t launch_suffix(const DecodeParams &a, hipStream_t stream) {
+  if (a.S == 0 || a.G == 0) return hipSuccess;
+  if (a.D != 128) return hipErrorInvalidValue;
+  return dispatch128<SuffixF, hipError_t>(a.dtype, a.B, hipErrorInvalidValue, a, stream);
+}
 
 int decode_waves() { return kNumWaves; }
 

@@ -153,6 +153,11 @@ struct GroupStream {
   float *ws_l;
   float *ws_o;
   int64_t blk_stride, num_blocks;
+  int64_t tstride;  // table entries between the rows of two sequences of this launch
+  bool pfx;         // the prefix pass of a shared-prefix decode
+  float *pfx_m;
+  float *pfx_l;
+  float *pfx_o;
   int S, Hkv, H, maxb, nq, gq, M;
   float scale_log2, v_scale;
   int lane, g, r;
@@ -183,6 +188,12 @@ struct GroupStream {
     Hkv = a.Hkv;
     H = a.H;
     maxb = a.maxb;
+    pfx = a.pfx_pass == 1;
+    // prefix pass: group i reads the table row of its first sequence
+    tstride = (int64_t)a.maxb * (pfx ? a.pfx_group : 1);
+    pfx_m = a.pfx_m;
+    pfx_l = a.pfx_l;
+    pfx_o = a.pfx_o;
     nq = a.nq;
     gq = a.H / a.Hkv;
     M = gq * nq;
@@ -200,7 +211,7 @@ struct GroupStream {
   // block; tokens past it are masked).
   __device__ __forceinline__ uint32_t load_entries(const Chunk &d) const {
     const int lb = min(first_block(d.c) + min(lane, NE - 1), last_block(d));
-    return (uint32_t)tables[(int64_t)d.s * maxb + lb];
+    return (uint32_t)tables[(int64_t)d.s * tstride + lb];
   }
 
   // Base element offset of token t of chunk d (its block from the entries).
@@ -280,7 +291,8 @@ struct GroupStream {
     // row r sees tokens [t_lo, min(t_hi, its causal limit))
     const int t_lo = d.cb * TC;
     const int t_hi = min(d.L, d.ce * TC);
-    const int lim = r < M ? d.L - nq + 1 + r / gq : 0;
+    // (prefix pass: every row sees the whole shared prefix)
+    const int lim = r < M ? (pfx ? d.L : d.L - nq + 1 + r / gq) : 0;
     const int t_row = min(t_hi, lim);
     float sc[4];
 #pragma unroll
@@ -373,7 +385,21 @@ struct GroupStream {
 #pragma unroll
       for (int s_ = 0; s_ < 8; ++s_) acc[s_] *= v_scale;
     }
-    if (d.cb == 0 && d.ce * TC >= d.L) {
+    if (pfx && d.cb == 0 && d.ce * TC >= d.L) {
+      // the whole row of a prefix pass: its softmax state (max in log2
+      // units, sum, unnormalised V sums) for the suffix pass
+      const int64_t pi = ((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi;
+      float *o = pfx_o + pi * GD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int s_ = 0; s_ < 8; ++s_) o[8 * (4 * g + i) + s_] = acc[s_][i] + nanv;
+      }
+      if (g == 0) {
+        pfx_m[pi] = m + nanv;
+        pfx_l[pi] = lp + nanv;
+      }
+    } else if (d.cb == 0 && d.ce * TC >= d.L) {
       // the whole row: final output, four runs of 8 dims per lane
       uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
       const float inv = 1.f / lp;
@@ -412,7 +438,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) build_cost_prefix<ST::TC>(a, a.Hkv, cum, lens, lane, a.nq);
+  if (wave == 0) build_cost_prefix<ST::TC>(a, a.Hkv, cum, lens, lane, a.pfx_pass == 1 ? 1 : a.nq);
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = tid; i <= a.S; i += NW * 64) a.ws_cum[i] = cum[i];
@@ -460,6 +486,10 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   const int L = a.lens[s];
   const uint64_t cum_s = (uint64_t)a.ws_cum[s];
   const uint64_t total = (uint64_t)a.ws_cum[a.S];
+  const bool pfx = a.pfx_pass == 1;
+  // prefix pass: a group without a valid prefix leaves no state (the suffix
+  // pass then reads none, or marks the row invalid)
+  if (pfx && (L <= 0 || L > a.maxb * a.B)) return;
   if (L <= 0 || L > a.maxb * a.B || L < a.nq) {
     const uint32_t v = (L == 0) ? 0u : 0x00010001u * to16<DT>(__builtin_nanf(""));
     if (live) {
@@ -510,6 +540,18 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] += f * ov[q][k];
     }
+  }
+  if (pfx) {
+    // the merged softmax state of the prefix (max in log2 units)
+    const int64_t pi = ((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi;
+    f4_t *dst = reinterpret_cast<f4_t *>(a.pfx_o + pi * GD + d0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = o[k];
+    if ((lane & 3) == 0) {
+      a.pfx_m[pi] = mx * kLog2e;
+      a.pfx_l[pi] = lsum;
+    }
+    return;
   }
   uint32_t w[16];
 #pragma unroll

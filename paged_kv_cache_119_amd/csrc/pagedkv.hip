@@ -102,15 +102,16 @@ int kernel_blocks_per_cu(int dev, const void *kernel, size_t lds) {
 
 // Workers (wavefronts) the balanced split launches on the current device: as
 // many as the device holds at once.  0 if the device cannot be queried.
-int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
+int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8, bool suffix = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int cus = device_cus(dev);
   if (cus <= 0) return 0;
   // occupancy for the LDS of this many sequences, rounded up to 4 KiB
-  const size_t lds = align_up(group ? pkv::group_lds_bytes(num_seqs)
-                              : fp8 ? pkv::fp8_lds_bytes(num_seqs)
-                                    : pkv::balanced_lds_bytes(num_seqs),
+  const size_t lds = align_up(group    ? pkv::group_lds_bytes(num_seqs)
+                              : fp8    ? pkv::fp8_lds_bytes(num_seqs)
+                              : suffix ? pkv::suffix_lds_bytes(num_seqs)
+                                       : pkv::balanced_lds_bytes(num_seqs),
                               4096);
   // the smallest occupancy over the instances a call may launch (fused append
   // or not, streamed or cached K/V loads), so that the split and merge passes
@@ -118,9 +119,10 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8) {
   int nb = 1 << 30;
   for (int nt = 0; nt < 2; ++nt) {
     for (int app = 0; app < 2; ++app) {
-      const void *k = group ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
-                      : fp8 ? pkv::fp8_kernel(p->dtype, p->block_size, nt, app)
-                            : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
+      const void *k = group    ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
+                      : fp8    ? pkv::fp8_kernel(p->dtype, p->block_size, nt, app)
+                      : suffix ? pkv::suffix_kernel(p->dtype, p->block_size, nt)
+                               : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
       if (!k) return 0;
       const int b = kernel_blocks_per_cu(dev, k, lds);
       if (b <= 0) return 0;
@@ -383,6 +385,52 @@ pkv_status fill_append(void *out, const void *q, const void *k_new, const void *
 
 // A per-pool FP8 scale: positive and finite, with a finite float32 reciprocal.
 bool fp8_scale_ok(float s) { return s > 0.f && s <= 3.0e38f && 1.0f / s > 0.f && 1.0f / s <= 3.0e38f; }
+
+// ---- shared prompt prefixes
+
+// Workspace of pkv_paged_attention_decode_shared: the prefix pass's balanced
+// layout (groups as sequences, their members as query rows), the prefix
+// states of every (sequence, head) row, then the suffix pass's layout.
+struct SharedLayout {
+  Layout pre, suf;
+  size_t off_pre, off_state_m, off_state_l, off_state_o, off_suf, bytes;
+};
+
+pkv_status shared_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks, const pkv_pool *p,
+                         int32_t group_size, SharedLayout *sl) {
+  if (!p) return PKV_ERR_NULL;
+  if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || group_size < 1) return PKV_ERR_SHAPE;
+  if (num_heads != p->num_kv_heads || p->head_dim != 128 || group_size < 2 || group_size > 16 ||
+      num_seqs > pkv::kBalancedMaxSeqs)
+    return PKV_ERR_UNSUPPORTED;
+  if (num_seqs % group_size != 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks * p->block_size > (1 << 30)) return PKV_ERR_SHAPE;
+  *sl = SharedLayout{};
+  const int32_t groups = num_seqs / group_size;
+  // prefix pass: the matrix-core kernel's layout for `groups` sequences of
+  // group_size query rows per KV head
+  const pkv_status st = decode_layout(groups, num_heads, max_blocks, p, 0, group_size, &sl->pre);
+  if (st != PKV_OK) return st;
+  const pkv_status st2 = decode_layout(num_seqs, num_heads, max_blocks, p, 0, 1, &sl->suf);
+  if (st2 != PKV_OK) return st2;
+  if (!sl->pre.group || !sl->suf.balanced || sl->suf.group) return PKV_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)num_seqs * num_heads;
+  sl->off_pre = 0;
+  sl->off_state_m = align_up(sl->pre.bytes, kAlign);
+  sl->off_state_l = sl->off_state_m + align_up(rows * sizeof(float), kAlign);
+  sl->off_state_o = sl->off_state_l + align_up(rows * sizeof(float), kAlign);
+  sl->off_suf = sl->off_state_o + align_up(rows * p->head_dim * sizeof(float), kAlign);
+  sl->bytes = sl->off_suf + align_up(sl->suf.bytes, kAlign);
+  return PKV_OK;
+}
+
+void set_workspace(pkv::DecodeParams *a, const Layout &lay, char *base) {
+  a->ws_m = (float *)(base + lay.off_m);
+  a->ws_l = (float *)(base + lay.off_l);
+  a->ws_o = (float *)(base + lay.off_o);
+  a->ws_cum = (int64_t *)(base + lay.off_cum);
+}
 
 }  // namespace
 
@@ -747,6 +795,89 @@ pkv_status pkv_paged_attention_decode_append_fp8(void *out, const void *q, const
   const pkv_status s1 = hip_status(launch_split(a, (hipStream_t)stream));
   if (s1 != PKV_OK) return s1;
   return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                         const pkv_pool *p, int32_t group_size) {
+  SharedLayout sl;
+  if (shared_layout(num_seqs, num_heads, max_blocks_per_seq, p, group_size, &sl) != PKV_OK) return 0;
+  return sl.bytes;
+}
+
+pkv_status pkv_paged_attention_decode_shared(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                             const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                             int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq,
+                                             const pkv_pool *p, int32_t group_size, const int32_t *prefix_lens,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  SharedLayout sl;
+  const pkv_status st = shared_layout(num_seqs, num_heads, max_blocks_per_seq, p, group_size, &sl);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !prefix_lens) return PKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16)) return PKV_ERR_SHAPE;
+  if (!workspace || workspace_bytes < sl.bytes || !aligned(workspace, kAlign)) return PKV_ERR_WORKSPACE;
+  const int32_t groups = num_seqs / group_size;
+  char *ws = (char *)workspace;
+  float *st_m = (float *)(ws + sl.off_state_m);
+  float *st_l = (float *)(ws + sl.off_state_l);
+  float *st_o = (float *)(ws + sl.off_state_o);
+
+  pkv::DecodeParams base{};
+  base.out = out;
+  base.q = q;
+  base.k_pool = k_pool;
+  base.v_pool = v_pool;
+  base.tables = block_tables;
+  base.scale_log2 = scale * 1.4426950408889634f;
+  base.v_scale = 1.0f;
+  base.num_blocks = p->num_blocks;
+  base.H = num_heads;
+  base.Hkv = p->num_kv_heads;
+  base.maxb = max_blocks_per_seq;
+  base.B = p->block_size;
+  base.D = p->head_dim;
+  base.dtype = p->dtype;
+  base.balanced = 1;
+  base.stream_kv = (p->flags & PKV_POOL_REUSE) ? 0 : 1;
+  base.pfx_group = group_size;
+  base.pfx_lens = prefix_lens;
+  base.pfx_m = st_m;
+  base.pfx_l = st_l;
+  base.pfx_o = st_o;
+
+  // prefix pass: groups as sequences, their members as the query rows of each
+  // KV head, every row over the whole prefix; then its merge
+  pkv::DecodeParams pre = base;
+  pre.S = groups;
+  pre.lens = prefix_lens;
+  pre.nq = group_size;
+  pre.group = 1;
+  pre.pfx_pass = 1;
+  set_workspace(&pre, sl.pre, ws + sl.off_pre);
+  pre.G = balanced_workers(p, groups, sl.pre, false);
+  if (pre.G == 0) return PKV_ERR_HIP;
+
+  // suffix pass: every sequence from its group's prefix length on, starting
+  // from the prefix state; then the merge of the rows it cuts
+  pkv::DecodeParams suf = base;
+  suf.S = num_seqs;
+  suf.lens = context_lens;
+  suf.nq = 1;
+  suf.pfx_pass = 2;
+  set_workspace(&suf, sl.suf, ws + sl.off_suf);
+  {
+    int32_t G = balanced_waves(p, num_seqs, false, false, true);
+    if (G == 0) return PKV_ERR_HIP;
+    const int nw = pkv::decode_waves();
+    const int64_t useful = (sl.suf.workers + nw - 1) / nw * nw;
+    suf.G = useful < G ? (int32_t)useful : G;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  pkv_status r = hip_status(pkv::launch_group_decode(pre, s));
+  if (r == PKV_OK) r = hip_status(pkv::launch_group_merge(pre, s));
+  if (r == PKV_OK) r = hip_status(pkv::launch_suffix(suf, s));
+  if (r == PKV_OK) r = hip_status(pkv::launch_decode_merge(suf, s));
+  return r;
 }
 
 size_t pkv_fp8_multi_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,

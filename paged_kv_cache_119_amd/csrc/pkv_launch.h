@@ -73,9 +73,29 @@ struct DecodeParams {
   // 1: K/V loads of the stream kernels are non-temporal (blocks read once
   // per call); 0: ordinary cached loads (blocks shared between sequences).
   int32_t stream_kv;
+  // Shared prompt prefixes (groups of pfx_group consecutive sequences whose
+  // first pfx_lens[group] tokens hold the same K/V).
+  //  pfx_pass 1, the prefix pass (matrix-core kernel): the sequences of this
+  //   launch are the groups (lens = pfx_lens, table row of group i = the row
+  //   of its first sequence), the query rows of a group are its sequences,
+  //   every row sees every prefix token, and each row's softmax state goes to
+  //   pfx_m (log2 units) / pfx_l / pfx_o (unnormalised) instead of out;
+  //  pfx_pass 2, the suffix pass (balanced kernel): sequence s attends over
+  //   tokens pfx_lens[s / pfx_group] .. L - 1, starting from that state.
+  int32_t pfx_pass;
+  int32_t pfx_group;
+  const int32_t *pfx_lens;
+  float *pfx_m;   // [S * H]
+  float *pfx_l;   // [S * H]
+  float *pfx_o;   // [S * H][D]
 };
 
 int decode_waves();
+// The suffix pass of the shared-prefix decode (16-bit, head_dim 128): its
+// kernel instance, dynamic LDS, split and merge launches.
+const void *suffix_kernel(int dtype, int block_size, int nt);
+size_t suffix_lds_bytes(int num_seqs);
+hipError_t launch_suffix(const DecodeParams &a, hipStream_t stream);
 // Tokens one wavefront step covers (partition sizes are multiples of it).
 int decode_chunk_tokens(int head_dim);
 // Dynamic LDS of the balanced kernel for num_seqs sequences.

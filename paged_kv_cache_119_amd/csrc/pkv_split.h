@@ -37,13 +37,38 @@ __device__ __forceinline__ uint64_t slice_of(uint64_t total, int G) {
   return max((uint64_t)1, udiv64(total + workers - 1, workers));
 }
 
+// Suffix pass of the shared-prefix decode: a row of L tokens whose first
+// `st` tokens were done by the prefix pass covers chunks c0 .. c0 + n - 1
+// (chunks of TC tokens from token 0).  A row with nothing left (L == st)
+// keeps one chunk, all of it masked, so that its output is still written from
+// the prefix state; st > L (a broken group) keeps one chunk and gives NaN.
+// Invalid contexts have no chunks.
+template <int TC>
+__device__ __forceinline__ void suffix_span(int L, int st, int maxb, int B, int &c0, int &n) {
+  if (L < 1 || L > maxb * B) {
+    c0 = 0;
+    n = 0;
+  } else if (st <= 0) {
+    c0 = 0;
+    n = (L + TC - 1) / TC;
+  } else if (st > L) {
+    c0 = (L - 1) / TC;
+    n = 1;
+  } else {
+    c0 = st / TC;
+    n = max(1, (L + TC - 1) / TC - c0);
+  }
+}
+
 // Prefix of the chunk count over sequences into LDS (cum[0] = 0, cum[S] =
 // total; a sequence has `rows` rows of row_chunks chunks each) and a copy of
 // the context lengths, computed by one wavefront: each lane sums a contiguous
-// run, then a scan.  Contexts shorter than min_len count as invalid.
-template <int TC>
+// run, then a scan.  Contexts shorter than min_len count as invalid.  PFX
+// (suffix pass): rows cover their suffix (suffix_span) and `starts` gets
+// each sequence's first token.
+template <int TC, bool PFX = false>
 __device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int rows, int64_t *cum, int32_t *lens,
-                                                  int lane, int min_len = 1) {
+                                                  int lane, int min_len = 1, int32_t *starts = nullptr) {
   const int S = a.S;
   const int per = (S + 63) / 64;
   const int s0 = min(S, lane * per);
@@ -52,7 +77,15 @@ __device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int row
   for (int s = s0; s < s1; ++s) {
     const int L = a.lens[s];
     lens[s] = L;
-    run += (int64_t)rows * row_chunks<TC>(L, a.maxb, a.B, min_len);
+    if constexpr (PFX) {
+      const int st = a.pfx_lens[s / a.pfx_group];
+      starts[s] = st;
+      int c0, n;
+      suffix_span<TC>(L, st, a.maxb, a.B, c0, n);
+      run += (int64_t)rows * n;
+    } else {
+      run += (int64_t)rows * row_chunks<TC>(L, a.maxb, a.B, min_len);
+    }
   }
   int64_t incl = run;
 #pragma unroll
@@ -63,44 +96,74 @@ __device__ __forceinline__ void build_cost_prefix(const DecodeParams &a, int row
   int64_t x = incl - run;  // exclusive prefix of this lane's run
   if (lane == 0) cum[0] = 0;
   for (int s = s0; s < s1; ++s) {
-    x += (int64_t)rows * row_chunks<TC>(lens[s], a.maxb, a.B, min_len);
+    if constexpr (PFX) {
+      int c0, n;
+      suffix_span<TC>(lens[s], starts[s], a.maxb, a.B, c0, n);
+      x += (int64_t)rows * n;
+    } else {
+      x += (int64_t)rows * row_chunks<TC>(lens[s], a.maxb, a.B, min_len);
+    }
     cum[s + 1] = x;
   }
 }
 
 // One chunk of a stream: chunk c of row (s, h), in the piece [cb, ce) of that
-// row the slice covers.  `valid` is false once the stream has ended; the
-// other fields then repeat the last chunk (so its loads stay in bounds).
+// row the slice covers.  Chunk indexes count TC-token chunks from token 0;
+// the row's chunks start at c0 (0 except in the suffix pass of a shared
+// prefix, whose rows start at token t0).  `valid` is false once the stream
+// has ended; the other fields then repeat the last chunk (so its loads stay
+// in bounds).
 struct Chunk {
-  int s, h, L, c, cb, ce;
+  int s, h, L, c, cb, ce, c0, t0;
   bool valid;
 };
 
 // Walks a wavefront's slice of the cost space chunk by chunk: sequences of
-// `rows` rows of ceil(L / TC) chunks each, with the chunk prefix `cum` and the
-// lengths `lens` in LDS.
-template <int TC>
+// `rows` rows of ceil(L / TC) chunks each (PFX: their suffix, suffix_span),
+// with the chunk prefix `cum`, the lengths `lens` (and PFX: the first tokens
+// `starts`) in LDS.
+template <int TC, bool PFX = false>
 struct ChunkCursor {
   const int64_t *cum;
   const int32_t *lens;
-  int S, rows, lane;
+  const int32_t *starts;
+  int S, rows, lane, maxb, B;
   uint64_t it_hi;
-  int cs_, ch_, cL, cn, cc, ccb, cce;  // s, h, L, chunks of row, chunk, piece [cb, ce)
-  uint64_t cseg;                      // cost position of chunk 0 of row (s, h)
+  int cs_, ch_, cL, cn, cc, ccb, cce;  // s, h, L, chunks of row, chunk, piece [cb, ce) (from the row's first)
+  int cc0, ct0;                       // row's first chunk and first token
+  uint64_t cseg;                      // cost position of the first chunk of row (s, h)
   bool cvalid;
   Chunk last;
 
-  __device__ __forceinline__ void init(const int64_t *cum_, const int32_t *lens_, int S_, int rows_, int lane_) {
+  __device__ __forceinline__ void init(const int64_t *cum_, const int32_t *lens_, int S_, int rows_, int lane_,
+                                       const int32_t *starts_ = nullptr, int maxb_ = 0, int B_ = 0) {
     cum = cum_;
     lens = lens_;
+    starts = starts_;
     S = S_;
     rows = rows_;
     lane = lane_;
+    maxb = maxb_;
+    B = B_;
     cvalid = false;
   }
 
   __device__ __forceinline__ uint64_t cum_at(int s) const { return uni64((uint64_t)cum[s]); }
   __device__ __forceinline__ int len_at(int s) const { return __builtin_amdgcn_readfirstlane(lens[s]); }
+
+  // Chunks of the rows of sequence s (which has some) and where they start.
+  __device__ __forceinline__ void span_of(int s) {
+    cL = len_at(s);
+    if constexpr (PFX) {
+      ct0 = __builtin_amdgcn_readfirstlane(starts[s]);
+      suffix_span<TC>(cL, ct0, maxb, B, cc0, cn);
+      ct0 = max(ct0, 0);
+    } else {
+      cc0 = 0;
+      ct0 = 0;
+      cn = (cL + TC - 1) / TC;
+    }
+  }
 
   // Largest s < S with cum[s] <= p (p < total): 64 samples per round.
   __device__ __forceinline__ int find_seq(uint64_t p) const {
@@ -123,8 +186,7 @@ struct ChunkCursor {
     const int s = find_seq(lo);
     const uint64_t base = cum_at(s);
     cs_ = s;
-    cL = len_at(s);
-    cn = (cL + TC - 1) / TC;  // sequence s has chunks: cum[s + 1] > lo >= cum[s]
+    span_of(s);  // sequence s has chunks: cum[s + 1] > lo >= cum[s]
     const uint64_t off = lo - base;  // < rows * cn
     const uint32_t h = off < (1ull << 32) ? (uint32_t)off / (uint32_t)cn : (uint32_t)udiv64(off, (uint64_t)cn);
     ch_ = (int)h;
@@ -149,8 +211,7 @@ struct ChunkCursor {
       while (cum_at(s + 1) == pos) ++s;  // sequences without chunks
       cs_ = s;
       ch_ = 0;
-      cL = len_at(s);
-      cn = (cL + TC - 1) / TC;
+      span_of(s);
     }
     cseg = pos;
     ccb = 0;
@@ -169,9 +230,11 @@ struct ChunkCursor {
     ch.s = cs_;
     ch.h = ch_;
     ch.L = cL;
-    ch.c = cc;
-    ch.cb = ccb;
-    ch.ce = cce;
+    ch.c = cc + cc0;
+    ch.cb = ccb + cc0;
+    ch.ce = cce + cc0;
+    ch.c0 = cc0;
+    ch.t0 = ct0;
     ch.valid = true;
     last = ch;
     if (cc + 1 < cce) ++cc;

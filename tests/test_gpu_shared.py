@@ -1,0 +1,220 @@
+"""GPU: decode of groups of sequences that share a prompt prefix
+(pkv_paged_attention_decode_shared: the prefix read once per group on the
+matrix cores, then each sequence's own tokens) against the float64 oracle's
+plain decode, which is the same attention over every sequence's whole
+context ("PagedAttention 完全拆解", 内存共享 / 共享前缀与系统提示词: shared
+prefix blocks are read like private ones)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import paged_kv_cache_119_amd as pkv  # noqa: E402
+from oracle import paged_oracle as po  # noqa: E402
+from synth import build_tables, duplicate_shared, make_pools, make_query, normal_16bit, to_bits  # noqa: E402
+
+from .gpu_util import DEV, HeadCache, assert_close, device_tables, log, oracle_samples, sample_pairs  # noqa: E402
+
+
+def _groups_case(prefixes, privs, H, D, B, dtype, seed):
+    """Groups of len(privs[g]) sequences; group g shares its first prefixes[g]
+    tokens, member j adds privs[g][j] tokens of its own.  Whole prefix blocks
+    are one copy referenced by every member; a partly filled last prefix
+    block is copied per member, as copy-on-write leaves it once the members
+    append.  Unused slots hold NaN."""
+    rng = np.random.default_rng(seed)
+    k = len(privs[0])
+    tables, lens, copies = [], [], []
+    nid = 0
+    for P, pv in zip(prefixes, privs):
+        full, part = divmod(P, B)
+        shared = list(range(nid, nid + full))
+        nid += full
+        first_part = None
+        for j, x in enumerate(pv):
+            L = P + x
+            row = list(shared)
+            own = -(-L // B) - full
+            ids = list(range(nid, nid + own))
+            nid += own
+            if part and own:
+                if first_part is None:
+                    first_part = ids[0]
+                else:
+                    copies.append((first_part, ids[0], part))
+            tables.append(row + ids)
+            lens.append(L)
+    N = nid + 3
+    perm = rng.permutation(N)
+    maxb = max(1, max(len(r) for r in tables))
+    tab = np.full((len(tables), maxb), -1, np.int32)
+    for s, r in enumerate(tables):
+        tab[s, :len(r)] = perm[np.asarray(r, dtype=np.int64)]
+    kp = normal_16bit((N, H, B, D), dtype, DEV, seed * 8 + 1)
+    vp = normal_16bit((N, H, B, D), dtype, DEV, seed * 8 + 2)
+    for src, dst, n in copies:  # equal contents for the prefix tokens
+        kp[perm[dst], :, :n] = kp[perm[src], :, :n]
+        vp[perm[dst], :, :n] = vp[perm[src], :, :n]
+    live = np.zeros((N, B), bool)
+    for s, L in enumerate(lens):
+        for j in range(L):
+            live[tab[s, j // B], j % B] = True
+    dead = torch.from_numpy(~live).to(DEV)[:, None, :, None].expand(kp.shape)
+    kp.masked_fill_(dead, float("nan"))
+    vp.masked_fill_(dead, float("nan"))
+    q = normal_16bit((len(lens), H, D), dtype, DEV, seed * 8 + 3)
+    return dict(kp=kp, vp=vp, q=q, tab=tab, lens=np.asarray(lens, np.int32), k=k,
+                pl=np.asarray(prefixes, np.int32), B=B, dtype=dtype, scale=1.0 / np.sqrt(D))
+
+
+def _copy_prefixes(c):
+    """The same batch with every member after a group's first reading its
+    own copy of the group's whole prefix blocks (appended to the pools)."""
+    tab = c["tab"].copy()
+    B, k = c["B"], c["k"]
+    src = []
+    nxt = c["kp"].shape[0]
+    for g, P in enumerate(c["pl"]):
+        for j in range(1, k):
+            s = g * k + j
+            for e in range(P // B):
+                src.append(int(tab[s, e]))
+                tab[s, e] = nxt
+                nxt += 1
+    idx = torch.tensor(src, dtype=torch.long, device=DEV)
+    return dict(c, tab=tab, kp=torch.cat([c["kp"], c["kp"][idx]], 0), vp=torch.cat([c["vp"], c["vp"][idx]], 0))
+
+
+def _run(c, tab=None, kp=None, vp=None):
+    tab = c["tab"] if tab is None else tab
+    out = pkv.paged_attention_decode_shared(c["q"], c["kp"] if kp is None else kp, c["vp"] if vp is None else vp,
+                                            torch.from_numpy(tab).to(DEV), torch.from_numpy(c["lens"]).to(DEV),
+                                            c["scale"], c["k"], torch.from_numpy(c["pl"]).to(DEV))
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(c):
+    return po.decode(to_bits(c["q"]), to_bits(c["kp"]), to_bits(c["vp"]), c["tab"], c["lens"], c["scale"], c["B"],
+                     c["dtype"])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+@pytest.mark.parametrize("k", [2, 6, 16])
+def test_groups_every_output(k, B, dtype):
+    """Prefixes across block and chunk edges (1, 17, 33, 512, 700 tokens, and
+    0: nothing shared), members with no own token, one token, and hundreds."""
+    log(f"shared prefix: k={k} B={B} {dtype}")
+    rng = np.random.default_rng(k * 100 + B)
+    prefixes = [33, 512, 1, 0, 700, 17]
+    privs = []
+    for g in range(len(prefixes)):
+        pv = [int(x) for x in rng.integers(0, 300, size=k)]
+        pv[0] = 0 if g % 2 == 0 else pv[0]   # a member with nothing past the prefix
+        pv[-1] = 1 if g % 3 == 0 else pv[-1]
+        if prefixes[g] == 0:
+            pv = [max(x, 1) for x in pv]
+        privs.append(pv)
+    c = _groups_case(prefixes, privs, 5, 128, B, dtype, 7 + k + B)
+    out = _run(c)
+    assert_close(to_bits(out), _oracle(c), dtype, f"shared k={k} B={B} {dtype}")
+
+
+def test_copies_of_the_prefix_give_the_same_bits():
+    """The result depends on the prefix contents only: one copy referenced by
+    every member, or a copy per member, give the same bits."""
+    prefixes, privs = [64, 129, 700], [[3, 0, 40, 200], [1, 1, 1, 1], [300, 2, 17, 64]]
+    a = _groups_case(prefixes, privs, 6, 128, 16, "f16", 31)
+    b = _copy_prefixes(a)
+    assert a["kp"].shape[0] < b["kp"].shape[0]
+    oa, ob = _run(a), _run(b)
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert_close(to_bits(ob), _oracle(b), "f16", "copied prefix")
+
+
+def test_sequence_shorter_than_its_prefix_gives_nan():
+    prefixes, privs = [100, 50], [[5, 0, 9], [1, 2, 3]]
+    c = _groups_case(prefixes, privs, 3, 128, 16, "bf16", 41)
+    pl = c["pl"].copy()
+    c["pl"] = np.asarray([101, 50], np.int32)  # member 1 of group 0 has exactly 100 tokens
+    out = _run(c)
+    o = po.bits_to_f64(to_bits(out), "bf16")
+    assert np.all(np.isnan(o[1]))
+    c["pl"] = pl
+    ref = _oracle(c)
+    good = [3, 4, 5]
+    assert_close(to_bits(out)[good], ref[good], "bf16", "groups after the broken one")
+
+
+def test_empty_and_invalid_contexts():
+    prefixes, privs = [40, 40], [[1, 2], [3, 4]]
+    c = _groups_case(prefixes, privs, 2, 128, 16, "f16", 43)
+    lens = c["lens"].copy()
+    lens[2] = 0
+    lens[3] = c["tab"].shape[1] * 16 + 5
+    c2 = dict(c, lens=lens)
+    out = _run(c2)
+    o = po.bits_to_f64(to_bits(out), "f16")
+    assert np.all(o[2] == 0) and np.all(np.isnan(o[3]))
+
+
+def test_shared_workload_sampled_and_copies_bitwise():
+    """The shared-prefix workload: 32 prompts x 6 siblings, a 512-token prefix
+    referenced by all six, 1..256 own tokens each.  Sampled outputs against
+    the oracle; the same bits with the prefix duplicated per sibling; the
+    plain decode of the same batch within the tolerance of the oracle too."""
+    log("shared workload: 192 seqs, group 6, prefix 512")
+    t = build_tables("shared")
+    k = t.extra["siblings"]
+    P = t.extra["prefix_blocks"] * t.block_size
+    tab, lens = device_tables(t)
+    kp, vp = make_pools(t, DEV)
+    q = make_query(t, DEV)
+    pl = torch.full((t.num_seqs // k,), P, dtype=torch.int32, device=DEV)
+    out = pkv.paged_attention_decode_shared(q, kp, vp, tab, lens, t.scale, k, pl)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(61)
+    pairs = sample_pairs(t, rng)
+    ref = oracle_samples(t, to_bits(q), HeadCache(kp, vp), pairs)
+    ob = to_bits(out)
+    assert_close(np.stack([ob[s, h] for s, h in pairs]), ref, t.dtype, f"shared call ({len(pairs)} samples)")
+    dup_tab, copies, n_total = duplicate_shared(t)
+    src = torch.tensor([c[0] for c in copies], device=DEV, dtype=torch.long)
+    kd = torch.cat([kp, kp[src]], 0)
+    vd = torch.cat([vp, vp[src]], 0)
+    out2 = pkv.paged_attention_decode_shared(q, kd, vd, torch.from_numpy(dup_tab).to(DEV), lens, t.scale, k, pl)
+    plain = pkv.paged_attention_decode(q, kp, vp, tab, lens, t.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    pb = to_bits(plain)
+    assert_close(np.stack([pb[s, h] for s, h in pairs]), ref, t.dtype, "plain decode, same samples")
+
+
+def test_argument_errors():
+    lib = pkv.load_library()
+    f = lib.pkv_paged_attention_decode_shared
+    w = lib.pkv_shared_prefix_workspace_bytes
+
+    def desc(H=4, D=128):
+        return pkv.make_pool_desc(64, 16, H, D, "f16")
+
+    d = desc()
+    assert w(12, 4, 8, ctypes.byref(d), 6) > 0
+    assert w(12, 4, 8, ctypes.byref(d), 1) == 0     # a group of one shares nothing
+    assert w(12, 4, 8, ctypes.byref(d), 17) == 0    # more than 16 sequences per group
+    assert w(12, 4, 8, ctypes.byref(d), 5) == 0     # 12 sequences are not groups of 5
+    assert w(12, 8, 8, ctypes.byref(d), 6) == 0     # grouped-query heads
+    assert w(12, 4, 8, ctypes.byref(desc(D=64)), 6) == 0
+    nul = None
+    assert f(nul, nul, nul, nul, nul, nul, 0.1, 12, 4, 8, ctypes.byref(d), 6, nul, nul, 0, nul) == 1
+    assert f(nul, nul, nul, nul, nul, nul, 0.1, 12, 4, 8, ctypes.byref(d), 5, nul, nul, 0, nul) == 2
+    assert f(nul, nul, nul, nul, nul, nul, 0.1, 12, 4, 8, ctypes.byref(d), 1, nul, nul, 0, nul) == 3
+    x = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    p = x.data_ptr()
+    assert f(p, p, p, p, p, p, 0.1, 12, 4, 8, ctypes.byref(d), 6, p, nul, 0, nul) == 4
