@@ -529,8 +529,9 @@ pkv_status pkv_reshape_and_cache_fp8(void *k_pool, void *v_pool, const void *k, 
  *   out, q        [num_seqs][num_heads][head_dim] 16-bit (p->dtype)
  *   num_heads     a multiple of Hkv, at most 16 query heads per KV head
  *                 (grouped-query heads run on the matrix-core kernel, with
- *                 the codes widened to the 16-bit type in registers);
- *                 head_dim 128; num_seqs <= 4096; else PKV_ERR_UNSUPPORTED
+ *                 the codes widened to the 16-bit type in registers, and
+ *                 need head_dim 128); one query head per KV head: head_dim
+ *                 64 or 128; num_seqs <= 4096; else PKV_ERR_UNSUPPORTED
  *   k_scale, v_scale  as for pkv_reshape_and_cache_fp8
  *   workspace     >= pkv_fp8_decode_workspace_bytes(...) bytes, 256-byte aligned
  * pkv_fp8_decode_workspace_bytes returns 0 for invalid or unsupported

@@ -744,7 +744,7 @@ __global__ __launch_bounds__(256) void decode_balanced_merge_kernel(DecodeParams
   // invalid context or an entry outside the pool.
   const int64_t merge_blocks = (rows + 3) / 4;
   if ((int64_t)blockIdx.x >= merge_blocks) {
-    constexpr int LPR = F8 ? 8 : D / 8;        // lanes per row
+    constexpr int LPR = F8 ? D / 16 : D / 8;  // lanes per row
     const int64_t row = (((int64_t)blockIdx.x - merge_blocks) * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
     const int p = lane % LPR;
     if (!a.append || row >= rows) return;
@@ -1040,13 +1040,23 @@ hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream) {
 #define PKV_BMERGE(DT, DD) \
   hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, Geo<DD>::TC, false>), dim3(hgrid), dim3(256), 0, stream, a)
     if (a.fp8) {
-      if (a.D != 128 || fp8_chunk_tokens() != 32) return hipErrorInvalidValue;
-      // with the append: one more workgroup per 32 rows writes the new codes
-      const int fgrid = grid + (a.append ? (int)((segs + 31) / 32) : 0);
-      if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_F16, 128, 32, true>), dim3(fgrid), dim3(256), 0, stream, a);
-      else
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<DT_BF16, 128, 32, true>), dim3(fgrid), dim3(256), 0, stream, a);
+      if (a.D != 64 && a.D != 128) return hipErrorInvalidValue;
+      // with the append: one more workgroup per 4 * 64 / (D / 16) rows writes
+      // the new codes
+      const int frows = 4 * 64 / (a.D / 16);
+      const int fgrid = grid + (a.append ? (int)((segs + frows - 1) / frows) : 0);
+      // the e4m3 split pass's chunks: 32 tokens at head_dim 128, 64 at 64
+#define PKV_FMERGE(DT, DD, TCC) \
+  hipLaunchKernelGGL((decode_balanced_merge_kernel<DT, DD, TCC, true>), dim3(fgrid), dim3(256), 0, stream, a)
+      if (fp8_chunk_tokens(a.D) != (a.D == 64 ? 64 : 32)) return hipErrorInvalidValue;
+      if (a.dtype == DT_F16) {
+        if (a.D == 64) PKV_FMERGE(DT_F16, 64, 64);
+        else PKV_FMERGE(DT_F16, 128, 32);
+      } else {
+        if (a.D == 64) PKV_FMERGE(DT_BF16, 64, 64);
+        else PKV_FMERGE(DT_BF16, 128, 32);
+      }
+#undef PKV_FMERGE
     } else if (a.dtype == DT_F16) {
       if (a.D == 64) PKV_BMERGE(DT_F16, 64);
       else PKV_BMERGE(DT_F16, 128);

@@ -15,9 +15,11 @@
 //    launch on large pools).  Grouped rows use a separate launch with no slot
 //    list before the split pass.
 //  * Decode (the attention equation of the same page, 背景): the balanced
-//    split and pipelined chunk stream of the 16-bit kernel, with 32-token
-//    chunks: 8 lanes hold a token row (16 codes each), a load instruction
-//    reads 8 whole rows (1 KiB).  Codes are widened in pairs by gfx950's
+//    split and pipelined chunk stream of the 16-bit kernel.  8 lanes hold a
+//    token row and a load instruction reads 8 whole rows: at head_dim 128,
+//    16 codes a lane (1 KiB an instruction) and 32-token chunks; at head_dim
+//    64, 8 codes a lane and 64-token chunks (4 KiB of each tensor per chunk
+//    either way).  Codes are widened in pairs by gfx950's
 //    packed conversions, exactly: K to the query's 16-bit type, so q.k runs
 //    on v_dot2c with exact products as in the 16-bit kernel; V to binary16,
 //    accumulated in float32 by mixed-precision FMAs.  The K scale is folded
@@ -34,11 +36,22 @@ namespace pkv {
 namespace {
 
 constexpr int kFp8Waves = PKV_DECODE_WAVES;
-constexpr int FD = 128;               // head_dim of this path
-constexpr int FLPT = 8;               // lanes per token row
-constexpr int FTPI = 64 / FLPT;       // token rows per load instruction
-constexpr int FNL = 4;                // loads per tensor per chunk
-constexpr int FTC = FNL * FTPI;       // tokens per chunk
+constexpr int FD = 128;  // head_dim of the grouped-row append below
+
+// Decode geometry for head_dim D: a lane loads BPL codes of a token row (16
+// at D = 128, 8 at D = 64), LPT = 8 lanes hold a row, a load instruction
+// reads 8 whole rows, and NL loads per tensor make a chunk of TC tokens, so
+// a chunk keeps 4 KiB of each tensor in flight at either head_dim.
+template <int D>
+struct F8Geo {
+  static constexpr int BPL = D == 128 ? 16 : 8;  // code bytes per lane per load
+  static constexpr int LPT = D / BPL;            // lanes per token row
+  static constexpr int TPI = 64 / LPT;           // token rows per load instruction
+  static constexpr int NL = 4096 / (64 * BPL);   // loads per tensor per chunk
+  static constexpr int TC = NL * TPI;            // tokens per chunk
+  static constexpr int NQ = BPL / 8;             // 16-byte pieces of 16-bit query per lane
+  static_assert(LPT == 8, "8 lanes per token row");
+};
 
 // Two e4m3 codes (bytes 0, 1 or, hi, bytes 2, 3 of w) -> a packed pair of the
 // 16-bit type, exactly (gfx950's packed conversion at unit scale).
@@ -117,26 +130,36 @@ __global__ __launch_bounds__(256) void append_last_fp8_kernel(DecodeParams a, fl
 // k_new / v_new, quantised here exactly as the append quantises it, in place
 // of the pool's codes (the merge launch writes the codes to the pool after
 // this pass has run).
-template <int DT, int B, bool NT, bool APP>
+template <int DT, int D, int B, bool NT, bool APP>
 struct Fp8Stream {
+  using GM = F8Geo<D>;
+  static constexpr int FLPT = GM::LPT, FTPI = GM::TPI, FNL = GM::NL, FTC = GM::TC, BPL = GM::BPL, NQ = GM::NQ;
   static constexpr int NE = FTC >= B ? FTC / B : 1;  // table entries per chunk
+  static constexpr int NWD = BPL / 4;                // dwords of codes per lane per load
   static_assert(B % FTPI == 0, "a load must not straddle two blocks");
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  using kv_t = typename std::conditional<BPL == 16, u32x4, u32x2_t>::type;
 
   struct BufP {
-    u32x4 k[FNL], v[FNL];
-    u32x4 q0, q1;
+    kv_t k[FNL], v[FNL];
+    u32x4 q[NQ];
     bool bad;
   };
   struct BufA {
-    u32x4 k[FNL], v[FNL];
-    u32x4 q0, q1;
+    kv_t k[FNL], v[FNL];
+    u32x4 q[NQ];
     // chunk of token L - 1 only: the new-token rows spread over the wave,
-    // lane l < 32 holding K elements 4l .. 4l+3, lane 32 + l V elements
-    // 4l .. 4l+3 (8 bytes a lane)
+    // lane l < D / 4 holding K elements 4l .. 4l+3, lane D / 4 + l V
+    // elements 4l .. 4l+3 (8 bytes a lane; lanes past D / 2 repeat them)
     uint32_t nw0, nw1;
     bool bad;
   };
   using Buf = typename std::conditional<APP, BufA, BufP>::type;
+
+  __device__ __forceinline__ static kv_t ld_codes(const uint8_t *p) {
+    if constexpr (BPL == 16) return ld_kv<NT>(p);
+    else return ld_kv8<NT>(p);
+  }
 
   const uint8_t *kp;
   const uint8_t *vp;
@@ -156,8 +179,8 @@ struct Fp8Stream {
   int lane, lane_off, row, qoff;
   int64_t worker;
   ChunkCursor<FTC> cur;
-  u32x4 qa, qb;  // this lane's 16 query elements as packed pairs
-  float m, l, acc[16];
+  u32x4 qv[NQ];  // this lane's BPL query elements as packed pairs
+  float m, l, acc[BPL];
   bool bad;
 
   __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_, int lane_) {
@@ -169,7 +192,7 @@ struct Fp8Stream {
     ws_m = a.ws_m;
     ws_l = a.ws_l;
     ws_o = a.ws_o;
-    blk_stride = (int64_t)a.Hkv * B * FD;
+    blk_stride = (int64_t)a.Hkv * B * D;
     num_blocks = a.num_blocks;
     H = a.H;
     maxb = a.maxb;
@@ -181,9 +204,9 @@ struct Fp8Stream {
     k_inv = a.k_inv;
     v_inv = a.v_inv;
     lane = lane_;
-    lane_off = lane * 16;
+    lane_off = lane * BPL;
     row = lane / FLPT;
-    qoff = (lane % FLPT) * 16;
+    qoff = (lane % FLPT) * BPL;
     cur.init(cum_, lens_, a.S, a.H, lane_);
   }
 
@@ -201,8 +224,8 @@ struct Fp8Stream {
   // Tokens past the context read the row of token L - 1 instead (cache lines
   // already fetched); they are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
-    const int64_t head_base = (int64_t)d.h * B * FD;
-    const int tail_off = ((d.L - 1) % B) * FD + qoff;
+    const int64_t head_base = (int64_t)d.h * B * D;
+    const int tail_off = ((d.L - 1) % B) * D + qoff;
     bool bd = false;
 #pragma unroll
     for (int i = 0; i < FNL; ++i) {
@@ -220,19 +243,21 @@ struct Fp8Stream {
         blk = 0;
       }
       const int64_t base = (int64_t)blk * blk_stride + head_base;
-      const int lo = (d.c * FTC + i * FTPI + row < d.L) ? off * FD + lane_off : tail_off;
-      b.k[i] = ld_kv<NT>(kp + base + lo);
-      b.v[i] = ld_kv<NT>(vp + base + lo);
+      const int lo = (d.c * FTC + i * FTPI + row < d.L) ? off * D + lane_off : tail_off;
+      b.k[i] = ld_codes(kp + base + lo);
+      b.v[i] = ld_codes(vp + base + lo);
     }
     b.bad = bd;
-    const uint16_t *q = qp + ((int64_t)d.s * H + d.h) * FD + qoff;
-    b.q0 = *reinterpret_cast<const u32x4 *>(q);
-    b.q1 = *reinterpret_cast<const u32x4 *>(q + 8);
+    const uint16_t *q = qp + ((int64_t)d.s * H + d.h) * D + qoff;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(q + 8 * j);
     if constexpr (APP) {
       // only the chunk of token L - 1 (once per row) loads the new rows
       if (is_app_chunk(d)) {
-        const int64_t src = (int64_t)d.s * new_stride + (int64_t)d.h * FD + 4 * (lane & 31);
-        const uint64_t w = *reinterpret_cast<const uint64_t *>((lane < 32 ? knp : vnp) + src);
+        constexpr int QL = D / 4;  // lanes quantising one tensor's row
+        const int ql = lane % (2 * QL);
+        const int64_t src = (int64_t)d.s * new_stride + (int64_t)d.h * D + 4 * (ql % QL);
+        const uint64_t w = *reinterpret_cast<const uint64_t *>((ql < QL ? knp : vnp) + src);
         b.nw0 = (uint32_t)w;
         b.nw1 = (uint32_t)(w >> 32);
       }
@@ -241,33 +266,31 @@ struct Fp8Stream {
 
   __device__ __forceinline__ void consume(const Chunk &d, Buf &b) {
     if (d.c == d.cb) {
-      qa = b.q0;
-      qb = b.q1;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) qv[j] = b.q[j];
       m = kNegInf;
       l = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+      for (int j = 0; j < BPL; ++j) acc[j] = 0.f;
       bad = false;
     }
     bad = bad || b.bad;
     if constexpr (APP) {
       if (is_app_chunk(d)) {
         // each lane quantises its 4 elements (the same quant4 steps as the
-        // append's); the lanes of token L - 1's row gather their 16 codes
-        // of K (from lanes 4(l%8) .. +3) and of V (32 + the same)
-        const float inv = lane < 32 ? k_inv : v_inv;
+        // append's); the lanes of token L - 1's row gather their BPL codes
+        // of K (from lanes NWD(l%8) .. +NWD-1) and of V (D / 4 + the same)
+        constexpr int QL = D / 4;
+        const float inv = (lane % (2 * QL)) < QL ? k_inv : v_inv;
         const int qd = (int)quant4(lo16<DT>(b.nw0) * inv, hi16<DT>(b.nw0) * inv, lo16<DT>(b.nw1) * inv,
                                    hi16<DT>(b.nw1) * inv);
-        const int sl = (lane & 7) * 4;
-        u32x4 kc, vc;
-        kc.x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * sl, qd);
-        kc.y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 1), qd);
-        kc.z = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 2), qd);
-        kc.w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + 3), qd);
-        vc.x = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (32 + sl), qd);
-        vc.y = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (33 + sl), qd);
-        vc.z = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (34 + sl), qd);
-        vc.w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (35 + sl), qd);
+        const int sl = (lane & 7) * NWD;
+        kv_t kc, vc;
+#pragma unroll
+        for (int j = 0; j < NWD; ++j) {
+          kc[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (sl + j), qd);
+          vc[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (QL + sl + j), qd);
+        }
 #pragma unroll
         for (int i = 0; i < FNL; ++i) {
           const bool sub = (d.c * FTC + i * FTPI + row) == d.L - 1;
@@ -283,18 +306,17 @@ struct Fp8Stream {
     for (int i = 0; i < FNL; ++i) {
       const int tok = d.c * FTC + i * FTPI + row;
       const bool valid = tok >= t_lo && tok < t_hi;
-      const uint32_t w[4] = {b.k[i].x, b.k[i].y, b.k[i].z, b.k[i].w};
-      const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
       float dot = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NWD; ++j) {
         // four codes -> two pairs of the query's type (exact), two dot2 steps
-        dot = dot2<DT>(qw[2 * j], pair16<DT>(w[j], false), dot);
-        dot = dot2<DT>(qw[2 * j + 1], pair16<DT>(w[j], true), dot);
+        const uint32_t w = b.k[i][j];
+        dot = dot2<DT>(qv[j / 2][2 * (j & 1)], pair16<DT>(w, false), dot);
+        dot = dot2<DT>(qv[j / 2][2 * (j & 1) + 1], pair16<DT>(w, true), dot);
       }
       const float dd = group_sum<FLPT>(dot) * scale_log2;
       z[i] = valid ? dd : kNegInf;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const kv_t zero = {};
       b.v[i] = valid ? b.v[i] : zero;
     }
     float mx = z[0];
@@ -312,14 +334,14 @@ struct Fp8Stream {
     }
     l = l * alpha + psum;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] *= alpha;
+    for (int j = 0; j < BPL; ++j) acc[j] *= alpha;
 #pragma unroll
     for (int i = 0; i < FNL; ++i) {
-      const uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NWD; ++j) {
         // four codes -> two binary16 pairs (exact), mixed-precision FMAs
-        const uint32_t h0 = pair16<DT_F16>(w[j], false), h1 = pair16<DT_F16>(w[j], true);
+        const uint32_t w = b.v[i][j];
+        const uint32_t h0 = pair16<DT_F16>(w, false), h1 = pair16<DT_F16>(w, true);
         acc[4 * j] = fmaf(pz[i], lo16<DT_F16>(h0), acc[4 * j]);
         acc[4 * j + 1] = fmaf(pz[i], hi16<DT_F16>(h0), acc[4 * j + 1]);
         acc[4 * j + 2] = fmaf(pz[i], lo16<DT_F16>(h1), acc[4 * j + 2]);
@@ -340,7 +362,7 @@ struct Fp8Stream {
       const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
       l = l * f1 + l2 * f2;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < BPL; ++j) {
         const float o2 = __shfl_xor(acc[j], off);
         acc[j] = acc[j] * f1 + o2 * f2;
       }
@@ -351,18 +373,19 @@ struct Fp8Stream {
       const float nanv = bad ? __builtin_nanf("") : 0.f;
       if (d.cb == 0 && d.ce * FTC >= d.L) {
         const float f = v_scale / l;
-        uint32_t w[8];
+        uint32_t w[BPL / 2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < BPL / 2; ++j)
           w[j] = (uint32_t)to16<DT>(acc[2 * j] * f + nanv) | ((uint32_t)to16<DT>(acc[2 * j + 1] * f + nanv) << 16);
-        uint16_t *o = outp + g * FD + qoff;
-        *reinterpret_cast<u32x4 *>(o) = u32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4 *>(o + 8) = u32x4{w[4], w[5], w[6], w[7]};
+        uint16_t *o = outp + g * D + qoff;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+          *reinterpret_cast<u32x4 *>(o + 8 * j) = u32x4{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
       } else {
         const int64_t u = worker + g;
-        float *o = ws_o + u * FD + qoff;
+        float *o = ws_o + u * D + qoff;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[j] = acc[j] * v_scale + nanv;
+        for (int j = 0; j < BPL; ++j) o[j] = acc[j] * v_scale + nanv;
         if (lane == 0) {
           ws_m[u] = m * kLn2 + nanv;  // natural-log units
           ws_l[u] = l + nanv;
@@ -372,9 +395,10 @@ struct Fp8Stream {
   }
 };
 
-template <int DT, int B, int NW, bool NT, bool APP>
+template <int DT, int D, int B, int NW, bool NT, bool APP>
 __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
-  using ST = Fp8Stream<DT, B, NT, APP>;
+  using ST = Fp8Stream<DT, D, B, NT, APP>;
+  constexpr int FTC = ST::FTC;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -402,49 +426,59 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(DecodeParams a) {
   __builtin_amdgcn_s_setprio(0);
 }
 
-template <int DT, bool NT, bool APP>
+template <int DT, int D, bool NT, bool APP>
 const void *fp8_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 8, kFp8Waves, NT, APP>);
-    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 16, kFp8Waves, NT, APP>);
-    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 32, kFp8Waves, NT, APP>);
-    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, 64, kFp8Waves, NT, APP>);
+    case 8: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, D, 8, kFp8Waves, NT, APP>);
+    case 16: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, D, 16, kFp8Waves, NT, APP>);
+    case 32: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, D, 32, kFp8Waves, NT, APP>);
+    case 64: return reinterpret_cast<const void *>(&decode_fp8_kernel<DT, D, 64, kFp8Waves, NT, APP>);
     default: return nullptr;
   }
 }
 
-template <int DT, int B, bool APP>
+template <int DT, int D, int B, bool APP>
 void launch_fp8_app(const DecodeParams &a, hipStream_t st) {
   if (a.stream_kv)
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, true, APP>), dim3(a.G / kFp8Waves),
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, D, B, kFp8Waves, true, APP>), dim3(a.G / kFp8Waves),
                        dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
   else
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, B, kFp8Waves, false, APP>), dim3(a.G / kFp8Waves),
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, D, B, kFp8Waves, false, APP>), dim3(a.G / kFp8Waves),
                        dim3(kFp8Waves * 64), fp8_lds_bytes(a.S), st, a);
 }
 
 template <int DT, int B>
 hipError_t launch_fp8(const DecodeParams &a, hipStream_t st) {
-  if (a.append) launch_fp8_app<DT, B, true>(a, st);
-  else launch_fp8_app<DT, B, false>(a, st);
+  if (a.D == 64) {
+    if (a.append) launch_fp8_app<DT, 64, B, true>(a, st);
+    else launch_fp8_app<DT, 64, B, false>(a, st);
+  } else {
+    if (a.append) launch_fp8_app<DT, 128, B, true>(a, st);
+    else launch_fp8_app<DT, 128, B, false>(a, st);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int fp8_chunk_tokens() { return FTC; }
+int fp8_chunk_tokens(int head_dim) { return head_dim == 64 ? F8Geo<64>::TC : F8Geo<128>::TC; }
 
 size_t fp8_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *fp8_kernel(int dtype, int block_size, int nt, int append) {
-  if (append) {
-    if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true, true>(block_size) : fp8_ptr<DT_BF16, true, true>(block_size);
-    return dtype == DT_F16 ? fp8_ptr<DT_F16, false, true>(block_size) : fp8_ptr<DT_BF16, false, true>(block_size);
+const void *fp8_kernel(int dtype, int head_dim, int block_size, int nt, int append) {
+  if (head_dim != 64 && head_dim != 128) return nullptr;
+#define PKV_P(DT, D)                                                                                   \
+  if (append) return nt ? fp8_ptr<DT, D, true, true>(block_size) : fp8_ptr<DT, D, false, true>(block_size); \
+  return nt ? fp8_ptr<DT, D, true, false>(block_size) : fp8_ptr<DT, D, false, false>(block_size);
+  if (dtype == DT_F16) {
+    if (head_dim == 64) { PKV_P(DT_F16, 64) }
+    PKV_P(DT_F16, 128)
   }
-  if (nt) return dtype == DT_F16 ? fp8_ptr<DT_F16, true, false>(block_size) : fp8_ptr<DT_BF16, true, false>(block_size);
-  return dtype == DT_F16 ? fp8_ptr<DT_F16, false, false>(block_size) : fp8_ptr<DT_BF16, false, false>(block_size);
+  if (head_dim == 64) { PKV_P(DT_BF16, 64) }
+  PKV_P(DT_BF16, 128)
+#undef PKV_P
 }
 
 hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {

@@ -120,7 +120,7 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8, bo
   for (int nt = 0; nt < 2; ++nt) {
     for (int app = 0; app < 2; ++app) {
       const void *k = group    ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
-                      : fp8    ? pkv::fp8_kernel(p->dtype, p->block_size, nt, app)
+                      : fp8    ? pkv::fp8_kernel(p->dtype, p->head_dim, p->block_size, nt, app)
                       : suffix ? pkv::suffix_kernel(p->dtype, p->block_size, nt)
                                : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
       if (!k) return 0;
@@ -157,8 +157,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   const int unit = partition_unit(p);
   *lay = Layout{};
   const int32_t rows = (num_heads / p->num_kv_heads) * num_queries;  // query rows per KV head
-  if (fp8 && (p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs))
-    return PKV_ERR_UNSUPPORTED;
+  if (fp8 && (partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)) return PKV_ERR_UNSUPPORTED;
   if (rows > 1) {
     // several query rows per KV head: the matrix-core kernel, balanced split only
     if (rows > 16 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
@@ -183,7 +182,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   }
   if (partition_size == 0 && num_seqs <= pkv::kBalancedMaxSeqs) {
     // work-balanced split; the cost space (chunks) must stay far below 2^47
-    const int tc = fp8 ? pkv::fp8_chunk_tokens() : pkv::decode_chunk_tokens(p->head_dim);
+    const int tc = fp8 ? pkv::fp8_chunk_tokens(p->head_dim) : pkv::decode_chunk_tokens(p->head_dim);
     const int64_t row_chunks = (ctx + tc - 1) / tc;
     const double cost = (double)num_seqs * num_heads * (double)row_chunks;
     if (cost >= 1.0e12) return PKV_ERR_SHAPE;
@@ -565,7 +564,7 @@ pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t m
       k = pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0);
       lds = pkv::group_lds_bytes(num_seqs);
     } else if (fp8) {
-      k = pkv::fp8_kernel(p->dtype, p->block_size, nt, append ? 1 : 0);
+      k = pkv::fp8_kernel(p->dtype, p->head_dim, p->block_size, nt, append ? 1 : 0);
       lds = pkv::fp8_lds_bytes(num_seqs);
     } else {
       k = pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, append ? 1 : 0, nt);

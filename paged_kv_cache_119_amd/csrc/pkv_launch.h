@@ -115,10 +115,10 @@ const void *group_kernel(int dtype, int block_size, int nt, int fp8);
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);
-// FP8 (e4m3) pools, head_dim 128, one query row per KV head.
-int fp8_chunk_tokens();
+// FP8 (e4m3) pools, head_dim 64 or 128, one query row per KV head.
+int fp8_chunk_tokens(int head_dim);
 size_t fp8_lds_bytes(int num_seqs);
-const void *fp8_kernel(int dtype, int block_size, int nt, int append);
+const void *fp8_kernel(int dtype, int head_dim, int block_size, int nt, int append);
 // The decode step's append into e4m3 pools: token L - 1 of every sequence
 // from k_new / v_new (a.append fields), slots from the block table.
 hipError_t launch_append_last_fp8(const DecodeParams &a, float k_inv, float v_inv, hipStream_t stream);
