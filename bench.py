@@ -285,7 +285,10 @@ def main(argv=None) -> int:
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
-        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, P, 1, False, not args.separate_append),
+        "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, P, 1, False,
+                                                          not args.separate_append),
+                                   f"{args.config}/decode" + ("/separate" if args.separate_append else "")
+                                   + ("/one-call" if args.one_call else "")),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -504,7 +507,8 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2)},
         "cpu_baseline": None,
         "read_ceiling": ceiling,
-        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, Q, args.kv == "fp8"),
+        "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, Q, args.kv == "fp8"),
+                                   f"{args.config}/rows/G{G}/Q{Q}" + ("/fp8" if fp8 else "")),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -633,7 +637,9 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,
-        "occupancy": pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True, not args.separate_append),
+        "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True,
+                                                          not args.separate_append),
+                                   f"{args.config}/fp8" + ("/separate" if args.separate_append else "")),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -731,6 +737,27 @@ def bench_shared(args, t, pkv, lib, dev) -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def measured_occupancy(key: str):
+    """Waves per SIMD measured by a rocprofv3 counter pass (recorded in
+    profiles/ by rocprof_summary tables --occupancy) for this workload and
+    mode, while the library sources are the ones it was measured on."""
+    from paged_kv_cache_119_amd.rocprof_summary import OCCUPANCY_FILE, library_hash
+    if not os.path.exists(OCCUPANCY_FILE):
+        return None
+    with open(OCCUPANCY_FILE) as f:
+        rec = json.load(f).get(key)
+    if not rec or rec.get("library_hash") != library_hash():
+        return None
+    return {"waves_per_simd": rec["waves_per_simd"], "kernel": rec["kernel"], "counter": rec["counter"],
+            "source": rec["summary"]}
+
+
+def with_measured(info: dict, key: str) -> dict:
+    info = dict(info)
+    info["measured"] = measured_occupancy(key)
+    return info
 
 
 def config_query_heads(t) -> int:

@@ -267,7 +267,7 @@ pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t m
  *                 h / (num_heads / Hkv) (grouped-query attention, the
  *                 Llama-2-70B shape of the iaim.asia block-table article,
  *                 "末尾块的内部碎片").  With more than one query head per KV
- *                 head the matrix-core kernel runs: head_dim 128,
+ *                 head the matrix-core kernel runs: head_dim 64 or 128,
  *                 partition_size 0, at most 16 query heads per KV head and
  *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED.  The
  *                 fused-append entry points then run the append as its own
@@ -473,8 +473,9 @@ pkv_status pkv_decode_merge(void *out, const int32_t *context_lens, int32_t num_
  *   out, q        [num_seqs][num_queries][num_heads][head_dim], element type of
  *                 the pool; out 16-byte aligned
  *   num_heads     a multiple of Hkv (as above); (num_heads / Hkv) *
- *                 num_queries <= 16 query rows per KV head, head_dim 128,
- *                 num_seqs <= 4096, else PKV_ERR_UNSUPPORTED
+ *                 num_queries <= 16 query rows per KV head, head_dim 64 or
+ *                 128 (e4m3 pools: 128), num_seqs <= 4096, else
+ *                 PKV_ERR_UNSUPPORTED
  *   workspace     >= pkv_multi_workspace_bytes(...) bytes, 256-byte aligned
  * Rows of a sequence with 0 < L < num_queries (or an invalid L) are NaN (the
  * queries must be part of the context); L == 0 gives zero rows.  Runs a split

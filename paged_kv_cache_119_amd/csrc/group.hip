@@ -54,7 +54,7 @@ namespace pkv {
 namespace {
 
 constexpr int kGroupWaves = PKV_DECODE_WAVES;
-constexpr int GD = 128;  // head_dim of this path
+constexpr int GD = 128;  // head_dim of the e4m3 path (the 16-bit path takes 64 or 128)
 constexpr int GTC = 16;  // tokens per MFMA tile (and per chunk of 16-bit pools)
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -123,8 +123,16 @@ __device__ __forceinline__ f4_t mfma_pv(uint32_t v01, uint32_t v23, uint32_t p01
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int DT, int B, bool NT, bool F8>
+// GDIM: head_dim, 128 or (16-bit pools) 64.  At 64, K rows are 8 lanes x 16
+// bytes (8 rows per load instruction, two loads per 16-token tile), S^T takes
+// 2 k-slices, and O^T 4 slices: slice s gives output dim 8(m % 8) + 2s +
+// m / 8 to operand row m, so that a lane (r, g) of the V load, which holds
+// dims 8(r % 8) .. +8, supplies element 2s + r / 8 of them.
+template <int DT, int B, bool NT, bool F8, int GDIM = 128>
 struct GroupStream {
+  static_assert(GDIM == 128 || (GDIM == 64 && !F8), "head_dim 128, or 64 with 16-bit pools");
+  static constexpr int NKS = GDIM / 32;  // k-slices of S^T (and whole-row K loads per 16-token tile)
+  static constexpr int NS = GDIM / 16;   // 16-dim slices of O^T
   // tokens per chunk: e4m3 chunks hold two 16-token tiles, so that a stage
   // keeps as many bytes in flight as a 16-bit one
   static constexpr int TC = F8 ? 2 * GTC : GTC;
@@ -132,7 +140,7 @@ struct GroupStream {
   static constexpr int NE = TC >= B ? TC / B : 1;  // table entries per chunk
 
   struct Buf16 {
-    u32x4 k[4], v[4], q[4];
+    u32x4 k[NKS], v[4], q[NKS];
     bool bad;
   };
   struct Buf8 {
@@ -163,12 +171,13 @@ struct GroupStream {
   int lane, g, r;
   int64_t worker;
   // 16-bit pools: this wavefront's K transpose tile (16 token rows of kKRow
-  // 16-byte pieces)
-  static constexpr int kKRow = 17;
+  // 16-byte pieces; the padding piece keeps 16 lanes' reads off one bank)
+  static constexpr int kKRow = GDIM / 8 + 1;
+  static constexpr int kTile = 16 * kKRow;
   u32x4 *ktile;
   ChunkCursor<TC> cur;  // the slice, chunk by chunk
   // running state of the current piece (row r of this lane)
-  f4_t acc[8];
+  f4_t acc[NS];
   float m, lp;
   bool bad;
 
@@ -182,7 +191,7 @@ struct GroupStream {
     ws_l = a.ws_l;
     ws_o = a.ws_o;
     cur.init(cum_, lens_, a.S, a.Hkv, lane_);
-    blk_stride = (int64_t)a.Hkv * B * GD;
+    blk_stride = (int64_t)a.Hkv * B * GDIM;
     num_blocks = a.num_blocks;
     S = a.S;
     Hkv = a.Hkv;
@@ -230,7 +239,7 @@ struct GroupStream {
       bd = true;
       blk = 0;
     }
-    return (int64_t)blk * blk_stride + (int64_t)d.h * B * GD + (int64_t)off * GD;
+    return (int64_t)blk * blk_stride + (int64_t)d.h * B * GDIM + (int64_t)off * GDIM;
   }
 
   // Stage 2: K rows (16-bit: whole rows of tokens 4j + g; e4m3: token r), V
@@ -245,7 +254,7 @@ struct GroupStream {
     // query row r of this KV head (rows >= M read row 0 and are zeroed)
     const int rr = r < M ? r : 0;
     const int qi = rr / gq, gi = rr - (rr / gq) * gq;
-    const int64_t qrow = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
+    const int64_t qrow = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GDIM;
     if constexpr (F8) {
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
@@ -261,33 +270,35 @@ struct GroupStream {
 #pragma unroll
       for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 32 * g + 8 * j);
     } else {
-      // whole token rows (4 rows of 256 bytes per instruction): lane (r, g)
-      // of load j gets token 4j + g, dims 8r .. 8r+7; consume transposes
-      // them into the matrix-core layout through LDS
+      // whole token rows (GDIM / 8 lanes a row): lane l of load j gets token
+      // j * RPL + l / (GDIM / 8), dims 8(l % (GDIM / 8)) .. +8; consume
+      // transposes them into the matrix-core layout through LDS
+      constexpr int LPR = GDIM / 8;  // lanes per row
+      constexpr int RPL = 64 / LPR;  // rows per load
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kb = token_base(d, e, min(4 * j + g, last), bd) + 8 * r;
+      for (int j = 0; j < NKS; ++j) {
+        const int64_t kb = token_base(d, e, min(RPL * j + lane / LPR, last), bd) + 8 * (lane % LPR);
         b.k[j] = ld_kv<NT>(kp + 2 * kb);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * r;
+        const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * (r % LPR);
         b.v[t] = ld_kv<NT>(vp + 2 * vb);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
+      for (int j = 0; j < NKS; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
     }
     b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
   }
 
   // One 16-token tile starting at token t0: scores, online softmax and the
   // weighted V sum.
-  __device__ __forceinline__ void tile(const Chunk &d, int t0, const u32x4 (&kk)[4], const u32x4 (&vv)[4],
-                                       const u32x4 (&q)[4]) {
+  __device__ __forceinline__ void tile(const Chunk &d, int t0, const u32x4 (&kk)[NKS], const u32x4 (&vv)[4],
+                                       const u32x4 (&q)[NKS]) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     f4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st = mfma_qk<DT>(kk[j], r < M ? q[j] : zero, st);
+    for (int j = 0; j < NKS; ++j) st = mfma_qk<DT>(kk[j], r < M ? q[j] : zero, st);
     // row r sees tokens [t_lo, min(t_hi, its causal limit))
     const int t_lo = d.cb * TC;
     const int t_hi = min(d.L, d.ce * TC);
@@ -330,12 +341,15 @@ struct GroupStream {
       v[t] = (tok >= t_lo && tok < t_hi) ? vv[t] : zero;
     }
 #pragma unroll
-    for (int s_ = 0; s_ < 8; ++s_) {
+    for (int s_ = 0; s_ < NS; ++s_) {
       acc[s_] *= alpha;
-      // element s_ of the four V rows: dword s_/2, low or high half
-      const uint32_t sel = (s_ & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t v01 = __builtin_amdgcn_perm(v[1][s_ >> 1], v[0][s_ >> 1], sel);
-      const uint32_t v23 = __builtin_amdgcn_perm(v[3][s_ >> 1], v[2][s_ >> 1], sel);
+      // element e of the four V rows: dword e / 2, low or high half (e = s_
+      // at head_dim 128; 2 s_ + r / 8 at 64)
+      const int hi = GDIM == 128 ? (s_ & 1) : (r >> 3);
+      const int dw = GDIM == 128 ? (s_ >> 1) : s_;
+      const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+      const uint32_t v01 = __builtin_amdgcn_perm(v[1][dw], v[0][dw], sel);
+      const uint32_t v23 = __builtin_amdgcn_perm(v[3][dw], v[2][dw], sel);
       acc[s_] = mfma_pv<PT>(v01, v23, p01, p23, r01, r23, acc[s_]);
     }
   }
@@ -346,13 +360,13 @@ struct GroupStream {
       m = kNegInf;
       lp = 0.f;
 #pragma unroll
-      for (int s_ = 0; s_ < 8; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s_ = 0; s_ < NS; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
       bad = false;
     }
     bad = bad || b.bad;
 #pragma unroll
     for (int u = 0; u < NSUB; ++u) {
-      u32x4 kk[4], vv[4];  // K and V fragments of tile u in the 16-bit type
+      u32x4 kk[NKS], vv[4];  // K and V fragments of tile u in the 16-bit type
       if constexpr (F8) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -361,12 +375,13 @@ struct GroupStream {
         for (int t = 0; t < 4; ++t) vv[t] = widen8<DT_F16>(b.v[4 * u + t][0], b.v[4 * u + t][1]);
       } else {
         // K rows -> this wavefront's LDS tile -> lane (r, g) reads token r's
-        // dims 32j + 8g .. +8 for k-slice j (rows padded to 17 x 16 bytes, so
-        // neither the writes nor the reads of 16 lanes share a bank)
+        // dims 32j + 8g .. +8 for k-slice j (rows padded by one 16-byte piece,
+        // so neither the writes nor the reads of 16 lanes share a bank)
+        constexpr int LPR = GDIM / 8, RPL = 64 / LPR;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ktile[(4 * j + g) * kKRow + r] = b.k[j];
+        for (int j = 0; j < NKS; ++j) ktile[(RPL * j + lane / LPR) * kKRow + lane % LPR] = b.k[j];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kk[j] = ktile[r * kKRow + 4 * j + g];
+        for (int j = 0; j < NKS; ++j) kk[j] = ktile[r * kKRow + 4 * j + g];
 #pragma unroll
         for (int t = 0; t < 4; ++t) vv[t] = b.v[t];
       }
@@ -378,47 +393,87 @@ struct GroupStream {
   __device__ __forceinline__ void finish_piece(const Chunk &d) {
     lp += __shfl_xor(lp, 16);
     lp += __shfl_xor(lp, 32);
-    if (r >= M) return;
-    const int qi = r / gq, gi = r - (r / gq) * gq;
-    const float nanv = bad ? __builtin_nanf("") : 0.f;
     if constexpr (F8) {
 #pragma unroll
-      for (int s_ = 0; s_ < 8; ++s_) acc[s_] *= v_scale;
+      for (int s_ = 0; s_ < NS; ++s_) acc[s_] *= v_scale;
     }
+    if constexpr (GDIM == 128) {
+      // slice s_, value i: dim 8(4g + i) + s_ -- four runs of 8 dims per lane
+      if (r >= M) return;
+      float run[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int s_ = 0; s_ < 8; ++s_) run[i][s_] = acc[s_][i];
+      }
+      const int run_dim[4] = {8 * (4 * g), 8 * (4 * g + 1), 8 * (4 * g + 2), 8 * (4 * g + 3)};
+      write_piece<4>(d, run, run_dim);
+    } else {
+      // slice s_, value i: element 2 s_ + (g / 2) of the block 4(g % 2) + i,
+      // so lanes (r, g) and (r, g ^ 2) hold the even and the odd elements of
+      // the same four blocks; they swap halves and keep two whole blocks each
+      const bool even = g < 2;
+      float recv[8];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) recv[4 * k + t] = __shfl_xor(even ? acc[t][2 + k] : acc[t][k], 32);
+      }
+      if (r >= M) return;
+      float run[2][8];
+      int run_dim[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        run_dim[k] = 8 * (4 * (g & 1) + (even ? k : 2 + k));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          run[k][2 * t] = even ? acc[t][k] : recv[4 * k + t];
+          run[k][2 * t + 1] = even ? recv[4 * k + t] : acc[t][2 + k];
+        }
+      }
+      write_piece<2>(d, run, run_dim);
+    }
+  }
+
+  // The finished piece of this lane's row r: runs of 8 consecutive dims.
+  template <int NR>
+  __device__ __forceinline__ void write_piece(const Chunk &d, const float (&run)[NR][8], const int (&run_dim)[NR]) {
+    const int qi = r / gq, gi = r - (r / gq) * gq;
+    const float nanv = bad ? __builtin_nanf("") : 0.f;
     if (pfx && d.cb == 0 && d.ce * TC >= d.L) {
       // the whole row of a prefix pass: its softmax state (max in log2
       // units, sum, unnormalised V sums) for the suffix pass
       const int64_t pi = ((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi;
-      float *o = pfx_o + pi * GD;
+      float *o = pfx_o + pi * GDIM;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NR; ++i) {
 #pragma unroll
-        for (int s_ = 0; s_ < 8; ++s_) o[8 * (4 * g + i) + s_] = acc[s_][i] + nanv;
+        for (int e = 0; e < 8; ++e) o[run_dim[i] + e] = run[i][e] + nanv;
       }
       if (g == 0) {
         pfx_m[pi] = m + nanv;
         pfx_l[pi] = lp + nanv;
       }
     } else if (d.cb == 0 && d.ce * TC >= d.L) {
-      // the whole row: final output, four runs of 8 dims per lane
-      uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GD;
+      // the whole row: final output
+      uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GDIM;
       const float inv = 1.f / lp;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NR; ++i) {
         u32x4 w;
-        w.x = pack2<DT>(acc[0][i] * inv + nanv, acc[1][i] * inv + nanv);
-        w.y = pack2<DT>(acc[2][i] * inv + nanv, acc[3][i] * inv + nanv);
-        w.z = pack2<DT>(acc[4][i] * inv + nanv, acc[5][i] * inv + nanv);
-        w.w = pack2<DT>(acc[6][i] * inv + nanv, acc[7][i] * inv + nanv);
-        *reinterpret_cast<u32x4 *>(o + 8 * (4 * g + i)) = w;
+        w.x = pack2<DT>(run[i][0] * inv + nanv, run[i][1] * inv + nanv);
+        w.y = pack2<DT>(run[i][2] * inv + nanv, run[i][3] * inv + nanv);
+        w.z = pack2<DT>(run[i][4] * inv + nanv, run[i][5] * inv + nanv);
+        w.w = pack2<DT>(run[i][6] * inv + nanv, run[i][7] * inv + nanv);
+        *reinterpret_cast<u32x4 *>(o + run_dim[i]) = w;
       }
     } else {
       const int64_t u = (worker + (int64_t)d.s * Hkv + d.h) * M + r;
-      float *o = ws_o + u * GD;
+      float *o = ws_o + u * GDIM;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NR; ++i) {
 #pragma unroll
-        for (int s_ = 0; s_ < 8; ++s_) o[8 * (4 * g + i) + s_] = acc[s_][i] + nanv;
+        for (int e = 0; e < 8; ++e) o[run_dim[i] + e] = run[i][e] + nanv;
       }
       if (g == 0) {
         ws_m[u] = m * kLn2 + nanv;  // natural-log units
@@ -428,9 +483,9 @@ struct GroupStream {
   }
 };
 
-template <int DT, int B, int NW, bool NT, bool F8>
+template <int DT, int B, int NW, bool NT, bool F8, int GDIM = 128>
 __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
-  using ST = GroupStream<DT, B, NT, F8>;
+  using ST = GroupStream<DT, B, NT, F8, GDIM>;
   extern __shared__ int64_t lds[];
   int64_t *cum = lds;                                         // [S + 1]
   int32_t *lens = reinterpret_cast<int32_t *>(lds + a.S + 1);  // [S]
@@ -451,10 +506,10 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   const uint64_t hi = min(total, lo + slice);
   if (lo >= hi) return;
 
-  __shared__ u32x4 ktiles[F8 ? 1 : NW * 16 * ST::kKRow];
+  __shared__ u32x4 ktiles[F8 ? 1 : NW * ST::kTile];
   ST st;
   st.init(a, cum, lens, lane);
-  st.ktile = ktiles + (F8 ? 0 : wave * 16 * ST::kKRow);
+  st.ktile = ktiles + (F8 ? 0 : wave * ST::kTile);
   st.worker = w;
   st.cur.enter(lo, hi);
   __builtin_amdgcn_s_setprio(3);
@@ -467,7 +522,8 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
 // rows cut over several workers.  The pieces' (m, l) and o rows are fetched
 // four pieces per round of loads.
 // TC: the chunk length of the split pass that wrote the partials.
-template <int DT, int TC>
+// GDIM: head_dim (each lane takes GDIM / 4 dims of its row).
+template <int DT, int TC, int GDIM = 128>
 __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
@@ -478,11 +534,12 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   const int s = (int)(grow / a.Hkv);
   const int h = (int)(grow - (int64_t)s * a.Hkv);
   const int r = lane >> 2;         // this lane's query row (16 rows x 4 lanes)
-  const int d0 = (lane & 3) * 32;  // and its 32 dims
+  constexpr int NV = GDIM / 16;     // float4s of this lane's dims
+  const int d0 = (lane & 3) * (GDIM / 4);  // and its GDIM / 4 dims
   const bool live = r < M;
   const int qi = r / gq, gi = r - (r / gq) * gq;
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) +
-                      (((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi) * GD + d0;
+                      (((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi) * GDIM + d0;
   const int L = a.lens[s];
   const uint64_t cum_s = (uint64_t)a.ws_cum[s];
   const uint64_t total = (uint64_t)a.ws_cum[a.S];
@@ -494,7 +551,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     const uint32_t v = (L == 0) ? 0u : 0x00010001u * to16<DT>(__builtin_nanf(""));
     if (live) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{v, v, v, v};
+      for (int k = 0; k < NV / 2; ++k) reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{v, v, v, v};
     }
     return;
   }
@@ -517,20 +574,20 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   }
   // pieces combined in worker order
   float lsum = 0.f;
-  f4 o[8];
+  f4 o[NV];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NV; ++k) o[k] = f4{0.f, 0.f, 0.f, 0.f};
   for (int64_t j0 = 0; j0 < n; j0 += 4) {
     float mv[4], lv[4];
-    f4 ov[4][8];
+    f4 ov[4][NV];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t u = slot(min(j0 + q, n - 1));
       mv[q] = a.ws_m[u];
       lv[q] = a.ws_l[u];
-      const f4 *src = reinterpret_cast<const f4 *>(a.ws_o + u * GD + d0);
+      const f4 *src = reinterpret_cast<const f4 *>(a.ws_o + u * GDIM + d0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) ov[q][k] = src[k];
+      for (int k = 0; k < NV; ++k) ov[q][k] = src[k];
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -538,57 +595,60 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
       const float f = (mv[q] == kNegInf) ? 0.f : fast_exp2((mv[q] - mx) * kLog2e);
       lsum += f * lv[q];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] += f * ov[q][k];
+      for (int k = 0; k < NV; ++k) o[k] += f * ov[q][k];
     }
   }
   if (pfx) {
     // the merged softmax state of the prefix (max in log2 units)
     const int64_t pi = ((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi;
-    f4_t *dst = reinterpret_cast<f4_t *>(a.pfx_o + pi * GD + d0);
+    f4_t *dst = reinterpret_cast<f4_t *>(a.pfx_o + pi * GDIM + d0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = o[k];
+    for (int k = 0; k < NV; ++k) dst[k] = o[k];
     if ((lane & 3) == 0) {
       a.pfx_m[pi] = mx * kLog2e;
       a.pfx_l[pi] = lsum;
     }
     return;
   }
-  uint32_t w[16];
+  uint32_t w[2 * NV];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < NV; ++k) {
     w[2 * k] = (uint32_t)to16<DT>(o[k][0] / lsum) | ((uint32_t)to16<DT>(o[k][1] / lsum) << 16);
     w[2 * k + 1] = (uint32_t)to16<DT>(o[k][2] / lsum) | ((uint32_t)to16<DT>(o[k][3] / lsum) << 16);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < NV / 2; ++k)
     reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
 }
 
-template <int DT, int B, bool NT, bool F8>
+template <int DT, int B, bool NT, bool F8, int GDIM>
 void go_group(const DecodeParams &a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, NT, F8>), dim3(a.G / kGroupWaves),
+  hipLaunchKernelGGL((decode_group_kernel<DT, B, kGroupWaves, NT, F8, GDIM>), dim3(a.G / kGroupWaves),
                      dim3(kGroupWaves * 64), group_lds_bytes(a.S), st, a);
 }
 
 template <int DT, int B>
 hipError_t launch_group(const DecodeParams &a, hipStream_t st) {
   if (a.fp8) {
-    if (a.stream_kv) go_group<DT, B, true, true>(a, st);
-    else go_group<DT, B, false, true>(a, st);
+    if (a.stream_kv) go_group<DT, B, true, true, 128>(a, st);
+    else go_group<DT, B, false, true, 128>(a, st);
+  } else if (a.D == 64) {
+    if (a.stream_kv) go_group<DT, B, true, false, 64>(a, st);
+    else go_group<DT, B, false, false, 64>(a, st);
   } else {
-    if (a.stream_kv) go_group<DT, B, true, false>(a, st);
-    else go_group<DT, B, false, false>(a, st);
+    if (a.stream_kv) go_group<DT, B, true, false, 128>(a, st);
+    else go_group<DT, B, false, false, 128>(a, st);
   }
   return hipGetLastError();
 }
 
-template <int DT, bool NT, bool F8>
+template <int DT, bool NT, bool F8, int GDIM>
 const void *group_ptr(int B) {
   switch (B) {
-    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves, NT, F8>);
-    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves, NT, F8>);
-    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves, NT, F8>);
-    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves, NT, F8>);
+    case 8: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 8, kGroupWaves, NT, F8, GDIM>);
+    case 16: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 16, kGroupWaves, NT, F8, GDIM>);
+    case 32: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 32, kGroupWaves, NT, F8, GDIM>);
+    case 64: return reinterpret_cast<const void *>(&decode_group_kernel<DT, 64, kGroupWaves, NT, F8, GDIM>);
     default: return nullptr;
   }
 }
@@ -599,13 +659,25 @@ size_t group_lds_bytes(int num_seqs) {
   return (size_t)(num_seqs + 1) * sizeof(int64_t) + (size_t)num_seqs * sizeof(int32_t);
 }
 
-const void *group_kernel(int dtype, int block_size, int nt, int fp8) {
+const void *group_kernel(int dtype, int head_dim, int block_size, int nt, int fp8) {
   if (fp8) {
-    if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, true>(block_size) : group_ptr<DT_BF16, true, true>(block_size);
-    return dtype == DT_F16 ? group_ptr<DT_F16, false, true>(block_size) : group_ptr<DT_BF16, false, true>(block_size);
+    if (head_dim != 128) return nullptr;
+    if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, true, 128>(block_size)
+                                   : group_ptr<DT_BF16, true, true, 128>(block_size);
+    return dtype == DT_F16 ? group_ptr<DT_F16, false, true, 128>(block_size)
+                           : group_ptr<DT_BF16, false, true, 128>(block_size);
   }
-  if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, false>(block_size) : group_ptr<DT_BF16, true, false>(block_size);
-  return dtype == DT_F16 ? group_ptr<DT_F16, false, false>(block_size) : group_ptr<DT_BF16, false, false>(block_size);
+  if (head_dim == 64) {
+    if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, false, 64>(block_size)
+                                   : group_ptr<DT_BF16, true, false, 64>(block_size);
+    return dtype == DT_F16 ? group_ptr<DT_F16, false, false, 64>(block_size)
+                           : group_ptr<DT_BF16, false, false, 64>(block_size);
+  }
+  if (head_dim != 128) return nullptr;
+  if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, false, 128>(block_size)
+                                 : group_ptr<DT_BF16, true, false, 128>(block_size);
+  return dtype == DT_F16 ? group_ptr<DT_F16, false, false, 128>(block_size)
+                         : group_ptr<DT_BF16, false, false, 128>(block_size);
 }
 
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream) {
@@ -632,6 +704,11 @@ hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream) {
       hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, 2 * GTC>), dim3(grid), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16, 2 * GTC>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (a.D == 64) {
+    if (a.dtype == DT_F16)
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, GTC, 64>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16, GTC, 64>), dim3(grid), dim3(256), 0, stream, a);
   } else if (a.dtype == DT_F16) {
     hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, GTC>), dim3(grid), dim3(256), 0, stream, a);
   } else {

@@ -119,7 +119,7 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8, bo
   int nb = 1 << 30;
   for (int nt = 0; nt < 2; ++nt) {
     for (int app = 0; app < 2; ++app) {
-      const void *k = group    ? pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0)
+      const void *k = group    ? pkv::group_kernel(p->dtype, p->head_dim, p->block_size, nt, fp8 ? 1 : 0)
                       : fp8    ? pkv::fp8_kernel(p->dtype, p->head_dim, p->block_size, nt, app)
                       : suffix ? pkv::suffix_kernel(p->dtype, p->block_size, nt)
                                : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
@@ -160,7 +160,8 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   if (fp8 && (partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)) return PKV_ERR_UNSUPPORTED;
   if (rows > 1) {
     // several query rows per KV head: the matrix-core kernel, balanced split only
-    if (rows > 16 || p->head_dim != 128 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
+    // (head_dim 64 or 128; e4m3 pools 128 only)
+    if (rows > 16 || (fp8 && p->head_dim != 128) || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
       return PKV_ERR_UNSUPPORTED;
     const int64_t row_chunks = (ctx + 15) / 16;
     const int64_t most = (int64_t)num_seqs * p->num_kv_heads * row_chunks;
@@ -561,7 +562,7 @@ pkv_status pkv_decode_launch_info(int32_t num_seqs, int32_t num_heads, int32_t m
   int64_t wgs = 0;
   if (lay.balanced) {
     if (lay.group) {
-      k = pkv::group_kernel(p->dtype, p->block_size, nt, fp8 ? 1 : 0);
+      k = pkv::group_kernel(p->dtype, p->head_dim, p->block_size, nt, fp8 ? 1 : 0);
       lds = pkv::group_lds_bytes(num_seqs);
     } else if (fp8) {
       k = pkv::fp8_kernel(p->dtype, p->head_dim, p->block_size, nt, append ? 1 : 0);

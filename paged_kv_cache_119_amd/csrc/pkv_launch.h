@@ -111,7 +111,7 @@ int64_t partition_grid(int64_t items);
 hipError_t launch_decode_partitions(const DecodeParams &a, hipStream_t stream);
 // Several query rows per KV head (grouped-query heads, multi-token queries).
 size_t group_lds_bytes(int num_seqs);
-const void *group_kernel(int dtype, int block_size, int nt, int fp8);
+const void *group_kernel(int dtype, int head_dim, int block_size, int nt, int fp8);
 hipError_t launch_group_decode(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams &a, hipStream_t stream);

@@ -1,5 +1,11 @@
 """Summarise rocprofv3 CSV output of bench.py into profiles/.
 
+    python -m paged_kv_cache_119_amd.rocprof_summary tables --title T --run LABEL trace|pmc DIR ... \\
+        --command "..." --out profiles/X.md [--occupancy KEY LABEL KERNEL]
+
+writes tables of kernel traces and counter passes (and, with --occupancy,
+the measured waves per SIMD bench.py reports beside HIP's figure);
+
     python -m paged_kv_cache_119_amd.rocprof_summary \\
         --trace DIR_WITH_kernel_stats.csv --fetch DIR_WITH_FETCH_counter_collection.csv \\
         --write DIR_WITH_WRITE_counter_collection.csv --config opt13b --partition-size 0 \\
@@ -36,6 +42,89 @@ def kernel_hash(root: str = ROOT) -> str:
     return h.hexdigest()[:16]
 
 
+def library_hash(root: str = ROOT) -> str:
+    """Hash of every library source (kernels and C ABI): an occupancy record is
+    valid only for them."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(root, "paged_kv_cache_119_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+OCCUPANCY_FILE = os.path.join(ROOT, "profiles", "occupancy_counters.json")
+
+
+def short_name(kernel: str) -> str:
+    """`decode_balanced_kernel<0, 128, 16, 4, true, true>` from the demangled name."""
+    k = kernel.replace("void ", "").replace("pkv::(anonymous namespace)::", "")
+    return k.split("(pkv::DecodeParams")[0]
+
+
+def tables_main(argv) -> int:
+    """Markdown tables from several rocprofv3 runs (kernel traces and counter
+    passes), optionally with the measured occupancy recorded for bench.py."""
+    ap = argparse.ArgumentParser(prog="rocprof_summary tables")
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--run", action="append", nargs=3, metavar=("LABEL", "KIND", "DIR"), required=True,
+                    help="KIND: trace (--kernel-trace --stats) or pmc (--pmc)")
+    ap.add_argument("--command", action="append", required=True)
+    ap.add_argument("--note", action="append", default=[])
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--occupancy", action="append", nargs=3, metavar=("KEY", "LABEL", "KERNEL"), default=[],
+                    help="record MeanOccupancyPerActiveCU of KERNEL in run LABEL under KEY for bench.py")
+    args = ap.parse_args(argv)
+    lines = [f"# rocprofv3 summary: {args.title}", "", "Commands (from the repository root, on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.command]
+    pmc = {}
+    for label, kind, d in args.run:
+        if kind == "trace":
+            lines += ["", f"## {label}: kernel trace", "", "| kernel | calls | mean us | min us | max us |",
+                      "|---|---|---|---|---|"]
+            for r in kernel_stats(d):
+                if "pkv" in r["name"]:
+                    lines.append(f"| `{short_name(r['name'])}` | {r['calls']} | {r['avg_us']:.2f} | "
+                                 f"{r['min_us']:.2f} | {r['max_us']:.2f} |")
+        else:
+            agg = counter_means(d)
+            pmc[label] = agg
+            counters = sorted({c for (_, c) in agg})
+            lines += ["", f"## {label}: counters (mean per dispatch)", "",
+                      "| kernel | dispatches | " + " | ".join(counters) + " |",
+                      "|---|---|" + "---|" * len(counters)]
+            for k in sorted({k for (k, _) in agg if "pkv" in k}):
+                vals = []
+                n = 0
+                for c in counters:
+                    v = agg.get((k, c), [])
+                    n = max(n, len(v))
+                    vals.append(f"{sum(v) / len(v):,.3f}" if v else "-")
+                lines.append(f"| `{short_name(k)}` | {n} | " + " | ".join(vals) + " |")
+    lines += [""] + [f"{n}" for n in args.note] + [""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    if args.occupancy:
+        rec = {}
+        if os.path.exists(OCCUPANCY_FILE):
+            with open(OCCUPANCY_FILE) as f:
+                rec = json.load(f)
+        for key, label, kernel in args.occupancy:
+            agg = pmc[label]
+            hits = [v for (k, c), v in agg.items() if c == "MeanOccupancyPerActiveCU" and kernel in k]
+            if not hits:
+                raise RuntimeError(f"no MeanOccupancyPerActiveCU for {kernel} in {label}")
+            waves_cu = sum(hits[0]) / len(hits[0])
+            rec[key] = {"kernel": kernel, "waves_per_active_cu": round(waves_cu, 3),
+                        "waves_per_simd": round(waves_cu / 4, 3), "library_hash": library_hash(),
+                        "counter": "MeanOccupancyPerActiveCU (SQ_LEVEL_WAVES / SQ_BUSY_CU_CYCLES)",
+                        "summary": os.path.relpath(args.out, ROOT)}
+        with open(OCCUPANCY_FILE, "w") as f:
+            json.dump(rec, f, indent=2)
+    print(args.out)
+    return 0
+
+
 def _one(pattern: str) -> str:
     hits = sorted(glob.glob(pattern, recursive=True))
     if not hits:
@@ -69,6 +158,10 @@ def copy_scale(agg: dict, counter: str) -> float:
 
 
 def main(argv=None) -> int:
+    import sys
+    argv = sys.argv[1:] if argv is None else argv
+    if argv and argv[0] == "tables":
+        return tables_main(argv[1:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)

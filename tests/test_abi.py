@@ -119,7 +119,10 @@ def test_validation_returns_status_before_any_launch(lib):
     assert st == 3                                                  # grouped rows: balanced split only
     st = lib.pkv_paged_attention_decode(p16, p16, p16, p16, p16, p16, 1.0, 4, 8, 8, ctypes.byref(_desc(D=64)),
                                         0, nul, 0, nul)
-    assert st == 3                                                  # grouped rows: head_dim 128 only
+    assert st == 4                                                  # grouped rows at head_dim 64: accepted
+    st = lib.pkv_paged_attention_decode(p16, p16, p16, p16, p16, p16, 1.0, 4, 4 * 17, 8,
+                                        ctypes.byref(_desc(D=64)), 0, nul, 0, nul)
+    assert st == 3                                                  # more than 16 query heads per KV head
     bad = _desc(B=12)
     st = lib.pkv_paged_attention_decode(nul, nul, nul, nul, nul, nul, 1.0, 4, 4, 8, ctypes.byref(bad), 0,
                                         nul, 0, nul)
