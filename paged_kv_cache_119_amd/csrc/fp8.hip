@@ -36,7 +36,6 @@ namespace pkv {
 namespace {
 
 constexpr int kFp8Waves = PKV_DECODE_WAVES;
-constexpr int FD = 128;  // head_dim of the grouped-row append below
 
 // Decode geometry for head_dim D: a lane loads BPL codes of a token row (16
 // at D = 128, 8 at D = 64), LPT = 8 lanes hold a row, a load instruction
@@ -106,7 +105,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 // nothing.
 template <int DT>
 __global__ __launch_bounds__(256) void append_last_fp8_kernel(DecodeParams a, float k_inv, float v_inv) {
-  const int per_row = FD / 16;
+  const int per_row = a.D / 16;
   const int64_t per_seq = (int64_t)a.Hkv * per_row;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)a.S * per_seq) return;
@@ -118,8 +117,8 @@ __global__ __launch_bounds__(256) void append_last_fp8_kernel(DecodeParams a, fl
   if (L <= 0 || L > a.maxb * a.B) return;
   const int blk = a.tables[(int64_t)s * a.maxb + (L - 1) / a.B];
   if (blk < 0 || (int64_t)blk >= a.num_blocks) return;
-  const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * FD + piece * 16;
-  const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * FD + piece * 16;
+  const int64_t dst = (((int64_t)blk * a.Hkv + h) * a.B + (L - 1) % a.B) * a.D + piece * 16;
+  const int64_t src = (int64_t)s * a.new_stride + (int64_t)h * a.D + piece * 16;
   quantise_piece<DT>(reinterpret_cast<uint8_t *>(const_cast<void *>(a.k_pool)),
                      reinterpret_cast<uint8_t *>(const_cast<void *>(a.v_pool)),
                      reinterpret_cast<const uint16_t *>(a.k_new) + src,
@@ -497,7 +496,7 @@ hipError_t launch_fp8_decode(const DecodeParams &a, hipStream_t stream) {
 }
 
 hipError_t launch_append_last_fp8(const DecodeParams &a, float k_inv, float v_inv, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.S * a.Hkv * (FD / 16);
+  const int64_t threads = (int64_t)a.S * a.Hkv * (a.D / 16);
   if (threads == 0) return hipSuccess;
   const int64_t grid = (threads + 255) / 256;
   if (a.dtype == DT_F16)

@@ -54,7 +54,6 @@ namespace pkv {
 namespace {
 
 constexpr int kGroupWaves = PKV_DECODE_WAVES;
-constexpr int GD = 128;  // head_dim of the e4m3 path (the 16-bit path takes 64 or 128)
 constexpr int GTC = 16;  // tokens per MFMA tile (and per chunk of 16-bit pools)
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -130,7 +129,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // dims 8(r % 8) .. +8, supplies element 2s + r / 8 of them.
 template <int DT, int B, bool NT, bool F8, int GDIM = 128>
 struct GroupStream {
-  static_assert(GDIM == 128 || (GDIM == 64 && !F8), "head_dim 128, or 64 with 16-bit pools");
+  static_assert(GDIM == 128 || GDIM == 64, "head_dim 64 or 128");
+  static constexpr int KPT = GDIM / 64;  // e4m3: 16-byte K loads per lane per 16-token tile
   static constexpr int NKS = GDIM / 32;  // k-slices of S^T (and whole-row K loads per 16-token tile)
   static constexpr int NS = GDIM / 16;   // 16-dim slices of O^T
   // tokens per chunk: e4m3 chunks hold two 16-token tiles, so that a stage
@@ -144,9 +144,9 @@ struct GroupStream {
     bool bad;
   };
   struct Buf8 {
-    u32x4 k[4];  // 32 codes of token r of each tile (k[2u], k[2u + 1]: tile u)
-    u32x2 v[8];  // 8 codes of each of tokens 4g .. 4g+3 of each tile (v[4u + t])
-    u32x4 q[4];
+    u32x4 k[2 * KPT];  // 16 KPT codes of token r of each tile (k[KPT u] ..: tile u)
+    u32x2 v[8];        // 8 codes of each of tokens 4g .. 4g+3 of each tile (v[4u + t])
+    u32x4 q[NKS];
     bool bad;
   };
   using Buf = typename std::conditional<F8, Buf8, Buf16>::type;
@@ -256,19 +256,23 @@ struct GroupStream {
     const int qi = rr / gq, gi = rr - (rr / gq) * gq;
     const int64_t qrow = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GDIM;
     if constexpr (F8) {
+      // K: lane (r, g) takes codes 16 KPT g .. +16 KPT of token r (dims of
+      // k-slices j: 16 KPT g + 8j .. +8, and the query fragment the same);
+      // V: 8 codes of tokens 4g + t at dims 8(r % (GDIM / 8))
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        const int64_t kb = token_base(d, e, min(GTC * u + r, last), bd) + 32 * g;
-        b.k[2 * u] = ld_kv<NT>(kp + kb);
-        b.k[2 * u + 1] = ld_kv<NT>(kp + kb + 16);
+        const int64_t kb = token_base(d, e, min(GTC * u + r, last), bd) + 16 * KPT * g;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) b.k[KPT * u + i] = ld_kv<NT>(kp + kb + 16 * i);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int64_t vb = token_base(d, e, min(GTC * u + 4 * g + t, last), bd) + 8 * r;
+          const int64_t vb = token_base(d, e, min(GTC * u + 4 * g + t, last), bd) + 8 * (r % (GDIM / 8));
           b.v[4 * u + t] = ld_kv8<NT>(vp + vb);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 32 * g + 8 * j);
+      for (int j = 0; j < NKS; ++j)
+        b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 16 * KPT * g + 8 * j);
     } else {
       // whole token rows (GDIM / 8 lanes a row): lane l of load j gets token
       // j * RPL + l / (GDIM / 8), dims 8(l % (GDIM / 8)) .. +8; consume
@@ -369,8 +373,8 @@ struct GroupStream {
       u32x4 kk[NKS], vv[4];  // K and V fragments of tile u in the 16-bit type
       if constexpr (F8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          kk[j] = widen8<DT>(b.k[2 * u + (j >> 1)][2 * (j & 1)], b.k[2 * u + (j >> 1)][2 * (j & 1) + 1]);
+        for (int j = 0; j < NKS; ++j)
+          kk[j] = widen8<DT>(b.k[KPT * u + (j >> 1)][2 * (j & 1)], b.k[KPT * u + (j >> 1)][2 * (j & 1) + 1]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) vv[t] = widen8<DT_F16>(b.v[4 * u + t][0], b.v[4 * u + t][1]);
       } else {
@@ -629,7 +633,10 @@ void go_group(const DecodeParams &a, hipStream_t st) {
 
 template <int DT, int B>
 hipError_t launch_group(const DecodeParams &a, hipStream_t st) {
-  if (a.fp8) {
+  if (a.fp8 && a.D == 64) {
+    if (a.stream_kv) go_group<DT, B, true, true, 64>(a, st);
+    else go_group<DT, B, false, true, 64>(a, st);
+  } else if (a.fp8) {
     if (a.stream_kv) go_group<DT, B, true, true, 128>(a, st);
     else go_group<DT, B, false, true, 128>(a, st);
   } else if (a.D == 64) {
@@ -660,6 +667,12 @@ size_t group_lds_bytes(int num_seqs) {
 }
 
 const void *group_kernel(int dtype, int head_dim, int block_size, int nt, int fp8) {
+  if (fp8 && head_dim == 64) {
+    if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, true, 64>(block_size)
+                                   : group_ptr<DT_BF16, true, true, 64>(block_size);
+    return dtype == DT_F16 ? group_ptr<DT_F16, false, true, 64>(block_size)
+                           : group_ptr<DT_BF16, false, true, 64>(block_size);
+  }
   if (fp8) {
     if (head_dim != 128) return nullptr;
     if (nt) return dtype == DT_F16 ? group_ptr<DT_F16, true, true, 128>(block_size)
@@ -699,7 +712,12 @@ hipError_t launch_group_merge(const DecodeParams &a, hipStream_t stream) {
   if (a.S == 0) return hipSuccess;
   const int64_t groups = (int64_t)a.S * a.Hkv;  // one wavefront per (sequence, KV head)
   const int grid = (int)((groups + 3) / 4);
-  if (a.fp8) {
+  if (a.fp8 && a.D == 64) {
+    if (a.dtype == DT_F16)
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, 2 * GTC, 64>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_group_merge_kernel<DT_BF16, 2 * GTC, 64>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (a.fp8) {
     if (a.dtype == DT_F16)
       hipLaunchKernelGGL((decode_group_merge_kernel<DT_F16, 2 * GTC>), dim3(grid), dim3(256), 0, stream, a);
     else

@@ -160,9 +160,7 @@ pkv_status decode_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   if (fp8 && (partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)) return PKV_ERR_UNSUPPORTED;
   if (rows > 1) {
     // several query rows per KV head: the matrix-core kernel, balanced split only
-    // (head_dim 64 or 128; e4m3 pools 128 only)
-    if (rows > 16 || (fp8 && p->head_dim != 128) || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs)
-      return PKV_ERR_UNSUPPORTED;
+    if (rows > 16 || partition_size != 0 || num_seqs > pkv::kBalancedMaxSeqs) return PKV_ERR_UNSUPPORTED;
     const int64_t row_chunks = (ctx + 15) / 16;
     const int64_t most = (int64_t)num_seqs * p->num_kv_heads * row_chunks;
     if ((double)most >= 1.0e12) return PKV_ERR_SHAPE;

@@ -191,12 +191,12 @@ def test_fp8_sizes_and_validation(lib):
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 0.0, 1.0, 4, 4, 8, ctypes.byref(d), nul, 0, nul) == 2
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 6, 8, ctypes.byref(d), nul, 0, nul) == 3
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4 * 17, 8, ctypes.byref(d), nul, 0, nul) == 3
-    # head_dim 64 is accepted (the call then stops at the missing workspace);
-    # with grouped heads (the matrix-core path) it is not
+    # head_dim 64 is accepted, with one query head per KV head and with
+    # grouped heads (the call then stops at the missing workspace)
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4, 8, ctypes.byref(_desc(D=64)), nul, 0,
              nul) == 4
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 8, 8, ctypes.byref(_desc(D=64)), nul, 0,
-             nul) == 3
+             nul) == 4
     assert g(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 4, 8, ctypes.byref(d), nul, 0, nul) == 4
     # workspace: partials of at most ceil(S * H * ceil(ctx / 32) / 8) workers plus one per row
     w = lib.pkv_fp8_decode_workspace_bytes

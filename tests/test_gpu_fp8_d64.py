@@ -1,7 +1,8 @@
 """GPU: the FP8 (e4m3) KV cache at head_dim 64 -- decode over e4m3 pools and
-the decode step with the quantising append -- against the float64 oracle
-(decode_rows_fp8, reshape_and_cache_fp8).  At head_dim 64 a lane holds 8
-codes of a row, 8 lanes a row, and a chunk is 64 tokens."""
+the decode step with the quantising append, one query row per KV head (the
+stream kernel: a lane holds 8 codes of a row, 8 lanes a row, a chunk is 64
+tokens) and several (the matrix-core kernel) -- against the float64 oracle
+(decode_rows_fp8, reshape_and_cache_fp8)."""
 
 import numpy as np
 import pytest
@@ -132,12 +133,58 @@ def test_fp8_d64_rows_cut_into_more_than_64_pieces():
     assert_close(to_bits(out), _oracle(c, q, D ** -0.5, 0.5, 1.5, "bf16"), "bf16", "fp8 D=64 long rows")
 
 
-def test_fp8_d64_grouped_heads_rejected():
-    """The matrix-core path (several query rows per KV head) is head_dim 128
-    only."""
-    c = _case([20, 30], 2, 16, seed=550)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B", [8, 16, 32, 64])
+@pytest.mark.parametrize("G,Q", [(8, 1), (1, 4), (3, 2)])
+def test_fp8_d64_rows_every_output(dtype, B, G, Q):
+    """Several query rows per KV head over e4m3 pools at head_dim 64 (the
+    matrix-core kernel): grouped heads and several query tokens."""
+    Hkv = 2
+    lengths = [max(L, Q) for L in LENGTHS]
+    c = _case(lengths, Hkv, B, seed=560 + B + G + 10 * Q)
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 561 + B)
+    ks, vs = 0.004, 0.006
     tab = torch.from_numpy(c["tables"]).to(DEV)
     lens = torch.from_numpy(c["lens"]).to(DEV)
-    q = normal_16bit((2, 8, D), "f16", DEV, 551)
-    with pytest.raises(pkv.PagedKVError):
-        pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, 0.1, 1.0, 1.0)
+    if Q == 1:
+        out = pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, D ** -0.5, ks, vs)
+    else:
+        out = pkv.paged_attention_multi_fp8(q, c["kp"], c["vp"], tab, lens, D ** -0.5, ks, vs)
+    torch.cuda.synchronize()
+    qb = to_bits(q)
+    qb = qb[:, None] if Q == 1 else qb
+    ref = po.decode_rows_fp8(qb, _codes(c["kp"]), _codes(c["vp"]), c["tables"], c["lens"], D ** -0.5, B, dtype,
+                             ks, vs)
+    ref = ref[:, 0] if Q == 1 else ref
+    assert_close(to_bits(out), ref, dtype, f"fp8 D=64 rows G={G} Q={Q} {dtype} B={B}")
+
+
+def test_fp8_d64_grouped_decode_step():
+    """The decode step with the quantising append and grouped heads at head
+    _dim 64 (the append is its own launch): codes and output as the oracle's."""
+    lengths = [1, 63, 64, 65, 300, 0]
+    H, Hkv, B, dtype = 8, 2, 16, "bf16"
+    c = _case([max(L, 1) for L in lengths], Hkv, B, seed=580)
+    c["lens"] = np.asarray(lengths, np.int32)
+    S = len(lengths)
+    kn = normal_16bit((S, Hkv, D), dtype, DEV, 581)
+    vn = normal_16bit((S, Hkv, D), dtype, DEV, 582)
+    q = normal_16bit((S, H, D), dtype, DEV, 583)
+    ks, vs = 0.02, 0.03
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    kw, vw = _codes(c["kp"]).copy(), _codes(c["vp"]).copy()
+    out = pkv.paged_attention_decode_append_fp8(q, kn, vn, c["kp"], c["vp"], tab, lens, D ** -0.5, ks, vs)
+    torch.cuda.synchronize()
+    slots = np.array([int(c["tables"][s, (L - 1) // B]) * B + (L - 1) % B if L > 0 else -1
+                      for s, L in enumerate(lengths)], np.int64)
+    po.reshape_and_cache_fp8(to_bits(kn), to_bits(vn), kw, vw, slots, B, dtype, ks, vs)
+    assert np.array_equal(_codes(c["kp"]), kw) and np.array_equal(_codes(c["vp"]), vw)
+    o = po.bits_to_f64(to_bits(out), dtype)
+    assert np.all(o[5] == 0)
+    good = list(range(5))
+    sub = dict(c, tables=c["tables"][good], lens=c["lens"][good])
+    ref = po.decode_rows_fp8(to_bits(q)[good][:, None], kw, vw, sub["tables"], sub["lens"], D ** -0.5, B, dtype,
+                             ks, vs)[:, 0]
+    assert_close(to_bits(out)[good], ref, dtype, "fp8 D=64 grouped decode step")
