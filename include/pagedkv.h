@@ -329,7 +329,7 @@ pkv_status pkv_paged_attention_decode(void *out, const void *q, const void *k_po
  *                 aligned; needs no initialisation.
  * Other arguments, layouts and device-side rules as in
  * pkv_paged_attention_decode; a sequence shorter than its group's prefix
- * gets a NaN row.  Restrictions (else PKV_ERR_UNSUPPORTED): head_dim 128,
+ * gets a NaN row.  Restrictions (else PKV_ERR_UNSUPPORTED): 16-bit pools,
  * num_heads == num_kv_heads, num_seqs <= 4096.  The result depends only on
  * the prefix contents: shared blocks and per-sequence copies give the same
  * bits.  Differs from pkv_paged_attention_decode only by rounding.

@@ -963,26 +963,10 @@ R dispatch(int dtype, int D, int B, R fail, Args... args) {
   return fail;
 }
 
-// F<DT, 128, B>::call(args...) for the runtime (dtype, B): head_dim 128 only.
-template <template <int, int, int> class F, typename R, typename... Args>
-R dispatch128(int dtype, int B, R fail, Args... args) {
-#define PKV_B(DT)                                  \
-  switch (B) {                                     \
-    case 8: return F<DT, 128, 8>::call(args...);   \
-    case 16: return F<DT, 128, 16>::call(args...); \
-    case 32: return F<DT, 128, 32>::call(args...); \
-    case 64: return F<DT, 128, 64>::call(args...); \
-    default: return fail;                          \
-  }
-  if (dtype == DT_F16) { PKV_B(DT_F16) }
-  PKV_B(DT_BF16)
-#undef PKV_B
-}
-
 }  // namespace
 
-const void *suffix_kernel(int dtype, int block_size, int nt) {
-  return dispatch128<SuffixPtrF, const void *>(dtype, block_size, nullptr, nt);
+const void *suffix_kernel(int dtype, int head_dim, int block_size, int nt) {
+  return dispatch<SuffixPtrF, const void *>(dtype, head_dim, block_size, nullptr, nt);
 }
 
 size_t suffix_lds_bytes(int num_seqs) {
@@ -991,8 +975,7 @@ size_t suffix_lds_bytes(int num_seqs) {
 
 hipError_t launch_suffix(const DecodeParams &a, hipStream_t stream) {
   if (a.S == 0 || a.G == 0) return hipSuccess;
-  if (a.D != 128) return hipErrorInvalidValue;
-  return dispatch128<SuffixF, hipError_t>(a.dtype, a.B, hipErrorInvalidValue, a, stream);
+  return dispatch<SuffixF, hipError_t>(a.dtype, a.D, a.B, hipErrorInvalidValue, a, stream);
 }
 
 int decode_waves() { return kNumWaves; }

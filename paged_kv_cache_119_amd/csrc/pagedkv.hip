@@ -121,7 +121,7 @@ int balanced_waves(const pkv_pool *p, int32_t num_seqs, bool group, bool fp8, bo
     for (int app = 0; app < 2; ++app) {
       const void *k = group    ? pkv::group_kernel(p->dtype, p->head_dim, p->block_size, nt, fp8 ? 1 : 0)
                       : fp8    ? pkv::fp8_kernel(p->dtype, p->head_dim, p->block_size, nt, app)
-                      : suffix ? pkv::suffix_kernel(p->dtype, p->block_size, nt)
+                      : suffix ? pkv::suffix_kernel(p->dtype, p->head_dim, p->block_size, nt)
                                : pkv::balanced_kernel(p->dtype, p->head_dim, p->block_size, app, nt);
       if (!k) return 0;
       const int b = kernel_blocks_per_cu(dev, k, lds);
@@ -399,8 +399,7 @@ pkv_status shared_layout(int32_t num_seqs, int32_t num_heads, int32_t max_blocks
   if (!p) return PKV_ERR_NULL;
   if (!pool_ok(p)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || max_blocks < 1 || group_size < 1) return PKV_ERR_SHAPE;
-  if (num_heads != p->num_kv_heads || p->head_dim != 128 || group_size < 2 || group_size > 16 ||
-      num_seqs > pkv::kBalancedMaxSeqs)
+  if (num_heads != p->num_kv_heads || group_size < 2 || group_size > 16 || num_seqs > pkv::kBalancedMaxSeqs)
     return PKV_ERR_UNSUPPORTED;
   if (num_seqs % group_size != 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks * p->block_size > (1 << 30)) return PKV_ERR_SHAPE;

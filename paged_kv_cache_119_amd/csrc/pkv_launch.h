@@ -91,9 +91,9 @@ struct DecodeParams {
 };
 
 int decode_waves();
-// The suffix pass of the shared-prefix decode (16-bit, head_dim 128): its
-// kernel instance, dynamic LDS, split and merge launches.
-const void *suffix_kernel(int dtype, int block_size, int nt);
+// The suffix pass of the shared-prefix decode (16-bit pools): its kernel
+// instance, dynamic LDS and launch (the merge is launch_decode_merge).
+const void *suffix_kernel(int dtype, int head_dim, int block_size, int nt);
 size_t suffix_lds_bytes(int num_seqs);
 hipError_t launch_suffix(const DecodeParams &a, hipStream_t stream);
 // Tokens one wavefront step covers (partition sizes are multiples of it).
