@@ -287,7 +287,8 @@ def main(argv=None) -> int:
         "read_ceiling": ceiling,
         "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, P, 1, False,
                                                           not args.separate_append),
-                                   f"{args.config}/decode" + ("/separate" if args.separate_append else "")
+                                   f"{args.config}/B{B}/decode" + (f"/P{P}" if P else "")
+                                   + ("/separate" if args.separate_append else "")
                                    + ("/one-call" if args.one_call else "")),
     }
     print(json.dumps(line), flush=True)
@@ -508,7 +509,7 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
         "cpu_baseline": None,
         "read_ceiling": ceiling,
         "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, Q, args.kv == "fp8"),
-                                   f"{args.config}/rows/G{G}/Q{Q}" + ("/fp8" if fp8 else "")),
+                                   f"{args.config}/B{B}/rows/G{G}/Q{Q}" + ("/fp8" if fp8 else "")),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -639,7 +640,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
         "read_ceiling": ceiling,
         "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, 1, True,
                                                           not args.separate_append),
-                                   f"{args.config}/fp8" + ("/separate" if args.separate_append else "")),
+                                   f"{args.config}/B{B}/fp8" + ("/separate" if args.separate_append else "")),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -714,6 +715,8 @@ def bench_shared(args, t, pkv, lib, dev) -> int:
     call_mean = float(np.mean(call_ms))
     achieved = by["total"] / (call_mean * 1e-3) / 1e9
     assert torch.isfinite(reps[0][3].float()).all().item(), "non-finite output"
+    kp, vp, q, out = reps[0]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(t, (kp, vp, q, None, None, out), args.cpu_budget_s)
     line = {
         "metric": METRIC,
         "value": round(by["logical"] / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
@@ -733,7 +736,9 @@ def bench_shared(args, t, pkv, lib, dev) -> int:
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": by["total"],
                      "mean_launch_us": round(call_mean * 1e3, 2)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
+        "occupancy": {"prefix_pass": measured_occupancy(f"{args.config}/B{B}/shared-prefix/prefix-pass"),
+                      "suffix_pass": measured_occupancy(f"{args.config}/B{B}/shared-prefix/suffix-pass")},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -62,6 +62,35 @@ def short_name(kernel: str) -> str:
     return k.split("(pkv::DecodeParams")[0]
 
 
+def occupancy_lines(agg: dict) -> list:
+    """Markdown rows of MeanOccupancyPerActiveCU per library kernel."""
+    out = ["| kernel | dispatches | waves per SIMD |", "|---|---|---|"]
+    for (k, c), v in sorted(agg.items()):
+        if c == "MeanOccupancyPerActiveCU" and "pkv" in k:
+            out.append(f"| `{short_name(k)}` | {len(v)} | {sum(v) / len(v):.3f} |")
+    return out
+
+
+def record_occupancy(agg: dict, key: str, kernel: str, summary: str) -> None:
+    """Store the measured occupancy of `kernel` under `key` for bench.py."""
+    hits = [v for (k, c), v in agg.items() if c == "MeanOccupancyPerActiveCU" and kernel in k]
+    if not hits:
+        raise RuntimeError(f"no MeanOccupancyPerActiveCU for {kernel}")
+    rec = {}
+    if os.path.exists(OCCUPANCY_FILE):
+        with open(OCCUPANCY_FILE) as f:
+            rec = json.load(f)
+    # The derived counter is SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES, both counted
+    # per SIMD: on gfx950 it reads in waves per SIMD (a plain streaming read
+    # of 131072 waves reads about 7.1 of the 8 slots).
+    rec[key] = {"kernel": kernel, "waves_per_simd": round(sum(hits[0]) / len(hits[0]), 3),
+                "library_hash": library_hash(),
+                "counter": "MeanOccupancyPerActiveCU (SQ_WAVE_CYCLES / SQ_BUSY_CU_CYCLES)",
+                "summary": os.path.relpath(summary, ROOT)}
+    with open(OCCUPANCY_FILE, "w") as f:
+        json.dump(dict(sorted(rec.items())), f, indent=2)
+
+
 def tables_main(argv) -> int:
     """Markdown tables from several rocprofv3 runs (kernel traces and counter
     passes), optionally with the measured occupancy recorded for bench.py."""
@@ -73,7 +102,7 @@ def tables_main(argv) -> int:
     ap.add_argument("--note", action="append", default=[])
     ap.add_argument("--out", required=True)
     ap.add_argument("--occupancy", action="append", nargs=3, metavar=("KEY", "LABEL", "KERNEL"), default=[],
-                    help="record MeanOccupancyPerActiveCU of KERNEL in run LABEL under KEY for bench.py")
+                    help="record MeanOccupancyPerActiveCU (waves per SIMD) of KERNEL in run LABEL under KEY for bench.py")
     args = ap.parse_args(argv)
     lines = [f"# rocprofv3 summary: {args.title}", "", "Commands (from the repository root, on one MI355X):", ""]
     lines += [f"    {c}" for c in args.command]
@@ -104,23 +133,8 @@ def tables_main(argv) -> int:
     lines += [""] + [f"{n}" for n in args.note] + [""]
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
-    if args.occupancy:
-        rec = {}
-        if os.path.exists(OCCUPANCY_FILE):
-            with open(OCCUPANCY_FILE) as f:
-                rec = json.load(f)
-        for key, label, kernel in args.occupancy:
-            agg = pmc[label]
-            hits = [v for (k, c), v in agg.items() if c == "MeanOccupancyPerActiveCU" and kernel in k]
-            if not hits:
-                raise RuntimeError(f"no MeanOccupancyPerActiveCU for {kernel} in {label}")
-            waves_cu = sum(hits[0]) / len(hits[0])
-            rec[key] = {"kernel": kernel, "waves_per_active_cu": round(waves_cu, 3),
-                        "waves_per_simd": round(waves_cu / 4, 3), "library_hash": library_hash(),
-                        "counter": "MeanOccupancyPerActiveCU (SQ_LEVEL_WAVES / SQ_BUSY_CU_CYCLES)",
-                        "summary": os.path.relpath(args.out, ROOT)}
-        with open(OCCUPANCY_FILE, "w") as f:
-            json.dump(rec, f, indent=2)
+    for key, label, kernel in args.occupancy:
+        record_occupancy(pmc[label], key, kernel, args.out)
     print(args.out)
     return 0
 
@@ -176,6 +190,9 @@ def main(argv=None) -> int:
     ap.add_argument("--out", required=True)
     ap.add_argument("--fetch-scale", type=float, default=None,
                     help="FETCH_SIZE scale measured in another run (when this run has no calibration copy)")
+    ap.add_argument("--occ", default=None, help="MeanOccupancyPerActiveCU run of the same command")
+    ap.add_argument("--occ-key", default=None, help="record the kernel's occupancy under this key for bench.py")
+    ap.add_argument("--note", action="append", default=[])
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic_decode_partition_opt13b.json"),
                     help="record for bench.py's traffic field ('none': write no record)")
     args = ap.parse_args(argv)
@@ -228,9 +245,16 @@ def main(argv=None) -> int:
         what = "measured fetch"
     lines += ["", f"Algorithmic bytes of one `{args.kernel}` launch: {args.algorithmic_bytes / 1e6:.2f} MB; "
               f"{what} {traffic / 1e6:.2f} MB ({traffic / args.algorithmic_bytes:.3f}x).", ""]
+    occ = counter_means(args.occ) if args.occ else None
+    if occ is not None:
+        lines += ["## Occupancy (rocprofv3 --pmc MeanOccupancyPerActiveCU, mean per dispatch)", ""]
+        lines += occupancy_lines(occ) + [""]
+    lines += [f"{n}" for n in args.note] + ([""] if args.note else [])
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as f:
         f.write("\n".join(lines))
+    if occ is not None and args.occ_key:
+        record_occupancy(occ, args.occ_key, args.kernel, args.out)
     if args.traffic_json == "none":
         print(args.out, f"traffic {traffic / 1e6:.2f} MB")
         return 0
