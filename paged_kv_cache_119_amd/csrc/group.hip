@@ -223,23 +223,49 @@ struct GroupStream {
     return (uint32_t)tables[(int64_t)d.s * tstride + lb];
   }
 
-  // Base element offset of token t of chunk d (its block from the entries).
-  __device__ __forceinline__ int64_t token_base(const Chunk &d, uint32_t e, int t, bool &bd) const {
-    int blk, off;
+  // The chunk's blocks (NE <= 4 wave-uniform block numbers, from its table
+  // entries); an entry outside the pool marks the chunk bad and reads block 0
+  // instead.  Named values rather than an array, and 32-bit: the per-token
+  // selection below then stays in registers.
+  struct Blocks {
+    int b0, b1, b2, b3;
+  };
+
+  __device__ __forceinline__ int block_of(uint32_t e, int i, bool &bd) const {
+    const int blk = __builtin_amdgcn_readlane((int)e, i);
+    const bool out = blk < 0 || (int64_t)blk >= num_blocks;
+    bd = bd || out;
+    return out ? 0 : blk;
+  }
+
+  __device__ __forceinline__ Blocks chunk_blocks(uint32_t e, bool &bd) const {
+    static_assert(NE == 1 || NE == 2 || NE == 4, "1, 2 or 4 blocks per chunk");
+    Blocks bk;
+    bk.b0 = block_of(e, 0, bd);
+    bk.b1 = bk.b2 = bk.b3 = bk.b0;
+    if constexpr (NE > 1) bk.b1 = block_of(e, 1, bd);
+    if constexpr (NE > 2) {
+      bk.b2 = block_of(e, 2, bd);
+      bk.b3 = block_of(e, 3, bd);
+    }
+    return bk;
+  }
+
+  // Element offset of token t (0 <= t < TC) of chunk d.
+  __device__ __forceinline__ int64_t token_off(const Chunk &d, Blocks bk, int t) const {
+    const int64_t hoff = (int64_t)d.h * B * GDIM;
     if constexpr (TC >= B) {
-      blk = __builtin_amdgcn_readlane((int)e, 0);
-#pragma unroll
-      for (int i = 1; i < NE; ++i) blk = (t / B == i) ? __builtin_amdgcn_readlane((int)e, i) : blk;
-      off = t % B;
+      const int i = t / B;
+      int blk = bk.b0;
+      if constexpr (NE > 1) blk = i == 1 ? bk.b1 : blk;
+      if constexpr (NE > 2) {
+        blk = i == 2 ? bk.b2 : blk;
+        blk = i == 3 ? bk.b3 : blk;
+      }
+      return (int64_t)blk * blk_stride + hoff + (int64_t)(t & (B - 1)) * GDIM;
     } else {
-      blk = __builtin_amdgcn_readlane((int)e, 0);
-      off = (d.c % (B / TC)) * TC + t;
+      return (int64_t)bk.b0 * blk_stride + hoff + (int64_t)((d.c % (B / TC)) * TC + t) * GDIM;
     }
-    if (blk < 0 || (int64_t)blk >= num_blocks) {
-      bd = true;
-      blk = 0;
-    }
-    return (int64_t)blk * blk_stride + (int64_t)d.h * B * GDIM + (int64_t)off * GDIM;
   }
 
   // Stage 2: K rows (16-bit: whole rows of tokens 4j + g; e4m3: token r), V
@@ -250,8 +276,10 @@ struct GroupStream {
   // traffic); they are masked.
   __device__ __forceinline__ void load_kv(const Chunk &d, uint32_t e, Buf &b) const {
     bool bd = false;
+    const Blocks bb = chunk_blocks(e, bd);
     const int last = d.L - 1 - d.c * TC;  // token L - 1 relative to the chunk
-    // query row r of this KV head (rows >= M read row 0 and are zeroed)
+    // query row r of this KV head (rows >= M read row 0; their results are
+    // never written)
     const int rr = r < M ? r : 0;
     const int qi = rr / gq, gi = rr - (rr / gq) * gq;
     const int64_t qrow = (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GDIM;
@@ -261,14 +289,15 @@ struct GroupStream {
       // V: 8 codes of tokens 4g + t at dims 8(r % (GDIM / 8))
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        const int64_t kb = token_base(d, e, min(GTC * u + r, last), bd) + 16 * KPT * g;
+        const int64_t kb = token_off(d, bb, min(GTC * u + r, last)) + 16 * KPT * g;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) b.k[KPT * u + i] = ld_kv<NT>(kp + kb + 16 * i);
+        // four consecutive tokens from a multiple of 4 lie in one block
+        const int t0 = min(GTC * u + 4 * g, last);
+        const int64_t vb = token_off(d, bb, t0) + 8 * (r % (GDIM / 8));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t vb = token_base(d, e, min(GTC * u + 4 * g + t, last), bd) + 8 * (r % (GDIM / 8));
-          b.v[4 * u + t] = ld_kv8<NT>(vp + vb);
-        }
+        for (int t = 0; t < 4; ++t)
+          b.v[4 * u + t] = ld_kv8<NT>(vp + vb + (int64_t)(min(GTC * u + 4 * g + t, last) - t0) * GDIM);
       }
 #pragma unroll
       for (int j = 0; j < NKS; ++j)
@@ -281,51 +310,77 @@ struct GroupStream {
       constexpr int RPL = 64 / LPR;  // rows per load
 #pragma unroll
       for (int j = 0; j < NKS; ++j) {
-        const int64_t kb = token_base(d, e, min(RPL * j + lane / LPR, last), bd) + 8 * (lane % LPR);
+        const int64_t kb = token_off(d, bb, min(RPL * j + lane / LPR, last)) + 8 * (lane % LPR);
         b.k[j] = ld_kv<NT>(kp + 2 * kb);
       }
+      const int t0 = min(4 * g, last);
+      const int64_t vb = token_off(d, bb, t0) + 8 * (r % LPR);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t vb = token_base(d, e, min(4 * g + t, last), bd) + 8 * (r % LPR);
-        b.v[t] = ld_kv<NT>(vp + 2 * vb);
-      }
+      for (int t = 0; t < 4; ++t) b.v[t] = ld_kv<NT>(vp + 2 * (vb + (int64_t)(min(4 * g + t, last) - t0) * GDIM));
 #pragma unroll
       for (int j = 0; j < NKS; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
     }
-    b.bad = __builtin_amdgcn_readfirstlane(__ballot(bd) != 0 ? 1 : 0) != 0;
+    b.bad = bd;
   }
 
   // One 16-token tile starting at token t0: scores, online softmax and the
-  // weighted V sum.
+  // weighted V sum.  The running max m is the reference the weights are
+  // taken against; it is raised, and the sums rescaled, only on tiles where
+  // some row's score passes it by more than kRaise (log2 units): the
+  // conditional rescaling of FlashAttention-4, which gives the same softmax
+  // up to rounding, keeps every weight below 2^kRaise and lets most tiles
+  // skip the rescale of the 4 x NS accumulators.
+  static constexpr float kRaise = 8.f;
+
   __device__ __forceinline__ void tile(const Chunk &d, int t0, const u32x4 (&kk)[NKS], const u32x4 (&vv)[4],
                                        const u32x4 (&q)[NKS]) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     f4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NKS; ++j) st = mfma_qk<DT>(kk[j], r < M ? q[j] : zero, st);
-    // row r sees tokens [t_lo, min(t_hi, its causal limit))
+    for (int j = 0; j < NKS; ++j) st = mfma_qk<DT>(kk[j], q[j], st);
+    // row r sees tokens [t_lo, min(t_hi, its causal limit)); rows >= M
+    // follow row 0 (prefix pass: every row sees the whole shared prefix)
     const int t_lo = d.cb * TC;
     const int t_hi = min(d.L, d.ce * TC);
-    // (prefix pass: every row sees the whole shared prefix)
-    const int lim = r < M ? (pfx ? d.L : d.L - nq + 1 + r / gq) : 0;
-    const int t_row = min(t_hi, lim);
+    const int lim0 = pfx ? d.L : d.L - nq + 1;
     float sc[4];
+    u32x4 v[4];
+    if (t0 >= t_lo && t0 + GTC <= min(t_hi, lim0)) {
+      // a tile inside every row's range: nothing masked
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = t0 + 4 * g + i;
-      sc[i] = (tok >= t_lo && tok < t_row) ? st[i] * scale_log2 : kNegInf;
+      for (int i = 0; i < 4; ++i) sc[i] = st[i] * scale_log2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = vv[t];
+    } else {
+      const int t_row = min(t_hi, pfx || r >= M ? lim0 : lim0 + r / gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 4 * g + i;
+        sc[i] = (tok >= t_lo && tok < t_row) ? st[i] * scale_log2 : kNegInf;
+      }
+      // V rows of tokens outside [t_lo, t_hi) are zeroed (unused slots may hold NaN)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tok = t0 + 4 * g + t;
+        v[t] = (tok >= t_lo && tok < t_hi) ? vv[t] : zero;
+      }
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float mref = (mnew == kNegInf) ? 0.f : mnew;  // no valid token yet
-    const float alpha = fast_exp2(m - mref);             // m == -inf gives 0
+    const bool raise = mx > m + kRaise;  // m == -inf: any valid score
+    if (__ballot(raise) != 0) {
+      const float alpha = raise ? fast_exp2(m - mx) : 1.f;  // m == -inf gives 0
+      lp *= alpha;
+#pragma unroll
+      for (int s_ = 0; s_ < NS; ++s_) acc[s_] *= alpha;
+      m = raise ? mx : m;
+    }
+    const float mref = (m == kNegInf) ? 0.f : m;  // no valid token yet
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mref);  // -inf gives 0
-    lp = lp * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-    m = mnew;
+    lp += (p[0] + p[1]) + (p[2] + p[3]);
     constexpr int PT = F8 ? DT_F16 : DT;  // type of the weighted V sum's operands
     uint32_t p01, p23, r01 = 0, r23 = 0;
     if constexpr (PT == DT_F16) {
@@ -337,16 +392,8 @@ struct GroupStream {
       r01 = pack2<PT>(p[0] - lo16<PT>(p01), p[1] - hi16<PT>(p01));
       r23 = pack2<PT>(p[2] - lo16<PT>(p23), p[3] - hi16<PT>(p23));
     }
-    // V rows of tokens outside [t_lo, t_hi) are zeroed (unused slots may hold NaN)
-    u32x4 v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = t0 + 4 * g + t;
-      v[t] = (tok >= t_lo && tok < t_hi) ? vv[t] : zero;
-    }
 #pragma unroll
     for (int s_ = 0; s_ < NS; ++s_) {
-      acc[s_] *= alpha;
       // element e of the four V rows: dword e / 2, low or high half (e = s_
       // at head_dim 128; 2 s_ + r / 8 at 64)
       const int hi = GDIM == 128 ? (s_ & 1) : (r >> 3);
