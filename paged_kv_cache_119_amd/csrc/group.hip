@@ -614,23 +614,23 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   const int64_t n = (int64_t)udiv64(end - 1, slice) - t_a + 1;
   if (n <= 1 || !live) return;  // one piece: it wrote the rows
   auto slot = [&](int64_t j) { return (t_a + j + grow) * M + r; };
-  // the row's max over its pieces, four pieces per round of loads
+  // pieces combined in worker order, with the row's max over its pieces
   float mx = kNegInf;
-  for (int64_t j0 = 0; j0 < n; j0 += 4) {
-    float mv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mv[q] = a.ws_m[slot(min(j0 + q, n - 1))];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
-  }
-  // pieces combined in worker order
   float lsum = 0.f;
   f4 o[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) o[k] = f4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t j0 = 0; j0 < n; j0 += 4) {
-    float mv[4], lv[4];
-    f4 ov[4][NV];
+  auto fold = [&](const float (&mv)[4], const float (&lv)[4], const f4 (&ov)[4][NV], int64_t j0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (j0 + q >= n) break;
+      const float f = (mv[q] == kNegInf) ? 0.f : fast_exp2((mv[q] - mx) * kLog2e);
+      lsum += f * lv[q];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) o[k] += f * ov[q][k];
+    }
+  };
+  auto fetch = [&](float (&mv)[4], float (&lv)[4], f4 (&ov)[4][NV], int64_t j0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t u = slot(min(j0 + q, n - 1));
@@ -640,13 +640,29 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
 #pragma unroll
       for (int k = 0; k < NV; ++k) ov[q][k] = src[k];
     }
+  };
+  if (n <= 4) {
+    // the usual case: every piece in one round of loads
+    float mv[4], lv[4];
+    f4 ov[4][NV];
+    fetch(mv, lv, ov, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (j0 + q >= n) break;
-      const float f = (mv[q] == kNegInf) ? 0.f : fast_exp2((mv[q] - mx) * kLog2e);
-      lsum += f * lv[q];
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
+    fold(mv, lv, ov, 0);
+  } else {
+    // the max first, four pieces per round of loads, then the sums
+    for (int64_t j0 = 0; j0 < n; j0 += 4) {
+      float mv[4];
 #pragma unroll
-      for (int k = 0; k < NV; ++k) o[k] += f * ov[q][k];
+      for (int q = 0; q < 4; ++q) mv[q] = a.ws_m[slot(min(j0 + q, n - 1))];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
+    }
+    for (int64_t j0 = 0; j0 < n; j0 += 4) {
+      float mv[4], lv[4];
+      f4 ov[4][NV];
+      fetch(mv, lv, ov, j0);
+      fold(mv, lv, ov, j0);
     }
   }
   if (pfx) {
