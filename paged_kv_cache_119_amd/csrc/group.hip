@@ -178,6 +178,13 @@ struct GroupStream {
   ChunkCursor<TC> cur;  // the slice, chunk by chunk
   // running state of the current piece (row r of this lane)
   f4_t acc[NS];
+  // The piece's query fragments, loaded with its first chunk and held for
+  // the rest (this saves the query re-reads, up to 4 KiB per chunk, that
+  // otherwise queue beside the K/V reads).  e4m3 at head_dim 64 re-reads them
+  // with every chunk instead: holding them costs the register room of its
+  // third wave per SIMD, which is worth more there.
+  static constexpr bool kHoldQ = !(F8 && GDIM == 64);
+  u32x4 qf[NKS];
   float m, lp;
   bool bad;
 
@@ -269,8 +276,8 @@ struct GroupStream {
   }
 
   // Stage 2: K rows (16-bit: whole rows of tokens 4j + g; e4m3: token r), V
-  // rows (tokens 4g .. 4g+3) and the query rows of chunk d; the same loads
-  // for every chunk.
+  // rows (tokens 4g .. 4g+3) of chunk d, and with the first chunk of a piece
+  // its query rows (the same for all its chunks).
   // Tokens past the context read the row of token L - 1 instead (cache
   // lines already fetched: the unused tail of the last block costs no HBM
   // traffic); they are masked.
@@ -299,9 +306,11 @@ struct GroupStream {
         for (int t = 0; t < 4; ++t)
           b.v[4 * u + t] = ld_kv8<NT>(vp + vb + (int64_t)(min(GTC * u + 4 * g + t, last) - t0) * GDIM);
       }
+      if (!kHoldQ || d.c == d.cb) {
 #pragma unroll
-      for (int j = 0; j < NKS; ++j)
-        b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 16 * KPT * g + 8 * j);
+        for (int j = 0; j < NKS; ++j)
+          b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 16 * KPT * g + 8 * j);
+      }
     } else {
       // whole token rows (GDIM / 8 lanes a row): lane l of load j gets token
       // j * RPL + l / (GDIM / 8), dims 8(l % (GDIM / 8)) .. +8; consume
@@ -317,8 +326,10 @@ struct GroupStream {
       const int64_t vb = token_off(d, bb, t0) + 8 * (r % LPR);
 #pragma unroll
       for (int t = 0; t < 4; ++t) b.v[t] = ld_kv<NT>(vp + 2 * (vb + (int64_t)(min(4 * g + t, last) - t0) * GDIM));
+      if (d.c == d.cb) {
 #pragma unroll
-      for (int j = 0; j < NKS; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
+        for (int j = 0; j < NKS; ++j) b.q[j] = *reinterpret_cast<const u32x4 *>(qp + qrow + 8 * g + 32 * j);
+      }
     }
     b.bad = bd;
   }
@@ -413,6 +424,8 @@ struct GroupStream {
 #pragma unroll
       for (int s_ = 0; s_ < NS; ++s_) acc[s_] = f4_t{0.f, 0.f, 0.f, 0.f};
       bad = false;
+#pragma unroll
+      for (int j = 0; j < NKS; ++j) qf[j] = b.q[j];
     }
     bad = bad || b.bad;
 #pragma unroll
@@ -436,7 +449,7 @@ struct GroupStream {
 #pragma unroll
         for (int t = 0; t < 4; ++t) vv[t] = b.v[t];
       }
-      tile(d, d.c * TC + GTC * u, kk, vv, b.q);
+      tile(d, d.c * TC + GTC * u, kk, vv, kHoldQ ? qf : b.q);
     }
     if (d.c == d.ce - 1) finish_piece(d);
   }
