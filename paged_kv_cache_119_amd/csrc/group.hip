@@ -39,9 +39,10 @@
 // sums when a piece is written.  The weighted V sum of e4m3 pools runs in
 // binary16 whatever the query type (V is exact in it, the weights round to
 // 11 bits as on the binary16 path): one product per slice.
-// The work split, the pipeline (table entries two chunks ahead, K/V/Q one
-// chunk ahead, arithmetic on the current chunk) and the partial results /
-// merge follow the balanced decode kernel; rows are (sequence, KV head).
+// The work split, the pipeline (table entries two chunks ahead, K/V one
+// chunk ahead, arithmetic on the current chunk; a piece's query fragments come
+// with its first chunk) and the partial results / merge follow the balanced
+// decode kernel; rows are (sequence, KV head).
 
 #include <type_traits>
 
