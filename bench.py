@@ -281,6 +281,7 @@ def main(argv=None) -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": kern_bytes,
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2),
+                     "median_us": round(float(np.median(kern_ms)) * 1e3, 2),
                      "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
@@ -489,6 +490,12 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
     if args.copy_calibration:
         copy_calibration(torch, dev)
     ceiling = read_ceiling(torch, dev, nbytes)
+    kp0, vp0, q0, out0 = reps[0]
+    cpu = None
+    if not args.no_cpu_baseline:
+        qrows = q0 if Q > 1 else q0[:, None]
+        cpu = cpu_baseline(t, (kp0, vp0, qrows, None, None, out0), args.cpu_budget_s,
+                           "rows_fp8" if fp8 else "rows", ks, vs, rows=(Q, H))
     line = {
         "metric": "paged attention, several query rows per KV head: achieved HBM GB/s + KV tokens/s",
         "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
@@ -505,8 +512,11 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
-                     "mean_launch_us": round(kern_mean_ms * 1e3, 2)},
-        "cpu_baseline": None,
+                     "mean_launch_us": round(kern_mean_ms * 1e3, 2),
+                     "median_us": round(float(np.median(kern_ms)) * 1e3, 2),
+                     "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
+        "cpu_baseline": cpu,
         "read_ceiling": ceiling,
         "occupancy": with_measured(pkv.decode_launch_info(S, H, t.max_blocks, desc, 0, Q, args.kv == "fp8"),
                                    f"{args.config}/B{B}/rows/G{G}/Q{Q}" + ("/fp8" if fp8 else "")),
@@ -634,6 +644,7 @@ def bench_fp8(args, t, pkv, lib, dev) -> int:
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": kern_bytes,
                      "mean_launch_us": round(kern_mean_ms * 1e3, 2),
+                     "median_us": round(float(np.median(kern_ms)) * 1e3, 2),
                      "p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 2),
                      "p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
@@ -735,7 +746,10 @@ def bench_shared(args, t, pkv, lib, dev) -> int:
                                "(decode_balanced_kernel) + merge", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": by["total"],
-                     "mean_launch_us": round(call_mean * 1e3, 2)},
+                     "mean_launch_us": round(call_mean * 1e3, 2),
+                     "median_us": round(float(np.median(call_ms)) * 1e3, 2),
+                     "p10_us": round(float(np.percentile(call_ms, 10)) * 1e3, 2),
+                     "p90_us": round(float(np.percentile(call_ms, 90)) * 1e3, 2)},
         "cpu_baseline": cpu,
         "occupancy": {"prefix_pass": measured_occupancy(f"{args.config}/B{B}/shared-prefix/prefix-pass"),
                       "suffix_pass": measured_occupancy(f"{args.config}/B{B}/shared-prefix/suffix-pass")},
@@ -884,7 +898,15 @@ def _oracle_pass(kind, files, meta, seqs, t_start, budget_s):
         while time.perf_counter() - t0 <= budget_s:
             s = seqs[i % len(seqs)]
             i += 1
-            if kind == "fp8":
+            if kind in ("rows", "rows_fp8"):  # q [S, Q, H, D]: every query row of the sequence
+                if kind == "rows_fp8":
+                    po.decode_rows_fp8(np.asarray(qb[s:s + 1]), kb, vb, tabs[s:s + 1], lens[s:s + 1],
+                                       meta["scale"], meta["block_size"], meta["dtype"], meta["k_scale"],
+                                       meta["v_scale"])
+                else:
+                    po.decode_rows(np.asarray(qb[s:s + 1]), kb, vb, tabs[s:s + 1], lens[s:s + 1], meta["scale"],
+                                   meta["block_size"], meta["dtype"])
+            elif kind == "fp8":
                 po.decode_rows_fp8(np.asarray(qb[s:s + 1])[:, None], kb, vb, tabs[s:s + 1], lens[s:s + 1],
                                    meta["scale"], meta["block_size"], meta["dtype"], meta["k_scale"],
                                    meta["v_scale"])
@@ -912,14 +934,17 @@ def host_cores() -> tuple:
     return max(1, min(aff, share)), aff
 
 
-def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, vs: float = 1.0):
+def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, vs: float = 1.0,
+                 rows: tuple = None):
     """The float64 oracle timed on the host's cores, on host copies of one
     replica: N worker processes (N from host_cores(), one BLAS thread each)
     take the batch's sequences round-robin and decode them, all heads,
     passing over their share again until the budget is used; all workers
     start at one wall-clock time and the rate is taken over the span from the
     first start to the last end.  A one-thread leg in this process (budget / 2) is
-    reported beside it.  GB/s of the same algorithmic bytes, and KV tokens/s."""
+    reported beside it.  GB/s of the same algorithmic bytes, and KV tokens/s.
+    kind "rows" / "rows_fp8": q is [S, Q, H, D] over pools of t.num_heads KV
+    heads, rows = (Q, H), and the bytes are those of the rows bench line."""
     import multiprocessing as mp
     import shutil
     import tempfile
@@ -930,7 +955,7 @@ def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, 
     from synth import to_bits
 
     kp, vp, q, _, _, _ = rep
-    if kind == "fp8":
+    if kind in ("fp8", "rows_fp8"):
         kb, vb = kp.cpu().numpy(), vp.cpu().numpy()
     else:
         kb, vb = to_bits(kp), to_bits(vp)
@@ -949,7 +974,15 @@ def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, 
 
         def rate(done, dt):
             lens = t.context_lens[np.asarray(done, dtype=np.int64)]
-            by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size, kv_dtype_bytes=kv_bytes)["total"]
+            if rows is not None:
+                Q, H = rows
+                L = lens.astype(np.int64)
+                by = (int(L.sum()) * t.num_heads * t.head_dim * 2 * (1 if kind == "rows_fp8" else 2)
+                      + 2 * len(done) * Q * H * t.head_dim * 2 + int((-(-L // t.block_size)).sum()) * 4
+                      + len(done) * 4)
+            else:
+                by = acc.decode_bytes(lens, t.num_heads, t.head_dim, 2, t.block_size,
+                                      kv_dtype_bytes=kv_bytes)["total"]
             return by, int(lens.sum())
 
         # one thread, in this process
@@ -970,10 +1003,12 @@ def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, 
         by, tok = rate(done, dt)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    what = "sequence decodes over e4m3 pools" if kind == "fp8" else "sequence decodes"
+    what = "sequence decodes" + (" over e4m3 pools" if kind in ("fp8", "rows_fp8") else "")
+    if rows is not None:
+        what += f" ({rows[0]} query token(s) x {rows[1]} query heads each)"
     return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
             "sample": f"{len(done)} {what} ({len(done) / t.num_seqs:.1f} passes over the {t.num_seqs}-sequence "
-                      f"batch, all {t.num_heads} heads), {tok} KV tokens, {dt:.1f} s, numpy float64, {n} worker "
+                      f"batch, all {t.num_heads} {"KV " if rows is not None else ""}heads), {tok} KV tokens, {dt:.1f} s, numpy float64, {n} worker "
                       f"processes x 1 BLAS thread ({aff} cores in the affinity set); the sequences dealt "
                       f"round-robin to the workers",
             "kv_tokens_per_s": round(tok / dt, 1),
