@@ -1008,7 +1008,8 @@ def cpu_baseline(t, rep, budget_s: float, kind: str = "16bit", ks: float = 1.0, 
         what += f" ({rows[0]} query token(s) x {rows[1]} query heads each)"
     return {"value": round(by / dt / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
             "sample": f"{len(done)} {what} ({len(done) / t.num_seqs:.1f} passes over the {t.num_seqs}-sequence "
-                      f"batch, all {t.num_heads} {"KV " if rows is not None else ""}heads), {tok} KV tokens, {dt:.1f} s, numpy float64, {n} worker "
+                      f"batch, all {t.num_heads} {'KV ' if rows is not None else ''}heads), {tok} KV tokens, "
+                      f"{dt:.1f} s, numpy float64, {n} worker "
                       f"processes x 1 BLAS thread ({aff} cores in the affinity set); the sequences dealt "
                       f"round-robin to the workers",
             "kv_tokens_per_s": round(tok / dt, 1),
