@@ -91,6 +91,36 @@ def record_occupancy(agg: dict, key: str, kernel: str, summary: str) -> None:
         json.dump(dict(sorted(rec.items())), f, indent=2)
 
 
+def step_timeline(trace_dir: str, kernel: str) -> list:
+    """Markdown lines: median duration of `kernel` and of the launch after it,
+    and the median gaps between them, from the dispatch timestamps."""
+    import statistics
+    hits = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not hits:
+        return []
+    rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                  for r in csv.DictReader(open(hits[0])))
+    split, after, gap_in, gap_out, name = [], [], [], [], None
+    for i in range(1, len(rows) - 1):
+        a, b, c = rows[i], rows[i + 1], rows[i - 1]
+        if kernel in a[2] and "pkv" in a[2] and "pkv" in b[2] and kernel not in b[2]:
+            split.append(a[1] - a[0])
+            after.append(b[1] - b[0])
+            gap_in.append(b[0] - a[1])
+            name = short_name(b[2])
+            if "pkv" in c[2] and kernel not in c[2]:
+                gap_out.append(a[0] - c[1])
+    if not split:
+        return []
+    med = lambda v: statistics.median(v) / 1e3  # noqa: E731
+    lines = ["## Step timeline (kernel trace timestamps, medians over the timed steps)", "",
+             f"| `{kernel}` | gap | `{name}` | gap to the next step's `{kernel}` | step |", "|---|---|---|---|---|",
+             f"| {med(split):.2f} us | {med(gap_in):.2f} us | {med(after):.2f} us | "
+             f"{med(gap_out) if gap_out else float('nan'):.2f} us | "
+             f"{med(split) + med(gap_in) + med(after) + (med(gap_out) if gap_out else 0.0):.2f} us |", ""]
+    return lines
+
+
 def tables_main(argv) -> int:
     """Markdown tables from several rocprofv3 runs (kernel traces and counter
     passes), optionally with the measured occupancy recorded for bench.py."""
@@ -245,6 +275,7 @@ def main(argv=None) -> int:
         what = "measured fetch"
     lines += ["", f"Algorithmic bytes of one `{args.kernel}` launch: {args.algorithmic_bytes / 1e6:.2f} MB; "
               f"{what} {traffic / 1e6:.2f} MB ({traffic / args.algorithmic_bytes:.3f}x).", ""]
+    lines += step_timeline(args.trace, args.kernel)
     occ = counter_means(args.occ) if args.occ else None
     if occ is not None:
         lines += ["## Occupancy (rocprofv3 --pmc MeanOccupancyPerActiveCU, mean per dispatch)", ""]
