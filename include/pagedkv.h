@@ -27,7 +27,10 @@
  *    decode kernels' occupancy, filled on first use under a lock.  It never
  *    synchronises: each call only enqueues kernels on `stream` (a
  *    hipStream_t; NULL means the default stream) of the current device and
- *    returns.  Calls are thread-safe.
+ *    returns.  Calls are thread-safe.  Kernels are all a call enqueues (no
+ *    memory sets, copies or allocations), so a call can be captured in a HIP
+ *    graph and replayed; the one-time set-up above runs on the first call,
+ *    which should be made before a capture.
  *  - Host-side validation runs before anything is enqueued; a call that
  *    returns an error status has enqueued nothing.  PKV_ERR_HIP means the
  *    runtime rejected a launch or a device query.
