@@ -230,3 +230,42 @@ def test_launch_info_validation(lib):
     assert f(8, 4, 16, None, 0, 1, 0, 0, ctypes.byref(info)) == 1                # no pool
     assert f(8, 4, 16, ctypes.byref(_desc(D=96)), 0, 1, 0, 0, ctypes.byref(info)) == 3
     assert f(8, 4, 16, ctypes.byref(d), 0, 17 * 4, 0, 0, ctypes.byref(info)) == 3  # > 16 rows per KV head
+
+
+def test_header_compiles_as_c_and_links(lib, tmp_path):
+    """A plain C99 program (gcc, -Wall -Wextra -Werror -pedantic) includes the
+    header, takes the address of every declared entry point, links against the
+    library and calls its host-only functions."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    names = _declared()
+    src = tmp_path / "abi_check.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <string.h>\n#include \"pagedkv.h\"\n"
+        "typedef void (*fn_t)(void);\n"
+        f"static const void *entry_points[{len(names)}];\n"
+        "int main(void) {\n"
+        + "".join(f"  entry_points[{i}] = (const void *)(size_t)&{n};\n" for i, n in enumerate(names))
+        + "  for (size_t i = 0; i < sizeof entry_points / sizeof entry_points[0]; ++i)\n"
+          "    if (!entry_points[i]) return 2;\n"
+          "  pkv_pool p;\n  memset(&p, 0, sizeof p);\n"
+          "  p.num_blocks = 10; p.block_size = 16; p.num_kv_heads = 4; p.head_dim = 128; p.dtype = PKV_BF16;\n"
+          "  printf(\"%d %zu %lld %s\\n\", pkv_version(), pkv_pool_bytes(&p),\n"
+          "         (long long)pkv_pool_index(&p, 3, 2, 5, 7), pkv_status_string(PKV_ERR_SHAPE));\n"
+          "  return 0;\n}\n")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(bd.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.dirname(HEADER)}", str(src),
+           "-o", str(exe), f"-L{libdir}", "-lpagedkv", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    version, nbytes, index, text = r.stdout.split(" ", 3)
+    assert int(version) == 2
+    assert int(nbytes) == 10 * 4 * 16 * 128 * 2
+    assert int(index) == ((3 * 4 + 2) * 16 + 5) * 128 + 7
+    assert text.strip() == pkv.status_string(2)
