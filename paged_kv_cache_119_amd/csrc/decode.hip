@@ -373,19 +373,54 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams a) {
   if (L <= 0 || L > a.maxb * a.B) return;
   const int n = (L + a.P - 1) / a.P;
   if (n < 2) return;
+  const int lane = threadIdx.x;
   const int64_t u0 = (int64_t)sh * a.MP;
   const float *mp = a.ws_m + u0;
   const float *lp = a.ws_l + u0;
-  float M = mp[0];
-  for (int p = 1; p < n; ++p) M = fmaxf(M, mp[p]);
-  float lsum = 0.f;
-  for (int p = 0; p < n; ++p) lsum += fast_exp2((mp[p] - M) * kLog2e) * lp[p];
-  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + (int64_t)sh * D;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float o = 0.f;
-    for (int p = 0; p < n; ++p) o += fast_exp2((mp[p] - M) * kLog2e) * a.ws_o[(u0 + p) * D + d];
-    out_row[d] = to16<DT>(o / lsum);
+  // the partitions' maximum: 64 partitions per round of loads, then the wave
+  float M = kNegInf;
+  for (int p0 = 0; p0 < n; p0 += 64)
+    if (p0 + lane < n) M = fmaxf(M, mp[p0 + lane]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  // each partition's weight, computed by one lane and read back by all,
+  // then both sums in partition order (the o rows fetched 8 partitions a
+  // round; each lane holds dims lane and lane + 64)
+  constexpr int NDL = D / 64;
+  float lsum = 0.f, o[NDL];
+#pragma unroll
+  for (int k = 0; k < NDL; ++k) o[k] = 0.f;
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int pl = p0 + lane < n ? p0 + lane : n - 1;
+    const float f = fast_exp2((mp[pl] - M) * kLog2e);
+    const float fl = f * lp[pl];
+    const int cnt = min(64, n - p0);
+    int q0 = 0;
+    for (; q0 + 8 <= cnt; q0 += 8) {  // whole batches: all 8 rows' loads, then the sums
+      float ov[8][NDL];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) ov[q][k] = a.ws_o[(u0 + p0 + q0 + q) * D + 64 * k + lane];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float fq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), q0 + q));
+        lsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), q0 + q));
+#pragma unroll
+        for (int k = 0; k < NDL; ++k) o[k] += fq * ov[q][k];
+      }
+    }
+    for (; q0 < cnt; ++q0) {  // the rest, one by one
+      const float fq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), q0));
+      lsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fl), q0));
+#pragma unroll
+      for (int k = 0; k < NDL; ++k) o[k] += fq * a.ws_o[(u0 + p0 + q0) * D + 64 * k + lane];
+    }
   }
+  uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) + (int64_t)sh * D;
+#pragma unroll
+  for (int k = 0; k < NDL; ++k) out_row[64 * k + lane] = to16<DT>(o[k] / lsum);
 }
 
 // ---------------------------------------------------------------------------
