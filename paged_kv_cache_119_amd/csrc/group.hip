@@ -188,6 +188,22 @@ struct GroupStream {
   u32x4 qf[NKS];
   float m, lp;
   bool bad;
+  // The wavefront's first cut piece (a slice that starts inside a row)
+  // finishes in the middle of its stream.  Its partial results are kept in
+  // LDS (row i at stage + i * kStageRow floats) and written to the workspace
+  // when the stream ends: stores issued mid-stream would hold up the
+  // wavefront's later loads until they complete (the vector memory counter
+  // counts loads and stores in one order).  At most two pieces of a slice are
+  // cut, the first and the last, and the last ends the stream anyway.
+#ifndef PKV_STAGE_F8_D64
+#define PKV_STAGE_F8_D64 0
+#endif
+  static constexpr bool kStage = PKV_STAGE_F8_D64 || !(F8 && GDIM == 64);
+  static constexpr int kStageRow = GDIM + 4;  // +16 bytes: rows start in different banks
+  float *stage;
+  bool staged;     // wave-uniform: the stage holds a piece
+  int64_t st_u0;   // its first workspace slot (row 0)
+  float st_m, st_l;  // its max (natural-log units) and sum, for this lane's row
 
   __device__ __forceinline__ void init(const DecodeParams &a, const int64_t *cum_, const int32_t *lens_, int lane_) {
     kp = reinterpret_cast<const char *>(a.k_pool);
@@ -458,6 +474,12 @@ struct GroupStream {
   __device__ __forceinline__ void finish_piece(const Chunk &d) {
     lp += __shfl_xor(lp, 16);
     lp += __shfl_xor(lp, 32);
+    const bool cut = !(d.cb == 0 && d.ce * TC >= d.L);
+    const bool to_stage = kStage && cut && !staged;
+    staged = staged || to_stage;
+    // every lane takes part in flush(): the slot is set here, before the
+    // lanes of rows >= M leave
+    if (to_stage) st_u0 = (worker + (int64_t)d.s * Hkv + d.h) * M;
     if constexpr (F8) {
 #pragma unroll
       for (int s_ = 0; s_ < NS; ++s_) acc[s_] *= v_scale;
@@ -472,7 +494,7 @@ struct GroupStream {
         for (int s_ = 0; s_ < 8; ++s_) run[i][s_] = acc[s_][i];
       }
       const int run_dim[4] = {8 * (4 * g), 8 * (4 * g + 1), 8 * (4 * g + 2), 8 * (4 * g + 3)};
-      write_piece<4>(d, run, run_dim);
+      write_piece<4>(d, run, run_dim, to_stage);
     } else {
       // slice s_, value i: element 2 s_ + (g / 2) of the block 4(g % 2) + i,
       // so lanes (r, g) and (r, g ^ 2) hold the even and the odd elements of
@@ -496,13 +518,31 @@ struct GroupStream {
           run[k][2 * t + 1] = even ? recv[4 * k + t] : acc[t][2 + k];
         }
       }
-      write_piece<2>(d, run, run_dim);
+      write_piece<2>(d, run, run_dim, to_stage);
+    }
+  }
+
+  // The staged piece to the workspace: its M rows of GDIM floats are
+  // contiguous there (slots st_u0 ..), so every store instruction writes
+  // whole lines.
+  __device__ __forceinline__ void flush() {
+    if (!staged) return;
+    constexpr int PR = GDIM / 4;  // 16-byte pieces per row
+    f4_t *dst = reinterpret_cast<f4_t *>(ws_o + st_u0 * GDIM);
+    for (int i = lane; i < M * PR; i += 64) {
+      const int row = i / PR, col = i - (i / PR) * PR;
+      dst[i] = *reinterpret_cast<const f4_t *>(stage + row * kStageRow + 4 * col);
+    }
+    if (g == 0 && r < M) {
+      ws_m[st_u0 + r] = st_m;
+      ws_l[st_u0 + r] = st_l;
     }
   }
 
   // The finished piece of this lane's row r: runs of 8 consecutive dims.
   template <int NR>
-  __device__ __forceinline__ void write_piece(const Chunk &d, const float (&run)[NR][8], const int (&run_dim)[NR]) {
+  __device__ __forceinline__ void write_piece(const Chunk &d, const float (&run)[NR][8], const int (&run_dim)[NR],
+                                              bool to_stage) {
     const int qi = r / gq, gi = r - (r / gq) * gq;
     const float nanv = bad ? __builtin_nanf("") : 0.f;
     if (pfx && d.cb == 0 && d.ce * TC >= d.L) {
@@ -532,6 +572,15 @@ struct GroupStream {
         w.w = pack2<DT>(run[i][6] * inv + nanv, run[i][7] * inv + nanv);
         *reinterpret_cast<u32x4 *>(o + run_dim[i]) = w;
       }
+    } else if (to_stage) {
+      float *o = stage + r * kStageRow;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[run_dim[i] + e] = run[i][e] + nanv;
+      }
+      st_m = m * kLn2 + nanv;
+      st_l = lp + nanv;
     } else {
       const int64_t u = (worker + (int64_t)d.s * Hkv + d.h) * M + r;
       float *o = ws_o + u * GDIM;
@@ -572,14 +621,18 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   if (lo >= hi) return;
 
   __shared__ u32x4 ktiles[F8 ? 1 : NW * ST::kTile];
+  __shared__ float stages[ST::kStage ? NW * 16 * ST::kStageRow : 1];
   ST st;
   st.init(a, cum, lens, lane);
   st.ktile = ktiles + (F8 ? 0 : wave * ST::kTile);
+  st.stage = stages + (ST::kStage ? wave * 16 * ST::kStageRow : 0);
+  st.staged = false;
   st.worker = w;
   st.cur.enter(lo, hi);
   __builtin_amdgcn_s_setprio(3);
   run_stream(st, (int)(hi - lo));
   __builtin_amdgcn_s_setprio(0);
+  st.flush();
 }
 
 // One wavefront per (sequence, KV head), for its M query rows (16 rows x 4
