@@ -42,8 +42,7 @@
 // The work split, the pipeline (table entries two chunks ahead, K/V one
 // chunk ahead, arithmetic on the current chunk; a piece's query fragments come
 // with its first chunk) and the partial results / merge follow the balanced
-// decode kernel; rows are (sequence, KV head).  A wavefront's first cut piece
-// waits in LDS and is written when its stream ends (GroupStream::stage).
+// decode kernel; rows are (sequence, KV head).
 
 #include <type_traits>
 
