@@ -397,8 +397,9 @@ def read_ceiling(torch, dev, nbytes: int) -> dict:
 def bench_rows(args, t, pkv, lib, dev) -> int:
     """Several query rows per KV head on the matrix-core kernel: G query heads
     per KV head (grouped-query decode) and/or Q query tokens per sequence.
-    One step = the split pass and the merge pass of one call; the roofline
-    times the split pass (for Q > 1, the whole call)."""
+    One step = the split pass and the merge pass; the roofline times the
+    split pass (16-bit pools with Q > 1: the whole call, which has no
+    separate passes)."""
     import numpy as np
     import torch
 
@@ -446,12 +447,14 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
         if ev is not None:
             ev[0].record(stream)
         if fp8:
-            check(lib.pkv_paged_attention_multi_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
-                                                    tab.data_ptr(), lens.data_ptr(), ctypes.c_float(D ** -0.5),
-                                                    ctypes.c_float(ks), ctypes.c_float(vs), S, Q, H, t.max_blocks,
-                                                    dref, ws.data_ptr(), wsb, sp), "paged_attention_multi_fp8")
+            check(lib.pkv_decode_partitions_fp8(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+                                                tab.data_ptr(), lens.data_ptr(), ctypes.c_float(D ** -0.5),
+                                                ctypes.c_float(ks), ctypes.c_float(vs), S, Q, H, t.max_blocks,
+                                                dref, ws.data_ptr(), wsb, sp), "decode_partitions_fp8")
             if ev is not None:
                 ev[1].record(stream)
+            check(lib.pkv_decode_merge_fp8(out.data_ptr(), lens.data_ptr(), S, Q, H, t.max_blocks, dref,
+                                           ws.data_ptr(), wsb, sp), "decode_merge_fp8")
         elif Q == 1:
             check(lib.pkv_decode_partitions(out.data_ptr(), q.data_ptr(), kp.data_ptr(), vp.data_ptr(), tab.data_ptr(),
                                             lens.data_ptr(), ctypes.c_float(D ** -0.5), S, H, t.max_blocks, dref, 0,
@@ -508,7 +511,8 @@ def bench_rows(args, t, pkv, lib, dev) -> int:
                    "global_batch": S, "kv_tokens": t.kv_tokens(), "query_rows_per_kv_head": G * Q,
                    "parallelism": "none (1 GPU)"},
         "kv_tokens_per_s": round(t.kv_tokens() / (ms_per_step * 1e-3), 1),
-        "roofline": {"kernel": "decode_group_kernel" + (" (e4m3 K/V) + merge" if fp8 else " + merge" if Q > 1 else ""),
+        "roofline": {"kernel": (("decode_fp8_kernel" if fp8 else "decode_balanced_kernel") if G * Q == 1
+                                else "decode_group_kernel" + (" (e4m3 K/V)" if fp8 else " + merge" if Q > 1 else "")),
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,

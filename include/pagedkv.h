@@ -591,6 +591,29 @@ pkv_status pkv_paged_attention_multi_fp8(void *out, const void *q, const void *k
                                          int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
                                          void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * pkv_decode_partitions_fp8, pkv_decode_merge_fp8 -- the two passes of
+ * pkv_paged_attention_multi_fp8 (and, with num_queries == 1, of
+ * pkv_paged_attention_decode_fp8) as separate calls, as pkv_decode_partitions
+ * and pkv_decode_merge are for 16-bit pools: the split pass leaves the output
+ * rows of the (sequence, head) rows it handled in one piece and partial
+ * results for the rest in the workspace; the merge pass completes them and
+ * writes the rows of empty or invalid contexts.  The V scale is applied by
+ * the split pass, so the merge takes no scales.  Both calls must get the same
+ * shape arguments, pool and workspace; in between the workspace must not be
+ * touched.  Arguments, rules and errors as in pkv_paged_attention_multi_fp8;
+ * the output and the workspace are the caller's, the calls only enqueue
+ * kernels on `stream`.  The two calls give the one call's output bit for bit.
+ */
+pkv_status pkv_decode_partitions_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                     float k_scale, float v_scale, int32_t num_seqs, int32_t num_queries,
+                                     int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+pkv_status pkv_decode_merge_fp8(void *out, const int32_t *context_lens, int32_t num_seqs, int32_t num_queries,
+                                int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                const void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

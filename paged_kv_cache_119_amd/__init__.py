@@ -8,7 +8,7 @@ it plus byte accounting for the roofline.  Build the library with
 
 from ._binding import (EXPORTS, LIB_PATH, POOL_REUSE, PagedKVError, PoolDesc, alloc_workspace,  # noqa: F401
                        LaunchInfo, copy_blocks, decode_launch_info, decode_merge, decode_partition_size,
-                       decode_partitions, decode_partitions_append,
+                       decode_merge_fp8, decode_partitions, decode_partitions_append, decode_partitions_fp8,
                        decode_workspace_bytes, fp8_decode_workspace_bytes, fp8_multi_workspace_bytes, fp8_pool_bytes,
                        load_library,
                        make_pool_desc, multi_workspace_bytes, paged_attention_decode, paged_attention_decode_append,

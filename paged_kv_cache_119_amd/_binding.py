@@ -47,6 +47,8 @@ EXPORTS = (
     "pkv_paged_attention_decode_append_fp8",
     "pkv_fp8_multi_workspace_bytes",
     "pkv_paged_attention_multi_fp8",
+    "pkv_decode_partitions_fp8",
+    "pkv_decode_merge_fp8",
 )
 
 
@@ -130,6 +132,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pkv_paged_attention_decode_append_fp8": (ctypes.c_int, [vp, vp, vp, vp, i64, vp, vp, vp, vp, ctypes.c_float,
                                                                  ctypes.c_float, ctypes.c_float, i32, i32, i32, pool,
                                                                  vp, sz, vp]),
+        "pkv_decode_partitions_fp8": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                                     ctypes.c_float, i32, i32, i32, i32, pool, vp, sz, vp]),
+        "pkv_decode_merge_fp8": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, pool, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -589,6 +594,63 @@ def paged_attention_multi_fp8(q, k_pool, v_pool, block_tables, context_lens, sca
                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                            _stream_ptr(dev))
     _check(st, "pkv_paged_attention_multi_fp8")
+    return out
+
+
+def _fp8_rows(q, k_pool, v_pool, reuse_blocks):
+    """Pool descriptor and (S, Q, H) of a 16-bit query of [S, H, D] (one
+    token) or [S, Q, H, D] rows over e4m3 pools."""
+    desc = _fp8_pools(k_pool, v_pool, _dtype_name(q), reuse_blocks)
+    _need(q, "q", device=k_pool.device)
+    if q.dim() == 3:
+        S, H, D = (int(x) for x in q.shape)
+        Q = 1
+    elif q.dim() == 4:
+        S, Q, H, D = (int(x) for x in q.shape)
+    else:
+        raise ValueError(f"q must be [S, H, D] or [S, Q, H, D], got {tuple(q.shape)}")
+    if D != desc.head_dim:
+        raise ValueError(f"q head_dim {D} != pool head_dim {desc.head_dim}")
+    return desc, S, Q, H
+
+
+def decode_partitions_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale, out, workspace,
+                          reuse_blocks=False):
+    """The split pass over e4m3 pools alone (see pkv_decode_partitions_fp8):
+    ``q`` and ``out`` [S, H, D] or [S, Q, H, D]; decode_merge_fp8 with the same
+    workspace completes the call."""
+    torch = _torch()
+    lib = load_library()
+    desc, S, Q, H = _fp8_rows(q, k_pool, v_pool, reuse_blocks)
+    dev = k_pool.device
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("q, block_tables and context_lens disagree on the number of sequences")
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    maxb = int(block_tables.shape[1])
+    st = lib.pkv_decode_partitions_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
+                                       float(k_scale), float(v_scale), S, Q, H, maxb, ctypes.byref(desc),
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream_ptr(dev))
+    _check(st, "pkv_decode_partitions_fp8")
+    return out
+
+
+def decode_merge_fp8(out, context_lens, max_blocks_per_seq, k_pool, workspace, reuse_blocks=False):
+    """The merge pass over e4m3 pools alone (see pkv_decode_merge_fp8);
+    ``out`` as given to decode_partitions_fp8."""
+    torch = _torch()
+    lib = load_library()
+    desc, S, Q, H = _fp8_rows(out, k_pool, k_pool, reuse_blocks)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=k_pool.device)
+    st = lib.pkv_decode_merge_fp8(out.data_ptr(), context_lens.data_ptr(), S, Q, H, int(max_blocks_per_seq),
+                                  ctypes.byref(desc), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(k_pool.device))
+    _check(st, "pkv_decode_merge_fp8")
     return out
 
 

@@ -902,4 +902,31 @@ pkv_status pkv_paged_attention_multi_fp8(void *out, const void *q, const void *k
   return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
+pkv_status pkv_decode_partitions_fp8(void *out, const void *q, const void *k_pool, const void *v_pool,
+                                     const int32_t *block_tables, const int32_t *context_lens, float scale,
+                                     float k_scale, float v_scale, int32_t num_seqs, int32_t num_queries,
+                                     int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+  if (!fp8_scale_ok(k_scale) || !fp8_scale_ok(v_scale)) return PKV_ERR_SHAPE;
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, q, k_pool, v_pool, block_tables, context_lens, scale, num_seqs,
+                                    num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, true, &a,
+                                    num_queries, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
+  return hip_status(launch_split(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_decode_merge_fp8(void *out, const int32_t *context_lens, int32_t num_seqs, int32_t num_queries,
+                                int32_t num_heads, int32_t max_blocks_per_seq, const pkv_pool *p,
+                                const void *workspace, size_t workspace_bytes, void *stream) {
+  pkv::DecodeParams a;
+  const pkv_status st = fill_params(out, nullptr, nullptr, nullptr, nullptr, context_lens, 1.0f, num_seqs,
+                                    num_heads, max_blocks_per_seq, p, 0, workspace, workspace_bytes, false, &a,
+                                    num_queries, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

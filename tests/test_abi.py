@@ -209,6 +209,32 @@ def test_fp8_sizes_and_validation(lib):
     assert w(S, 8, maxb, ctypes.byref(d)) == lib.pkv_multi_workspace_bytes(S, 1, 8, maxb, ctypes.byref(d))
 
 
+def test_fp8_split_and_merge_validation(lib):
+    """The two passes of the e4m3 decode as separate calls check their
+    arguments as the one call does (no launch in any of these)."""
+    d = _desc(D=128)
+    nul = None
+    fake = ctypes.c_void_p(1 << 20)
+    sp, mg = lib.pkv_decode_partitions_fp8, lib.pkv_decode_merge_fp8
+    # zero sequences: nothing to do
+    assert sp(nul, nul, nul, nul, nul, nul, 0.1, 1.0, 1.0, 0, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 0
+    assert mg(nul, nul, 0, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 0
+    # scales: the split pass rejects what the one call rejects
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("nan"), 1.0)):
+        assert sp(fake, fake, fake, fake, fake, fake, 0.1, ks, vs, 4, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 2
+    # 6 query heads over 4 KV heads, more than 16 query rows per KV head
+    assert sp(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 1, 6, 8, ctypes.byref(d), nul, 0, nul) == 3
+    assert mg(fake, fake, 4, 1, 6, 8, ctypes.byref(d), nul, 0, nul) == 3
+    assert sp(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 5, 16, 8, ctypes.byref(d), nul, 0, nul) == 3
+    # a missing workspace
+    assert sp(fake, fake, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 4
+    assert mg(fake, fake, 4, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 4
+    assert mg(fake, fake, 4, 2, 8, 8, ctypes.byref(d), nul, 0, nul) == 4
+    # null pointers
+    assert sp(fake, nul, fake, fake, fake, fake, 0.1, 1.0, 1.0, 4, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 1
+    assert mg(nul, fake, 4, 1, 4, 8, ctypes.byref(d), nul, 0, nul) == 1
+
+
 def test_product_path_never_imports_the_oracle():
     """The library package must not reach the CPU oracle in any form."""
     pkg = os.path.join(ROOT, "paged_kv_cache_119_amd")
