@@ -595,7 +595,9 @@ pkv_status pkv_paged_attention_multi_fp8(void *out, const void *q, const void *k
  * pkv_decode_partitions_fp8, pkv_decode_merge_fp8 -- the two passes of
  * pkv_paged_attention_multi_fp8 (and, with num_queries == 1, of
  * pkv_paged_attention_decode_fp8) as separate calls, as pkv_decode_partitions
- * and pkv_decode_merge are for 16-bit pools: the split pass leaves the output
+ * and pkv_decode_merge are for 16-bit pools (attention over a context cut
+ * into pieces, each piece's (m, l, o) combined by the log-sum-exp merge:
+ * "PagedAttention 完全拆解", 原理详解（二）): the split pass leaves the output
  * rows of the (sequence, head) rows it handled in one piece and partial
  * results for the rest in the workspace; the merge pass completes them and
  * writes the rows of empty or invalid contexts.  The V scale is applied by
