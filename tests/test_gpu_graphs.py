@@ -166,3 +166,27 @@ def test_graph_shared_prefix():
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
     _check_replays(lambda: pkv.paged_attention_decode_shared(q, kp, vp, tab, lens, t.scale, k, pl, out=out,
                                                              workspace=ws), [out])
+
+
+def test_graph_fp8_split_and_merge_calls(opt13b):
+    """The e4m3 decode's two passes as separate calls, one query row and four
+    query heads per KV head."""
+    c = opt13b
+    t = c["t"]
+    S, H, D = t.num_seqs, t.num_heads, t.head_dim
+    log("graph: e4m3 split + merge as two calls (opt13b pools)")
+    kp, vp = make_fp8_pools(t, DEV)
+    for G in (1, 4):
+        q = c["q"] if G == 1 else normal_16bit((S, G * H, D), t.dtype, DEV, 9105)
+        out = torch.empty_like(q)
+        need = pkv.fp8_decode_workspace_bytes(S, G * H, t.max_blocks, kp, t.dtype)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
+
+        def two_calls():
+            pkv.decode_partitions_fp8(q, kp, vp, c["tab"], c["lens"], t.scale, 1.0 / 60, 1.0 / 60, out, ws)
+            pkv.decode_merge_fp8(out, c["lens"], t.max_blocks, kp, ws)
+
+        _check_replays(two_calls, [out])
+        one = pkv.paged_attention_decode_fp8(q, kp, vp, c["tab"], c["lens"], t.scale, 1.0 / 60, 1.0 / 60)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(one)), f"G={G}: two calls differ from the one call"
