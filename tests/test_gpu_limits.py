@@ -119,3 +119,45 @@ def test_fp8_at_the_limit():
         t2 = torch.from_numpy(np.concatenate([tables, tables[:1]])).to(DEV)
         l2 = torch.from_numpy(np.concatenate([lens, lens[:1]])).to(DEV)
         pkv.paged_attention_decode_fp8(q2, kp, vp, t2, l2, D ** -0.5, 0.004, 0.006)
+
+
+@pytest.mark.parametrize("G,Q", [(4, 1), (1, 4)])
+def test_fp8_grouped_at_the_limit(G, Q):
+    """e4m3 pools through the matrix-core kernel (several query rows per KV
+    head) at the largest batch, with its staging buffer in LDS beside the
+    per-sequence cost prefix; one more sequence is rejected."""
+    S, Hkv = 4096, 2
+    log(f"fp8 grouped limit: {S} sequences G={G} Q={Q}")
+    lens, tables, N = _tables(S, 430 + G + Q)
+    lens = np.maximum(lens, Q).astype(np.int32)
+    nb = -(-lens // B)
+    assert np.all(nb <= np.sum(tables >= 0, axis=1))
+    live = np.zeros((N, B), bool)
+    for s in range(S):
+        for j in range(int(lens[s])):
+            live[tables[s, j // B], j % B] = True
+    kp = random_e4m3((N, Hkv, B, D), DEV, 431, 0, 15)
+    vp = random_e4m3((N, Hkv, B, D), DEV, 432, 0, 15)
+    dead = torch.from_numpy(~live).to(DEV)[:, None, :, None].expand(kp.shape)
+    for pool in (kp, vp):
+        pool.masked_fill_(dead, FP8_NAN)
+    shape = (S, Hkv * G, D) if Q == 1 else (S, Q, Hkv * G, D)
+    q = normal_16bit(shape, "bf16", DEV, 433)
+    tab = torch.from_numpy(tables).to(DEV)
+    ll = torch.from_numpy(lens).to(DEV)
+    call = pkv.paged_attention_decode_fp8 if Q == 1 else pkv.paged_attention_multi_fp8
+    out = call(q, kp, vp, tab, ll, D ** -0.5, 0.004, 0.006)
+    torch.cuda.synchronize()
+    ob = to_bits(out)
+    assert np.all(np.isfinite(po.bits_to_f64(ob, "bf16")))
+    pick = _sample(S, 434)
+    qb = to_bits(q)[pick]
+    ref = po.decode_rows_fp8(qb[:, None] if Q == 1 else qb, kp.cpu().numpy(), vp.cpu().numpy(), tables[pick],
+                             lens[pick], D ** -0.5, B, "bf16", 0.004, 0.006)
+    ref = ref[:, 0] if Q == 1 else ref
+    assert_close(ob[pick], ref, "bf16", f"fp8 grouped {S} sequences G={G} Q={Q} ({len(pick)} sampled)")
+    with pytest.raises(pkv.PagedKVError):
+        q2 = normal_16bit((S + 1, *shape[1:]), "bf16", DEV, 435)
+        t2 = torch.from_numpy(np.concatenate([tables, tables[:1]])).to(DEV)
+        l2 = torch.from_numpy(np.concatenate([lens, lens[:1]])).to(DEV)
+        call(q2, kp, vp, t2, l2, D ** -0.5, 0.004, 0.006)
