@@ -636,11 +636,20 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
 }
 
 // One wavefront per (sequence, KV head), for its M query rows (16 rows x 4
-// lanes x 32 dims): rows of empty or invalid contexts, and the LSE merge of
+// lanes): rows of empty or invalid contexts, and the LSE merge of
 // rows cut over several workers.  The pieces' (m, l) and o rows are fetched
-// four pieces per round of loads.
+// four pieces at a time (rows cut into more pieces: every piece's m first,
+// 16 a round).
 // TC: the chunk length of the split pass that wrote the partials.
-// GDIM: head_dim (each lane takes GDIM / 4 dims of its row).
+// GDIM: head_dim.  Lane c (of the four lanes of a row) takes dims 16k + 4c
+// .. +4, k < GDIM / 16: one load instruction then reads 64 contiguous bytes of
+// each row's partial result.  Whole runs of 32 dims a lane touched 16 bytes
+// of 64 cache lines per instruction; this layout made the merge 13-26% faster.
+// The compiler issues each piece's loads inside the test for that piece, so a
+// row's pieces are loaded one after another.  Holding all four in flight
+// (selects instead of the test, with or without loads of absent pieces, 2 or
+// 3 waves per SIMD) measured slower: the merge is bound by its loads' cache
+// lines more than by their round trips.
 template <int DT, int TC, int GDIM = 128>
 __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
   typedef float f4 __attribute__((ext_vector_type(4)));
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   const int h = (int)(grow - (int64_t)s * a.Hkv);
   const int r = lane >> 2;         // this lane's query row (16 rows x 4 lanes)
   constexpr int NV = GDIM / 16;     // float4s of this lane's dims
-  const int d0 = (lane & 3) * (GDIM / 4);  // and its GDIM / 4 dims
+  const int d0 = (lane & 3) * 4;    // the first of them (then every 16th)
   const bool live = r < M;
   const int qi = r / gq, gi = r - (r / gq) * gq;
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) +
@@ -669,7 +678,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     const uint32_t v = (L == 0) ? 0u : 0x00010001u * to16<DT>(__builtin_nanf(""));
     if (live) {
 #pragma unroll
-      for (int k = 0; k < NV / 2; ++k) reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{v, v, v, v};
+      for (int k = 0; k < NV; ++k) *reinterpret_cast<u32x2 *>(out_row + 16 * k) = u32x2{v, v};
     }
     return;
   }
@@ -703,9 +712,9 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
       const int64_t u = slot(min(j0 + q, n - 1));
       mv[q] = a.ws_m[u];
       lv[q] = a.ws_l[u];
-      const f4 *src = reinterpret_cast<const f4 *>(a.ws_o + u * GDIM + d0);
+      const float *src = a.ws_o + u * GDIM + d0;
 #pragma unroll
-      for (int k = 0; k < NV; ++k) ov[q][k] = src[k];
+      for (int k = 0; k < NV; ++k) ov[q][k] = *reinterpret_cast<const f4 *>(src + 16 * k);
     }
   };
   if (n <= 4) {
@@ -717,14 +726,19 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
     fold(mv, lv, ov, 0);
   } else {
-    // the max first, four pieces per round of loads, then the sums
-    for (int64_t j0 = 0; j0 < n; j0 += 4) {
-      float mv[4];
+    // the max first (the four lanes of a row take every fourth piece, 16
+    // pieces a round), then the sums, four pieces per round
+    const int c = lane & 3;
+    for (int64_t j0 = 0; j0 < n; j0 += 16) {
+      float mm[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) mv[q] = a.ws_m[slot(min(j0 + q, n - 1))];
+      for (int i = 0; i < 4; ++i) mm[i] = a.ws_m[slot(min(j0 + 4 * i + c, n - 1))];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, mm[i]);
     }
+    // across the row's four lanes (all live or all not)
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
     for (int64_t j0 = 0; j0 < n; j0 += 4) {
       float mv[4], lv[4];
       f4 ov[4][NV];
@@ -735,24 +749,21 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   if (pfx) {
     // the merged softmax state of the prefix (max in log2 units)
     const int64_t pi = ((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi;
-    f4_t *dst = reinterpret_cast<f4_t *>(a.pfx_o + pi * GDIM + d0);
+    float *dst = a.pfx_o + pi * GDIM + d0;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) dst[k] = o[k];
+    for (int k = 0; k < NV; ++k) *reinterpret_cast<f4_t *>(dst + 16 * k) = o[k];
     if ((lane & 3) == 0) {
       a.pfx_m[pi] = mx * kLog2e;
       a.pfx_l[pi] = lsum;
     }
     return;
   }
-  uint32_t w[2 * NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    w[2 * k] = (uint32_t)to16<DT>(o[k][0] / lsum) | ((uint32_t)to16<DT>(o[k][1] / lsum) << 16);
-    w[2 * k + 1] = (uint32_t)to16<DT>(o[k][2] / lsum) | ((uint32_t)to16<DT>(o[k][3] / lsum) << 16);
+    const uint32_t w0 = (uint32_t)to16<DT>(o[k][0] / lsum) | ((uint32_t)to16<DT>(o[k][1] / lsum) << 16);
+    const uint32_t w1 = (uint32_t)to16<DT>(o[k][2] / lsum) | ((uint32_t)to16<DT>(o[k][3] / lsum) << 16);
+    *reinterpret_cast<u32x2 *>(out_row + 16 * k) = u32x2{w0, w1};
   }
-#pragma unroll
-  for (int k = 0; k < NV / 2; ++k)
-    reinterpret_cast<u32x4 *>(out_row)[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
 }
 
 template <int DT, int B, bool NT, bool F8, int GDIM>

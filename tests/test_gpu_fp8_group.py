@@ -97,6 +97,29 @@ def test_fp8_grouped_query_llama70b_shape_sampled():
     assert_close(to_bits(out)[pick], ref, "bf16", f"fp8 gqa 64/8 ({len(pick)} sequences)")
 
 
+@pytest.mark.parametrize("G,Q", [(8, 1), (2, 4)])
+def test_fp8_rows_long_context_many_pieces(G, Q):
+    """Long rows over two KV heads, e4m3 pools (32-token chunks): the longest
+    row is cut into far more than 16 pieces, so the merge takes their maxima
+    over several rounds before the sums; every output against the oracle."""
+    Hkv, B, dtype = 2, 16, "bf16"
+    lengths = [30000, 17777, 16, 40]
+    log(f"fp8 rows, long contexts: G={G} Q={Q}")
+    c = _case(lengths, Hkv, B, seed=2500 + 10 * G + Q, exp_lo=4, exp_hi=10)
+    desc = pkv.make_pool_desc(c["kp"].shape[0], B, Hkv, D, dtype)
+    info = pkv.decode_launch_info(len(lengths), Hkv * G, c["tables"].shape[1], desc, 0, Q, True)
+    workers = info["workgroups"] * info["waves_per_workgroup"]
+    chunks = [-(-L // 32) for L in lengths]
+    total = Hkv * sum(chunks)
+    assert max(chunks) // -(-total // max(1, min(workers, total // 8))) > 16
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 2510 + G + Q)
+    out = _run(c, q, D ** -0.5, 0.5, 1.5)
+    torch.cuda.synchronize()
+    assert_close(to_bits(out), _oracle(c, q, D ** -0.5, 0.5, 1.5, dtype), dtype,
+                 f"fp8 rows G={G} Q={Q}, long contexts")
+
+
 def test_fp8_rows_edge_cases_and_policy():
     """L == 0 gives zeros; L < Q and an out-of-pool entry give NaN rows; the
     other rows are unaffected; streamed and cached loads agree bit for bit."""

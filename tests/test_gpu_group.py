@@ -97,6 +97,35 @@ def test_grouped_query_llama70b_shape_sampled():
     assert_close(to_bits(out)[pick], ref, "bf16", f"gqa 64/8 ({len(pick)} sequences)")
 
 
+def _cut_rows_min_pieces(lengths, Hkv, TC, workers):
+    """A lower bound on the pieces the balanced split cuts the longest row
+    into: rows of ceil(L / TC) chunks, slices of the total over at most
+    `workers` (each at least 8 chunks)."""
+    chunks = [-(-L // TC) for L in lengths]
+    total = Hkv * sum(chunks)
+    sl = -(-total // max(1, min(workers, total // 8)))
+    return max(chunks) // sl
+
+
+@pytest.mark.parametrize("G,Q", [(8, 1), (2, 4), (1, 16)])
+def test_rows_long_context_many_pieces(G, Q):
+    """Long rows over two KV heads at head_dim 128: the longest row is cut
+    into far more than 16 pieces, so the merge takes their maxima over several
+    rounds before the sums; every output against the oracle."""
+    Hkv, B, dtype = 2, 16, "bf16"
+    lengths = [30000, 17777, 16, 40]
+    log(f"rows, long contexts: G={G} Q={Q}")
+    c = _case(lengths, Hkv, B, dtype, seed=2400 + 10 * G + Q)
+    desc = pkv.make_pool_desc(c["kp"].shape[0], B, Hkv, D, dtype)
+    info = pkv.decode_launch_info(len(lengths), Hkv * G, c["tables"].shape[1], desc, 0, Q)
+    assert _cut_rows_min_pieces(lengths, Hkv, 16, info["workgroups"] * info["waves_per_workgroup"]) > 16
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 2410 + G + Q)
+    out = _run(c, q, D ** -0.5)
+    torch.cuda.synchronize()
+    assert_close(to_bits(out), _oracle(c, q, D ** -0.5, dtype), dtype, f"rows G={G} Q={Q}, long contexts")
+
+
 def test_rows_edge_cases_empty_short_and_bad_entries():
     """L == 0 gives zeros; L < Q (queries not in the context) and a table
     entry outside the pool give NaN rows; the other rows are unaffected; NaN
