@@ -19,7 +19,7 @@
 //    load instruction would touch 16 rows x 64 bytes (half cache lines), so
 //    16-bit K is loaded as whole rows (lane l of load j: token 4j + l/16,
 //    dims 8(l%16) .. +8) and transposed through a per-wavefront LDS tile
-//    before the products (8% faster on the Llama-2-70B shape).
+//    before the products (5% faster on the Llama-2-70B shape).
 //  * Q: lane l holds query row l%16, the same dims -- the B operand of Q^T.
 //  * S^T result: lane l holds tokens 4(l/16) .. +4 of row l%16 -- the B
 //    operand P^T of the 16x16x16 product (k = tokens 4(l/16) .. +4).
@@ -195,10 +195,10 @@ struct GroupStream {
   // wavefront's later loads until they complete (the vector memory counter
   // counts loads and stores in one order).  At most two pieces of a slice are
   // cut, the first and the last, and the last ends the stream anyway.
-#ifndef PKV_STAGE_F8_D64
-#define PKV_STAGE_F8_D64 0
-#endif
-  static constexpr bool kStage = PKV_STAGE_F8_D64 || !(F8 && GDIM == 64);
+  // e4m3 pools at head_dim 64 store the piece directly: the stage's
+  // registers would cost that kernel its third wave per SIMD (measured
+  // slower).
+  static constexpr bool kStage = !(F8 && GDIM == 64);
   static constexpr int kStageRow = GDIM + 4;  // +16 bytes: rows start in different banks
   float *stage;
   bool staged;     // wave-uniform: the stage holds a piece
