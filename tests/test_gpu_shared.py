@@ -127,6 +127,20 @@ def test_groups_every_output(k, B, dtype, D):
     assert_close(to_bits(out), _oracle(c), dtype, f"shared k={k} B={B} {dtype} D={D}")
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_long_prefixes_cut_into_many_pieces(D):
+    """Two groups of four over 20,000- and 9,000-token prefixes on two heads:
+    the prefix pass cuts each prefix row into far more than 16 pieces, so
+    its merge takes their maxima over several rounds before it writes the
+    prefix state; every output against the oracle."""
+    log(f"shared prefix, long prefixes: D={D}")
+    prefixes = [20000, 9000]
+    privs = [[0, 5, 130, 17], [1, 64, 300, 2]]
+    c = _groups_case(prefixes, privs, 2, D, 16, "bf16", 41 + D)
+    out = _run(c)
+    assert_close(to_bits(out), _oracle(c), "bf16", f"shared, long prefixes, D={D}")
+
+
 def test_copies_of_the_prefix_give_the_same_bits():
     """The result depends on the prefix contents only: one copy referenced by
     every member, or a copy per member, give the same bits."""
