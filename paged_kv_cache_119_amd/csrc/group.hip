@@ -172,9 +172,19 @@ struct GroupStream {
   int lane, g, r;
   int64_t worker;
   // 16-bit pools: this wavefront's K transpose tile (16 token rows of kKRow
-  // 16-byte pieces; the padding piece keeps 16 lanes' reads off one bank)
+  // 16-byte pieces; the padding piece keeps 16 lanes' reads off one bank).
   static constexpr int kKRow = GDIM / 8 + 1;
   static constexpr int kTile = 16 * kKRow;
+  // A whole row's output (M rows of GDIM 16-bit values): with 16-bit pools
+  // at head_dim 128 (kTileOut) and M > 8 it passes through the K tile, so
+  // that a store instruction writes whole rows; stored from the lanes' runs,
+  // an instruction puts 16 bytes in each of 32 lines (16 query tokens: split
+  // pass 94 against 91.5 us).  Otherwise the lanes store their runs: with
+  // M <= 8, and over e4m3 pools, the tiled stores measured no faster, and at
+  // head_dim 64 their registers would cost a wave per SIMD.  Keeping a whole
+  // row's output in LDS until the stream ends (as the first cut piece is)
+  // gained nothing either.
+  static constexpr bool kTileOut = !F8 && GDIM == 128;
   u32x4 *ktile;
   ChunkCursor<TC> cur;  // the slice, chunk by chunk
   // running state of the current piece (row r of this lane)
@@ -486,7 +496,6 @@ struct GroupStream {
     }
     if constexpr (GDIM == 128) {
       // slice s_, value i: dim 8(4g + i) + s_ -- four runs of 8 dims per lane
-      if (r >= M) return;
       float run[4][8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -494,7 +503,7 @@ struct GroupStream {
         for (int s_ = 0; s_ < 8; ++s_) run[i][s_] = acc[s_][i];
       }
       const int run_dim[4] = {8 * (4 * g), 8 * (4 * g + 1), 8 * (4 * g + 2), 8 * (4 * g + 3)};
-      write_piece<4>(d, run, run_dim, to_stage);
+      end_piece<4>(d, run, run_dim, cut, to_stage);
     } else {
       // slice s_, value i: element 2 s_ + (g / 2) of the block 4(g % 2) + i,
       // so lanes (r, g) and (r, g ^ 2) hold the even and the odd elements of
@@ -506,7 +515,6 @@ struct GroupStream {
 #pragma unroll
         for (int t = 0; t < 4; ++t) recv[4 * k + t] = __shfl_xor(even ? acc[t][2 + k] : acc[t][k], 32);
       }
-      if (r >= M) return;
       float run[2][8];
       int run_dim[2];
 #pragma unroll
@@ -518,7 +526,63 @@ struct GroupStream {
           run[k][2 * t + 1] = even ? recv[4 * k + t] : acc[t][2 + k];
         }
       }
-      write_piece<2>(d, run, run_dim, to_stage);
+      end_piece<2>(d, run, run_dim, cut, to_stage);
+    }
+  }
+
+  // Eight output values of a run, normalised and rounded to the element type.
+  __device__ __forceinline__ static u32x4 pack8(const float (&v)[8], float inv, float nanv) {
+    u32x4 w;
+    w.x = pack2<DT>(v[0] * inv + nanv, v[1] * inv + nanv);
+    w.y = pack2<DT>(v[2] * inv + nanv, v[3] * inv + nanv);
+    w.z = pack2<DT>(v[4] * inv + nanv, v[5] * inv + nanv);
+    w.w = pack2<DT>(v[6] * inv + nanv, v[7] * inv + nanv);
+    return w;
+  }
+
+  // A whole row (not a prefix pass, kTileOut, M > 8): its final output
+  // through the tile, with every lane; otherwise the lanes of rows < M write
+  // the piece.
+  template <int NR>
+  __device__ __forceinline__ void end_piece(const Chunk &d, const float (&run)[NR][8], const int (&run_dim)[NR],
+                                            bool cut, bool to_stage) {
+    if constexpr (kTileOut) {
+      if (!cut && !pfx && M > 8) {
+        // lane (r, g) leaves its runs at piece run_dim / 8 of tile row r
+        if (r < M) {
+          const float nanv = bad ? __builtin_nanf("") : 0.f;
+          const float inv = 1.f / lp;
+#pragma unroll
+          for (int i = 0; i < NR; ++i) ktile[r * kKRow + run_dim[i] / 8] = pack8(run[i], inv, nanv);
+        }
+        store_out_rows(((int64_t)d.s * nq * H + (int64_t)d.h * gq) * GDIM,
+                       [&](int rr, int p) { return ktile[rr * kKRow + p]; });
+        return;
+      }
+    }
+    if (r >= M) return;
+    write_piece<NR>(d, run, run_dim, to_stage);
+  }
+
+  // Lane l stores piece l % PPR of query row RPI j + l / PPR of the output
+  // rows whose pieces src(rr, p) returns (rr < 16), so that a store
+  // instruction writes RPI whole rows; row (qi, gi) lies (qi H + gi) GDIM
+  // elements past row (0, 0) at o_base.
+  template <class Src>
+  __device__ __forceinline__ void store_out_rows(int64_t o_base, Src src) {
+    constexpr int PPR = GDIM / 8;  // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;  // rows per store instruction
+    const int p = lane % PPR;
+    const float inv_gq = 1.f / (float)gq;
+#pragma unroll 1  // unrolled, the rounds' registers cost a wave per SIMD
+    for (int j = 0; j < 16 / RPI; ++j) {
+      if (RPI * j >= M) break;
+      const int rr = RPI * j + lane / PPR;
+      const u32x4 w = src(min(rr, 15), p);
+      // rr / gq: (rr + 1/2) / gq lies at least 1/32 from an integer
+      const int qi = (int)(((float)rr + 0.5f) * inv_gq);
+      const int gi = rr - qi * gq;
+      if (rr < M) *reinterpret_cast<u32x4 *>(outp + o_base + (qi * H + gi) * GDIM + 8 * p) = w;
     }
   }
 
@@ -539,7 +603,8 @@ struct GroupStream {
     }
   }
 
-  // The finished piece of this lane's row r: runs of 8 consecutive dims.
+  // The finished piece of this lane's row r (a cut piece, or a whole row not
+  // stored through the tile): runs of 8 consecutive dims.
   template <int NR>
   __device__ __forceinline__ void write_piece(const Chunk &d, const float (&run)[NR][8], const int (&run_dim)[NR],
                                               bool to_stage) {
@@ -564,14 +629,7 @@ struct GroupStream {
       uint16_t *o = outp + (((int64_t)d.s * nq + qi) * H + (int64_t)d.h * gq + gi) * GDIM;
       const float inv = 1.f / lp;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        u32x4 w;
-        w.x = pack2<DT>(run[i][0] * inv + nanv, run[i][1] * inv + nanv);
-        w.y = pack2<DT>(run[i][2] * inv + nanv, run[i][3] * inv + nanv);
-        w.z = pack2<DT>(run[i][4] * inv + nanv, run[i][5] * inv + nanv);
-        w.w = pack2<DT>(run[i][6] * inv + nanv, run[i][7] * inv + nanv);
-        *reinterpret_cast<u32x4 *>(o + run_dim[i]) = w;
-      }
+      for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(o + run_dim[i]) = pack8(run[i], inv, nanv);
     } else if (to_stage) {
       float *o = stage + r * kStageRow;
 #pragma unroll
