@@ -160,6 +160,39 @@ def test_fp8_d64_rows_every_output(dtype, B, G, Q):
     assert_close(to_bits(out), ref, dtype, f"fp8 D=64 rows G={G} Q={Q} {dtype} B={B}")
 
 
+@pytest.mark.parametrize("G,Q", [(8, 1), (2, 4)])
+def test_fp8_d64_rows_long_context_many_pieces(G, Q):
+    """Long rows over two KV heads, e4m3 pools at head_dim 64 (the matrix-core
+    kernel, 32-token chunks): the longest row is cut into far more than 16
+    pieces, so the merge takes their maxima over several rounds before the
+    sums; every output against the oracle."""
+    Hkv, B, dtype = 2, 16, "bf16"
+    lengths = [30000, 17777, 16, 40]
+    log(f"fp8 D=64 rows, long contexts: G={G} Q={Q}")
+    c = _case(lengths, Hkv, B, seed=580 + 10 * G + Q, exp_lo=4, exp_hi=10)
+    desc = pkv.make_pool_desc(c["kp"].shape[0], B, Hkv, D, dtype)
+    info = pkv.decode_launch_info(len(lengths), Hkv * G, c["tables"].shape[1], desc, 0, Q, True)
+    workers = info["workgroups"] * info["waves_per_workgroup"]
+    chunks = [-(-L // 32) for L in lengths]
+    total = Hkv * sum(chunks)
+    assert max(chunks) // -(-total // max(1, min(workers, total // 8))) > 16
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 581 + G + Q)
+    tab = torch.from_numpy(c["tables"]).to(DEV)
+    lens = torch.from_numpy(c["lens"]).to(DEV)
+    if Q == 1:
+        out = pkv.paged_attention_decode_fp8(q, c["kp"], c["vp"], tab, lens, D ** -0.5, 0.5, 1.5)
+    else:
+        out = pkv.paged_attention_multi_fp8(q, c["kp"], c["vp"], tab, lens, D ** -0.5, 0.5, 1.5)
+    torch.cuda.synchronize()
+    qb = to_bits(q)
+    qb = qb[:, None] if Q == 1 else qb
+    ref = po.decode_rows_fp8(qb, _codes(c["kp"]), _codes(c["vp"]), c["tables"], c["lens"], D ** -0.5, B, dtype,
+                             0.5, 1.5)
+    ref = ref[:, 0] if Q == 1 else ref
+    assert_close(to_bits(out), ref, dtype, f"fp8 D=64 rows G={G} Q={Q}, long contexts")
+
+
 def test_fp8_d64_grouped_decode_step():
     """The decode step with the quantising append and grouped heads at head
     _dim 64 (the append is its own launch): codes and output as the oracle's."""
