@@ -78,6 +78,23 @@ def test_rows_per_kv_head_small_shapes(dtype, B, G, Q):
     assert_close(to_bits(out), ref, dtype, f"rows G={G} Q={Q} {dtype} B={B}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("G,Q", [(3, 4), (5, 3), (6, 2), (2, 5), (9, 1), (4, 3), (7, 2), (1, 11)])
+def test_rows_between_9_and_15_per_kv_head(dtype, G, Q):
+    """9 to 15 query rows per KV head with odd group sizes: whole rows'
+    outputs go through the wavefront's LDS tile and are stored as whole rows,
+    row (token i, head j) found from the tile row; every output against the
+    oracle, long rows cut into pieces included."""
+    Hkv = 2
+    lengths = [max(L, Q) for L in LENGTHS] + [3000, 1234]
+    c = _case(lengths, Hkv, 16, dtype, seed=1500 + 10 * G + Q)
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 1510 + G + Q)
+    out = _run(c, q, D ** -0.5)
+    torch.cuda.synchronize()
+    assert_close(to_bits(out), _oracle(c, q, D ** -0.5, dtype), dtype, f"rows G={G} Q={Q} {dtype}")
+
+
 def test_grouped_query_llama70b_shape_sampled():
     """64 sequences, 64 query heads over 8 KV heads (groups of 8), bf16, B=16,
     lognormal context lengths (median 300, up to 2048); sampled sequences
