@@ -79,6 +79,21 @@ def test_fp8_rows_small_shapes(dtype, B, G, Q):
     assert_close(to_bits(out), _oracle(c, q, D ** -0.5, ks, vs, dtype), dtype, f"fp8 rows G={G} Q={Q} {dtype} B={B}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("G,Q", [(3, 4), (5, 3), (9, 1), (1, 11), (7, 2)])
+def test_fp8_rows_between_9_and_15_per_kv_head(dtype, G, Q):
+    """9 to 15 query rows per KV head with odd group sizes over e4m3 pools;
+    long rows cut into pieces included; every output against the oracle."""
+    Hkv = 2
+    lengths = [max(L, Q) for L in LENGTHS] + [3000, 1234]
+    c = _case(lengths, Hkv, 16, seed=2600 + 10 * G + Q, exp_lo=4, exp_hi=12)
+    shape = (len(lengths), Hkv * G, D) if Q == 1 else (len(lengths), Q, Hkv * G, D)
+    q = normal_16bit(shape, dtype, DEV, 2610 + G + Q)
+    out = _run(c, q, D ** -0.5, 0.02, 0.03)
+    torch.cuda.synchronize()
+    assert_close(to_bits(out), _oracle(c, q, D ** -0.5, 0.02, 0.03, dtype), dtype, f"fp8 rows G={G} Q={Q} {dtype}")
+
+
 def test_fp8_grouped_query_llama70b_shape_sampled():
     """64 sequences, 64 query heads over 8 KV heads, bf16 queries, e4m3 pools,
     B=16, lognormal lengths up to 2048; sampled sequences against the oracle."""
