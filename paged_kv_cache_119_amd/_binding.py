@@ -351,13 +351,21 @@ def _decode_args(q, k_pool, v_pool, block_tables, context_lens, out, reuse_block
     return desc, S, H, int(block_tables.shape[1]), out
 
 
+def _ws_arg(ws, device):
+    """A caller's workspace: a contiguous GPU tensor on the pools' device (any
+    dtype; the library checks its size and alignment).  Its pointer and size in
+    bytes."""
+    _need(ws, "workspace", device=device)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def _workspace(ws, S, H, maxb, k_pool, partition_size):
     need = decode_workspace_bytes(S, H, maxb, k_pool, partition_size)
     if ws is None:
         if need == 0:
             return 0, 0
         ws = alloc_workspace(S, H, maxb, k_pool, partition_size)
-    return ws.data_ptr(), ws.numel() * ws.element_size()
+    return _ws_arg(ws, k_pool.device)
 
 
 def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
@@ -418,7 +426,7 @@ def paged_attention_decode_shared(q, k_pool, v_pool, block_tables, context_lens,
     st = lib.pkv_paged_attention_decode_shared(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                                block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, H,
                                                maxb, ctypes.byref(desc), int(group_size), prefix_lens.data_ptr(),
-                                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                               *_ws_arg(workspace, k_pool.device),
                                                _stream_ptr(k_pool.device))
     _check(st, "pkv_paged_attention_decode_shared")
     return out
@@ -458,8 +466,7 @@ def paged_attention_multi(q, k_pool, v_pool, block_tables, context_lens, scale, 
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     st = lib.pkv_paged_attention_multi(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                        block_tables.data_ptr(), context_lens.data_ptr(), float(scale), S, Q, H, maxb,
-                                       ctypes.byref(desc), workspace.data_ptr(),
-                                       workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+                                       ctypes.byref(desc), *_ws_arg(workspace, k_pool.device), _stream_ptr(dev))
     _check(st, "pkv_paged_attention_multi")
     return out
 
@@ -549,7 +556,7 @@ def paged_attention_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, sc
     st = lib.pkv_paged_attention_decode_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                             block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
                                             float(k_scale), float(v_scale), S, H, maxb, ctypes.byref(desc),
-                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            *_ws_arg(workspace, k_pool.device),
                                             _stream_ptr(dev))
     _check(st, "pkv_paged_attention_decode_fp8")
     return out
@@ -591,7 +598,7 @@ def paged_attention_multi_fp8(q, k_pool, v_pool, block_tables, context_lens, sca
     st = lib.pkv_paged_attention_multi_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                            block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
                                            float(k_scale), float(v_scale), S, Q, H, maxb, ctypes.byref(desc),
-                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                           *_ws_arg(workspace, k_pool.device),
                                            _stream_ptr(dev))
     _check(st, "pkv_paged_attention_multi_fp8")
     return out
@@ -634,7 +641,7 @@ def decode_partitions_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, 
     st = lib.pkv_decode_partitions_fp8(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                        block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
                                        float(k_scale), float(v_scale), S, Q, H, maxb, ctypes.byref(desc),
-                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       *_ws_arg(workspace, k_pool.device),
                                        _stream_ptr(dev))
     _check(st, "pkv_decode_partitions_fp8")
     return out
@@ -648,8 +655,7 @@ def decode_merge_fp8(out, context_lens, max_blocks_per_seq, k_pool, workspace, r
     desc, S, Q, H = _fp8_rows(out, k_pool, k_pool, reuse_blocks)
     _need(context_lens, "context_lens", dtype=torch.int32, ndim=1, device=k_pool.device)
     st = lib.pkv_decode_merge_fp8(out.data_ptr(), context_lens.data_ptr(), S, Q, H, int(max_blocks_per_seq),
-                                  ctypes.byref(desc), workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream_ptr(k_pool.device))
+                                  ctypes.byref(desc), *_ws_arg(workspace, k_pool.device), _stream_ptr(k_pool.device))
     _check(st, "pkv_decode_merge_fp8")
     return out
 
@@ -690,8 +696,8 @@ def paged_attention_decode_append_fp8(q, k_new, v_new, k_pool, v_pool, block_tab
     st = lib.pkv_paged_attention_decode_append_fp8(
         out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), int(k_new.stride(0)) if S > 0 else 0,
         k_pool.data_ptr(), v_pool.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), float(scale),
-        float(k_scale), float(v_scale), S, H, maxb, ctypes.byref(desc), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+        float(k_scale), float(v_scale), S, H, maxb, ctypes.byref(desc), *_ws_arg(workspace, k_pool.device),
+        _stream_ptr(dev))
     _check(st, "pkv_paged_attention_decode_append_fp8")
     return out
 
