@@ -693,34 +693,35 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(DecodeParams a) {
   st.flush();
 }
 
-// One wavefront per (sequence, KV head), for its M query rows (16 rows x 4
-// lanes): rows of empty or invalid contexts, and the LSE merge of
-// rows cut over several workers.  The pieces' (m, l) and o rows are fetched
-// four pieces at a time (rows cut into more pieces: every piece's m first,
-// 16 a round).
-// TC: the chunk length of the split pass that wrote the partials.
-// GDIM: head_dim.  Lane c (of the four lanes of a row) takes dims 16k + 4c
-// .. +4, k < GDIM / 16: one load instruction then reads 64 contiguous bytes of
-// each row's partial result.  Whole runs of 32 dims a lane touched 16 bytes
-// of 64 cache lines per instruction; this layout made the merge 13-26% faster.
-// The compiler issues each piece's loads inside the test for that piece, so a
-// row's pieces are loaded one after another.  Holding all four in flight
-// (selects instead of the test, with or without loads of absent pieces, 2 or
-// 3 waves per SIMD) measured slower: the merge is bound by its loads' cache
-// lines more than by their round trips.
-template <int DT, int TC, int GDIM = 128>
-__global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
+// One wavefront per (sequence, KV head), for its M query rows: rows of empty
+// or invalid contexts, and the LSE merge of rows cut over several workers.
+// A row takes LPR lanes (16 when M <= 4, 8 when M <= 8, else 4), so that
+// the wavefront's lanes are busy and a load instruction reads whole lines:
+// lane c of a row takes dims 4c + 4 LPR k .. +4 (k < GDIM / (4 LPR)) of the
+// pieces' partial results.  The pieces' (m, l) and o rows are fetched four
+// pieces at a time (rows cut into more pieces: every piece's m first, 4 LPR
+// a round).  The compiler issues each piece's loads inside the test for that
+// piece, so a row's pieces are loaded one after another; holding all four in
+// flight (selects instead of the test, with or without loads of absent
+// pieces, 2 or 3 waves per SIMD) measured slower: the merge is bound by the
+// cache lines its loads touch more than by their round trips.  With 4 lanes
+// a row holding runs of 32 dims, a load instruction touched 16 bytes of 64
+// lines; interleaving the dims made the merge 13-26% faster.
+// TC: the chunk length of the split pass that wrote the partials; GDIM:
+// head_dim.
+template <int DT, int TC, int GDIM, int LPR>
+__device__ __forceinline__ void merge_rows(const DecodeParams &a, int lane, int64_t grow) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  const int lane = threadIdx.x & 63;
+  static_assert(GDIM % (4 * LPR) == 0, "whole float4s per lane");
   const int gq = a.H / a.Hkv;
   const int M = gq * a.nq;
-  const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hkv + h
-  if (grow >= (int64_t)a.S * a.Hkv) return;
   const int s = (int)(grow / a.Hkv);
   const int h = (int)(grow - (int64_t)s * a.Hkv);
-  const int r = lane >> 2;         // this lane's query row (16 rows x 4 lanes)
-  constexpr int NV = GDIM / 16;     // float4s of this lane's dims
-  const int d0 = (lane & 3) * 4;    // the first of them (then every 16th)
+  const int r = lane / LPR;            // this lane's query row
+  const int c = lane % LPR;            // and its place among the row's lanes
+  constexpr int NV = GDIM / (4 * LPR);  // float4s of this lane's dims
+  constexpr int DS = 4 * LPR;           // dims between them
+  const int d0 = 4 * c;                 // the first of them
   const bool live = r < M;
   const int qi = r / gq, gi = r - (r / gq) * gq;
   uint16_t *out_row = reinterpret_cast<uint16_t *>(a.out) +
@@ -736,7 +737,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     const uint32_t v = (L == 0) ? 0u : 0x00010001u * to16<DT>(__builtin_nanf(""));
     if (live) {
 #pragma unroll
-      for (int k = 0; k < NV; ++k) *reinterpret_cast<u32x2 *>(out_row + 16 * k) = u32x2{v, v};
+      for (int k = 0; k < NV; ++k) *reinterpret_cast<u32x2 *>(out_row + DS * k) = u32x2{v, v};
     }
     return;
   }
@@ -772,7 +773,7 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
       lv[q] = a.ws_l[u];
       const float *src = a.ws_o + u * GDIM + d0;
 #pragma unroll
-      for (int k = 0; k < NV; ++k) ov[q][k] = *reinterpret_cast<const f4 *>(src + 16 * k);
+      for (int k = 0; k < NV; ++k) ov[q][k] = *reinterpret_cast<const f4 *>(src + DS * k);
     }
   };
   if (n <= 4) {
@@ -784,19 +785,18 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     for (int q = 0; q < 4; ++q) mx = fmaxf(mx, mv[q]);
     fold(mv, lv, ov, 0);
   } else {
-    // the max first (the four lanes of a row take every fourth piece, 16
-    // pieces a round), then the sums, four pieces per round
-    const int c = lane & 3;
-    for (int64_t j0 = 0; j0 < n; j0 += 16) {
+    // the max first (the row's lanes take every LPR-th piece, 4 LPR pieces
+    // a round), then the sums, four pieces per round
+    for (int64_t j0 = 0; j0 < n; j0 += 4 * LPR) {
       float mm[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mm[i] = a.ws_m[slot(min(j0 + 4 * i + c, n - 1))];
+      for (int i = 0; i < 4; ++i) mm[i] = a.ws_m[slot(min(j0 + LPR * i + c, n - 1))];
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, mm[i]);
     }
-    // across the row's four lanes (all live or all not)
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    // across the row's lanes (all live or all not)
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     for (int64_t j0 = 0; j0 < n; j0 += 4) {
       float mv[4], lv[4];
       f4 ov[4][NV];
@@ -809,8 +809,8 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
     const int64_t pi = ((int64_t)s * a.nq + qi) * a.H + (int64_t)h * gq + gi;
     float *dst = a.pfx_o + pi * GDIM + d0;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) *reinterpret_cast<f4_t *>(dst + 16 * k) = o[k];
-    if ((lane & 3) == 0) {
+    for (int k = 0; k < NV; ++k) *reinterpret_cast<f4_t *>(dst + DS * k) = o[k];
+    if (c == 0) {
       a.pfx_m[pi] = mx * kLog2e;
       a.pfx_l[pi] = lsum;
     }
@@ -820,8 +820,22 @@ __global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a)
   for (int k = 0; k < NV; ++k) {
     const uint32_t w0 = (uint32_t)to16<DT>(o[k][0] / lsum) | ((uint32_t)to16<DT>(o[k][1] / lsum) << 16);
     const uint32_t w1 = (uint32_t)to16<DT>(o[k][2] / lsum) | ((uint32_t)to16<DT>(o[k][3] / lsum) << 16);
-    *reinterpret_cast<u32x2 *>(out_row + 16 * k) = u32x2{w0, w1};
+    *reinterpret_cast<u32x2 *>(out_row + DS * k) = u32x2{w0, w1};
   }
+}
+
+template <int DT, int TC, int GDIM = 128>
+__global__ __launch_bounds__(256) void decode_group_merge_kernel(DecodeParams a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t grow = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // s * Hkv + h
+  if (grow >= (int64_t)a.S * a.Hkv) return;
+  const int M = (a.H / a.Hkv) * a.nq;
+  if (M <= 4)
+    merge_rows<DT, TC, GDIM, 16>(a, lane, grow);
+  else if (M <= 8)
+    merge_rows<DT, TC, GDIM, 8>(a, lane, grow);
+  else
+    merge_rows<DT, TC, GDIM, 4>(a, lane, grow);
 }
 
 template <int DT, int B, bool NT, bool F8, int GDIM>
